@@ -1,0 +1,181 @@
+"""CPU oracle of the paged-KV input path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product (``paged_kv_input_amd``)
+never does, and the two share no code.  The arithmetic lives in ``oracle.c``
+(plain C, one thread); this module compiles it with gcc and marshals NumPy
+arrays through ctypes.
+
+Sources: "Deep Dive into vLLM's Scheduling Mechanism: The Complete CPU-to-GPU
+Mapping Pipeline" (kongchang.com/en, with its Chinese original) for the whole
+chain, and "从源码读 vLLM Scheduler" (caffein.top) for the scheduler examples.
+Every function is pinned by CPU tests (worked examples, brute force, library
+routines, closed forms, invariants); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+# Contract values, restated (not shared) from the library's public header.
+OK = 0
+EINVAL = -1
+ST_BAD_ROW, ST_BAD_COUNT, ST_TOKEN_SUM, ST_POS_OOR = 0x01, 0x02, 0x04, 0x08
+ST_LB_OOR, ST_BLOCK_OOR, ST_SLOT_OOR = 0x10, 0x20, 0x40
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags=(), strict: bool = True) -> str:
+    """Compile the oracle with gcc into a shared library (always rebuilds)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", *(["-Werror"] if strict else []),
+           "-fPIC", "-shared", *extra_flags, src, "-o", out + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    lib.orc_prepare_batch.restype = ctypes.c_int
+    lib.orc_prepare_batch.argtypes = [_I32, _I32, _P, _P, _P, _I32, _P, _I64, _I32,
+                                      _P, _P, _P, _P, _P, _P]
+    lib.orc_compute_slot_mapping.restype = ctypes.c_int
+    lib.orc_compute_slot_mapping.argtypes = [_I32, _I32, _P, _P, _P, _P, _P, _I32, _I32,
+                                             _I32, _I32, _P, _P, _P]
+    lib.orc_scatter_kv.restype = ctypes.c_int
+    lib.orc_scatter_kv.argtypes = [_I32, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _P]
+    return lib
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the oracle library, compiling it first if it is missing or stale."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if (not os.path.exists(_LIB)) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            _lib = _declare(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def prepare_batch(sched_rows, num_scheduled, completed, token_ids, T=None, *, lib=None,
+                  with_input_ids=True):
+    """Oracle of ``prepare_batch``.  Returns a dict of NumPy outputs plus
+    ``status`` (OR of status bits) and ``rc`` (return code)."""
+    lib = lib or load()
+    rows, counts, comp = _i32(sched_rows), _i32(num_scheduled), _i32(completed)
+    tok = _i32(token_ids)
+    n = rows.shape[0]
+    if T is None:
+        T = int(np.maximum(counts.astype(np.int64), 0).sum())
+    R = comp.shape[0]
+    L = tok.shape[1] if tok.ndim == 2 else 0
+    out = {
+        "index_mapping": np.full(n, -7, np.int32),
+        "query_start_loc": np.full(n + 1, -7, np.int32),
+        "seq_lens": np.full(n, -7, np.int32),
+        "positions": np.full(max(T, 0), -7, np.int32),
+        "input_ids": np.full(max(T, 0), -7, np.int32) if with_input_ids else None,
+    }
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_prepare_batch(n, T, _ptr(rows), _ptr(counts), _ptr(comp), R, _ptr(tok),
+                               tok.strides[0] // 4 if tok.ndim == 2 else 0, L,
+                               _ptr(out["index_mapping"]), _ptr(out["query_start_loc"]),
+                               _ptr(out["seq_lens"]), _ptr(out["positions"]),
+                               _ptr(out["input_ids"]), _ptr(st))
+    out["status"], out["rc"] = int(st[0]), int(rc)
+    return out
+
+
+IBT_UNWRITTEN = -9  # fill value of input_block_tables entries the call must not write
+
+
+def compute_slot_mapping(index_mapping, query_start_loc, seq_lens, positions, block_table,
+                         block_size, num_blocks, *, with_ibt=True, lib=None):
+    """Oracle of ``compute_slot_mapping`` for one KV-cache group."""
+    lib = lib or load()
+    im, qsl, sl, pos = _i32(index_mapping), _i32(query_start_loc), _i32(seq_lens), _i32(positions)
+    bt = _i32(block_table)
+    n, T = im.shape[0], pos.shape[0]
+    R, MB = bt.shape
+    out = {
+        "slot_mapping": np.full(T, -7, np.int32),
+        "input_block_tables": np.full((n, MB), IBT_UNWRITTEN, np.int32) if with_ibt else None,
+    }
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_compute_slot_mapping(n, T, _ptr(im), _ptr(qsl), _ptr(sl), _ptr(pos), _ptr(bt),
+                                      R, MB, block_size, num_blocks, _ptr(out["slot_mapping"]),
+                                      _ptr(out["input_block_tables"]), _ptr(st))
+    out["status"], out["rc"] = int(st[0]), int(rc)
+    return out
+
+
+def scatter_kv(k, v, k_cache, v_cache, slot_mapping, *, lib=None):
+    """Oracle of ``scatter_kv``: writes into ``k_cache``/``v_cache`` in place.
+
+    ``k``/``v`` are [T, ...] arrays whose rows may be strided; the caches are
+    C-contiguous [num_slots, ...] arrays with the same row size.  Returns
+    ``(rc, status)``.
+    """
+    lib = lib or load()
+    sm = _i32(slot_mapping)
+    T = sm.shape[0]
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    row_bytes = int(np.prod(k_cache.shape[1:])) * k_cache.itemsize
+    num_slots = k_cache.shape[0]
+    for a in (k, v):
+        assert a.shape[0] == T
+        assert int(np.prod(a.shape[1:])) * a.itemsize == row_bytes
+        # each row itself must be contiguous: only the token stride may differ
+        assert a.shape[0] == 0 or a[0].flags.c_contiguous
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_scatter_kv(T, row_bytes, _ptr(k), k.strides[0] if T else row_bytes,
+                            _ptr(v), v.strides[0] if T else row_bytes,
+                            _ptr(k_cache), _ptr(v_cache), num_slots, _ptr(sm), _ptr(st))
+    return int(rc), int(st[0])
+
+
+def run_chain(batch, *, caches=None, sentinel=0xFFFF, lib=None):
+    """Whole chain on one ``workloads.Batch``: prepare, then per group the slot
+    mapping and the scatter into host caches (filled with ``sentinel`` words
+    unless ``caches`` is given).  Returns (prep, [per-group dict])."""
+    lib = lib or load()
+    prep = prepare_batch(batch.sched_rows, batch.num_scheduled, batch.completed,
+                         batch.token_ids, batch.T, lib=lib)
+    groups = []
+    for gi, g in enumerate(batch.groups):
+        sm = compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                  prep["seq_lens"], prep["positions"], g.block_table,
+                                  g.block_size, g.num_blocks, lib=lib)
+        if caches is not None:
+            kc, vc = caches[gi]
+        else:
+            kc = np.full((g.num_slots, g.num_heads, g.head_dim), sentinel, np.uint16)
+            vc = np.full((g.num_slots, g.num_heads, g.head_dim), sentinel, np.uint16)
+        rc, st = scatter_kv(g.k, g.v, kc, vc, sm["slot_mapping"], lib=lib)
+        sm["scatter_rc"], sm["scatter_status"] = rc, st
+        sm["k_cache"], sm["v_cache"] = kc, vc
+        groups.append(sm)
+    return prep, groups

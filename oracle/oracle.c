@@ -1,0 +1,364 @@
+/*
+ * oracle.c -- plain CPU oracle of the schedule -> flat GPU inputs -> paged K/V
+ * write chain.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference for the HIP
+ * library in paged_kv_input_amd/.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load it; the product never does.  It shares no
+ * source, header, helper or constant table with the HIP library: the numeric
+ * values of return codes and status bits below restate the public contract and
+ * are compared, not shared.
+ *
+ * It is written to be checked by eye against the pages, not to be fast: one
+ * thread, plain loops, a library sort.  Sources, cited by title and section:
+ *
+ *   [KC]  "Deep Dive into vLLM's Scheduling Mechanism: The Complete CPU-to-GPU
+ *         Mapping Pipeline" (kongchang.com/en) and its Chinese original
+ *         "vLLM调度机制深度解析：CPU到GPU的完整映射流程" (kongchang.com).
+ *   [CF]  "从源码读 vLLM Scheduler：一轮调度如何分配请求与 KV Cache" (caffein.top).
+ *
+ * Notation follows [KC] "Summary of the Four Index Space Mappings":
+ * request_state_index (row of the worker's persistent state), batch_index (row
+ * of this step's compact batch), flat_token_index (position in the flattened
+ * token sequence) and position (the token's ordinal inside its own request).
+ *
+ * Pins (all in tests/, run on the CPU): every function here is pinned.
+ *   orc_prepare_batch        -- [KC] worked example values (golden file), the
+ *                               [CF] prefix example, brute-force loops on tiny
+ *                               batches, NumPy lexsort/cumsum/repeat, closed-form
+ *                               token table, invariants.
+ *   orc_compute_slot_mapping -- the printed slot 207 and its derived neighbours,
+ *                               a paged address space enumerated block by block
+ *                               (no division), the contiguous-table closed form,
+ *                               block size 1, invariants.
+ *   orc_scatter_kv           -- NumPy fancy-index assignment, gather round trip,
+ *                               sentinel count.
+ * Readings of points the pages leave open are listed at each step (R1..R9).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Return codes (host-detectable argument errors). */
+#define ORC_OK      0
+#define ORC_EINVAL (-1)
+
+/* Status bits (data errors found while computing; OR-ed into *status). */
+#define ORC_ST_BAD_ROW    0x01u  /* request_state_index outside [0, R)            */
+#define ORC_ST_BAD_COUNT  0x02u  /* negative scheduled-token count                */
+#define ORC_ST_TOKEN_SUM  0x04u  /* sum of scheduled counts != T                  */
+#define ORC_ST_POS_OOR    0x08u  /* position < 0, or >= token-table width         */
+#define ORC_ST_LB_OOR     0x10u  /* logic_block >= block-table width              */
+#define ORC_ST_BLOCK_OOR  0x20u  /* physical_block_id < 0 or >= pool size         */
+#define ORC_ST_SLOT_OOR   0x40u  /* slot_id >= cache slots                        */
+
+/* One scheduled request while the batch is being assembled. */
+typedef struct {
+    int32_t tokens_this_step;     /* num_scheduled (negative counts read as 0) */
+    int32_t request_state_index;  /* the request's row in the persistent state */
+} sched_req;
+
+/*
+ * [KC] "Extracting the Execution Batch from Global State": the batch is ordered
+ * by the number of tokens each request executes this step.
+ * R1 (direction): ascending -- the only order that gives the printed
+ *     query_start_loc [0, 1, 9] (the 1-token request B before the 8-token A).
+ * R2 (ties): smaller request_state_index first, so the batch depends only on
+ *     which requests are scheduled, not on the order the host listed them.
+ */
+static int by_tokens_then_row(const void* pa, const void* pb)
+{
+    const sched_req* a = (const sched_req*)pa;
+    const sched_req* b = (const sched_req*)pb;
+    if (a->tokens_this_step != b->tokens_this_step)
+        return a->tokens_this_step < b->tokens_this_step ? -1 : 1;
+    if (a->request_state_index != b->request_state_index)
+        return a->request_state_index < b->request_state_index ? -1 : 1;
+    return 0;
+}
+
+/*
+ * Batch assembly and flattening ([KC] "Batch Construction and Sequence
+ * Flattening" and "Contiguous Token Sequence Processing"; seq_lens from
+ * "Complete Input Preparation for the Attention Module").
+ *
+ *   sched_rows[n], num_scheduled[n]  this step's schedule, in host order
+ *   completed[R]                     tokens each state row has already processed
+ *   token_ids[R * token_stride]      the persistent token table, row-major
+ *   outputs: index_mapping[n], query_start_loc[n+1], seq_lens[n],
+ *            positions[T], input_ids[T] (input_ids may be NULL: not produced)
+ *
+ * R3: a position starts at completed_tokens, the value *before* this step
+ *     (31 done -> position 31; 16 done -> positions 16..23 in the example).
+ * R4: input_ids[t] = token_ids[row][position]: the "corresponding positions" of
+ *     the request's token list, kept as a persistent per-row table.
+ * R5: seq_lens[b] = completed + tokens this step (history plus new).
+ * R6 (data errors, never out-of-bounds accesses): a row outside [0, R) leaves
+ *     its request in the batch order with seq_len -1 and its tokens at position
+ *     -1 / input id -1; a negative count is read as 0; prefix sums saturate at
+ *     INT32_MAX; tokens past the last request (sum < T) get position -1 and
+ *     input id -1; tokens beyond T (sum > T) are dropped; a position outside
+ *     [0, L) gets input id -1.  Positions and seq_lens keep the low 32 bits of
+ *     the 64-bit sum.
+ */
+int orc_prepare_batch(int32_t n, int32_t T,
+                      const int32_t* sched_rows, const int32_t* num_scheduled,
+                      const int32_t* completed, int32_t R,
+                      const int32_t* token_ids, int64_t token_stride, int32_t L,
+                      int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
+                      int32_t* positions, int32_t* input_ids, uint32_t* status)
+{
+    if (n < 0 || T < 0 || R < 0 || L < 0)
+        return ORC_EINVAL;
+    if (query_start_loc == NULL)
+        return ORC_EINVAL;
+    if (n > 0 && (sched_rows == NULL || num_scheduled == NULL || index_mapping == NULL ||
+                  seq_lens == NULL || (R > 0 && completed == NULL)))
+        return ORC_EINVAL;
+    if (T > 0 && positions == NULL)
+        return ORC_EINVAL;
+    if (input_ids != NULL && T > 0 && ((R > 0 && L > 0 && token_ids == NULL) || token_stride < L))
+        return ORC_EINVAL;
+
+    uint32_t st = 0;
+
+    /* Step 1 -- extract the relevant requests from global state. */
+    sched_req* batch = (sched_req*)malloc(sizeof(sched_req) * (size_t)(n > 0 ? n : 1));
+    if (batch == NULL)
+        return ORC_EINVAL;
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t count = num_scheduled[i];
+        if (count < 0) {
+            st |= ORC_ST_BAD_COUNT;
+            count = 0;
+        }
+        batch[i].tokens_this_step = count;
+        batch[i].request_state_index = sched_rows[i];
+    }
+
+    /* Step 2 -- sort by the number of tokens to execute this step (R1, R2). */
+    qsort(batch, (size_t)n, sizeof(sched_req), by_tokens_then_row);
+
+    /* Step 3 -- assemble the batch: index_mapping[batch_index] = request_state_index. */
+    for (int32_t b = 0; b < n; ++b)
+        index_mapping[b] = batch[b].request_state_index;
+
+    /* Flattening keeps the request boundaries as a prefix sum (CSR row pointers). */
+    int64_t running = 0;
+    query_start_loc[0] = 0;
+    for (int32_t b = 0; b < n; ++b) {
+        running += batch[b].tokens_this_step;
+        query_start_loc[b + 1] = running > INT32_MAX ? INT32_MAX : (int32_t)running;
+    }
+    if (running != T)
+        st |= ORC_ST_TOKEN_SUM;
+
+    /* seq_lens: history plus this step's tokens, per batch row (R5). */
+    for (int32_t b = 0; b < n; ++b) {
+        int32_t row = batch[b].request_state_index;
+        if (row < 0 || row >= R) {
+            st |= ORC_ST_BAD_ROW;
+            seq_lens[b] = -1;
+            continue;
+        }
+        int64_t len = (int64_t)completed[row] + batch[b].tokens_this_step;
+        seq_lens[b] = (int32_t)(uint32_t)(uint64_t)len;
+    }
+
+    /* Every flat token starts unassigned (R6). */
+    for (int32_t t = 0; t < T; ++t) {
+        positions[t] = -1;
+        if (input_ids != NULL)
+            input_ids[t] = -1;
+    }
+
+    /* position and input_ids, request by request, token by token. */
+    for (int32_t b = 0; b < n; ++b) {
+        int32_t row = batch[b].request_state_index;
+        int64_t start = query_start_loc[b];
+        for (int64_t j = 0; j < batch[b].tokens_this_step; ++j) {
+            int64_t flat_token_index = start + j;
+            if (flat_token_index >= T)
+                break;                                   /* more tokens than T (R6) */
+            if (row < 0 || row >= R)
+                continue;                                /* flagged above */
+            int64_t position = (int64_t)completed[row] + j;   /* R3 */
+            positions[flat_token_index] = (int32_t)(uint32_t)(uint64_t)position;
+            if (position < 0 || position >= L) {
+                st |= ORC_ST_POS_OOR;
+                continue;
+            }
+            if (input_ids != NULL)
+                input_ids[flat_token_index] = token_ids[(int64_t)row * token_stride + position];
+        }
+    }
+
+    free(batch);
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * The physical-address chain of [KC] "Multi-Layer Coordinate Conversion
+ * Pipeline", for one KV-cache group (each group keeps a block table of its own
+ * and so gets a slot mapping of its own):
+ *
+ *   batch_index      -> request_state_index          (index_mapping)
+ *   flat_token_index -> position                     (one to one)
+ *   position         -> logic_block, offset          (division and remainder)
+ *   request_state_index, logic_block -> physical_block_id   (block_table)
+ *   physical_block_id, offset -> slot_id             (physical_block_id * block_size + offset)
+ *
+ * and the visible pages per request, input_block_tables, from "Complete Input
+ * Preparation for the Attention Module".
+ *
+ *   block_table[R * MB], row-major; input_block_tables[n * MB] (may be NULL).
+ *
+ * R7: a token belongs to batch row b when query_start_loc[b] <= t <
+ *     query_start_loc[b+1]; tokens before query_start_loc[0] or from
+ *     query_start_loc[n] on belong to no request and get slot -1, unflagged.
+ * R8: "visible" pages are the first ceil(seq_len / block_size) entries of the
+ *     request's table (the blocks holding history and new tokens); entries past
+ *     them are not written.  Visible entries are copied verbatim; one outside
+ *     [0, num_blocks) is flagged BLOCK_OOR.  A visible count above MB is flagged
+ *     LB_OOR and cut to MB.  seq_len <= 0 shows no page.
+ * R6 (continued): a bad row, a negative position, a logic_block >= MB or a
+ *     physical block outside [0, num_blocks) is flagged and gives slot -1.
+ */
+int orc_compute_slot_mapping(int32_t n, int32_t T,
+                             const int32_t* index_mapping, const int32_t* query_start_loc,
+                             const int32_t* seq_lens, const int32_t* positions,
+                             const int32_t* block_table, int32_t R, int32_t MB,
+                             int32_t block_size, int32_t num_blocks,
+                             int32_t* slot_mapping, int32_t* input_block_tables,
+                             uint32_t* status)
+{
+    if (n < 0 || T < 0 || R < 0 || MB < 0 || num_blocks < 0 || block_size <= 0)
+        return ORC_EINVAL;
+    if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX + 1)
+        return ORC_EINVAL;                       /* slot ids must fit in int32 */
+    if (query_start_loc == NULL || (n > 0 && index_mapping == NULL))
+        return ORC_EINVAL;
+    if (T > 0 && (positions == NULL || slot_mapping == NULL))
+        return ORC_EINVAL;
+    if ((n > 0 || T > 0) && R > 0 && MB > 0 && block_table == NULL)
+        return ORC_EINVAL;
+    if (input_block_tables != NULL && n > 0 && seq_lens == NULL)
+        return ORC_EINVAL;
+
+    uint32_t st = 0;
+
+    for (int32_t t = 0; t < T; ++t)
+        slot_mapping[t] = -1;                                   /* R7 */
+
+    for (int32_t batch_index = 0; batch_index < n; ++batch_index) {
+        int32_t request_state_index = index_mapping[batch_index];
+        int64_t begin = query_start_loc[batch_index];
+        int64_t end = query_start_loc[batch_index + 1];
+        if (begin < 0)
+            begin = 0;
+        if (end > T)
+            end = T;
+        for (int64_t flat_token_index = begin; flat_token_index < end; ++flat_token_index) {
+            if (request_state_index < 0 || request_state_index >= R) {
+                st |= ORC_ST_BAD_ROW;
+                continue;
+            }
+            int32_t position = positions[flat_token_index];
+            if (position < 0) {
+                st |= ORC_ST_POS_OOR;
+                continue;
+            }
+            int32_t logic_block = position / block_size;
+            int32_t offset = position % block_size;
+            if (logic_block >= MB) {
+                st |= ORC_ST_LB_OOR;
+                continue;
+            }
+            int32_t physical_block_id =
+                block_table[(int64_t)request_state_index * MB + logic_block];
+            if (physical_block_id < 0 || physical_block_id >= num_blocks) {
+                st |= ORC_ST_BLOCK_OOR;
+                continue;
+            }
+            slot_mapping[flat_token_index] = physical_block_id * block_size + offset;
+        }
+    }
+
+    if (input_block_tables != NULL) {
+        for (int32_t batch_index = 0; batch_index < n; ++batch_index) {
+            int32_t request_state_index = index_mapping[batch_index];
+            if (request_state_index < 0 || request_state_index >= R) {
+                st |= ORC_ST_BAD_ROW;
+                continue;
+            }
+            int32_t seq_len = seq_lens[batch_index];
+            int64_t visible = seq_len <= 0 ? 0 : ((int64_t)seq_len + block_size - 1) / block_size;
+            if (visible > MB) {
+                st |= ORC_ST_LB_OOR;
+                visible = MB;
+            }
+            for (int64_t i = 0; i < visible; ++i) {
+                int32_t blk = block_table[(int64_t)request_state_index * MB + i];
+                if (blk < 0 || blk >= num_blocks)
+                    st |= ORC_ST_BLOCK_OOR;
+                input_block_tables[(int64_t)batch_index * MB + i] = blk;
+            }
+        }
+    }
+
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * Write each new token's K and V into the paged cache at its slot ([KC]
+ * "Multi-Layer Coordinate Conversion Pipeline": slot_mapping is the write
+ * destination of this step's new K/V; "Address Calculation Example": a slot id
+ * counts cache units, one token's K and V over all heads, not bytes).
+ *
+ * R9 (layout): separate K and V caches, each [num_slots, row_bytes] with the
+ *     H x D row of a slot contiguous, so slot * row_bytes is the byte offset.
+ *     Token t's K row starts at k + t * k_stride bytes (likewise V), so K/V may be
+ *     strided views.  The payload is copied as bytes, never as numbers.
+ * R6 (continued): slot < 0 marks a token with nothing to write and is skipped
+ *     silently; slot >= num_slots is flagged SLOT_OOR and skipped.  Tokens are
+ *     written in flat order (duplicate slots break the caller's contract).
+ */
+int orc_scatter_kv(int32_t T, int64_t row_bytes,
+                   const void* k, int64_t k_stride, const void* v, int64_t v_stride,
+                   void* k_cache, void* v_cache, int64_t num_slots,
+                   const int32_t* slot_mapping, uint32_t* status)
+{
+    if (T < 0 || row_bytes <= 0 || num_slots < 0 || k_stride < row_bytes || v_stride < row_bytes)
+        return ORC_EINVAL;
+    if (T > 0 && (k == NULL || v == NULL || slot_mapping == NULL ||
+                  (num_slots > 0 && (k_cache == NULL || v_cache == NULL))))
+        return ORC_EINVAL;
+
+    uint32_t st = 0;
+    const unsigned char* ksrc = (const unsigned char*)k;
+    const unsigned char* vsrc = (const unsigned char*)v;
+    unsigned char* kdst = (unsigned char*)k_cache;
+    unsigned char* vdst = (unsigned char*)v_cache;
+
+    for (int32_t flat_token_index = 0; flat_token_index < T; ++flat_token_index) {
+        int64_t slot_id = slot_mapping[flat_token_index];
+        if (slot_id < 0)
+            continue;
+        if (slot_id >= num_slots) {
+            st |= ORC_ST_SLOT_OOR;
+            continue;
+        }
+        memcpy(kdst + slot_id * row_bytes, ksrc + (int64_t)flat_token_index * k_stride,
+               (size_t)row_bytes);
+        memcpy(vdst + slot_id * row_bytes, vsrc + (int64_t)flat_token_index * v_stride,
+               (size_t)row_bytes);
+    }
+
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}

@@ -1,0 +1,302 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes a loaded oracle library (the real one, or a copy
+with a planted mistake) and raises AssertionError when the oracle disagrees
+with: the values the pages print for their worked examples (golden files under
+tests/golden/), brute force on tiny batches, NumPy library routines, closed
+forms, or invariants.  test_oracle_pins.py runs them on the oracle;
+test_oracle_mutants.py checks that each planted mistake fails at least one.
+"""
+import json
+import os
+
+import numpy as np
+
+import oracle
+import workloads
+from bruteforce import chain as brute_chain
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _eq(a, b, what):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert a.shape == b.shape and np.array_equal(a, b), f"{what}: {a.tolist()} != {b.tolist()}"
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked examples
+# ---------------------------------------------------------------------------
+
+def pin_pages_example(lib):
+    """Printed and derived values of the kongchang.com worked example."""
+    g = _golden("pages_example.json")
+    b = workloads.pages_example()
+    prep, groups = oracle.run_chain(b, lib=lib)
+    assert prep["rc"] == 0 and prep["status"] == 0
+    _eq(prep["query_start_loc"], g["printed"]["query_start_loc"], "query_start_loc")
+    _eq(prep["positions"], g["printed"]["positions"], "positions")
+    first = g["printed"]["first_token_of_B"]
+    t = first["flat_token_index"]
+    gr = groups[0]
+    assert gr["rc"] == 0 and gr["status"] == 0
+    assert int(prep["positions"][t]) == first["position"]
+    bs = b.groups[0].block_size
+    assert int(prep["positions"][t]) // bs == first["logic_block"]
+    assert int(prep["positions"][t]) % bs == first["offset"]
+    assert int(gr["slot_mapping"][t]) == first["slot_id"]
+    assert int(gr["slot_mapping"][t]) // bs == first["physical_block_id"]
+    d = g["derived"]
+    _eq(prep["index_mapping"], d["index_mapping"], "index_mapping")
+    _eq(prep["seq_lens"], d["seq_lens"], "seq_lens")
+    _eq(gr["slot_mapping"], d["slot_mapping"], "slot_mapping")
+    _eq(gr["input_block_tables"], d["input_block_tables"], "input_block_tables")
+    _eq(prep["input_ids"], d["input_ids_identity_code"], "input_ids")
+    k, v = b.groups[0].k, b.groups[0].v
+    kc, vc = gr["k_cache"], gr["v_cache"]
+    _eq(kc[207], k[0], "K at slot 207")
+    _eq(vc[207], v[0], "V at slot 207")
+    for i in range(8):
+        _eq(kc[704 + i], k[1 + i], f"K at slot {704 + i}")
+        _eq(vc[704 + i], v[1 + i], f"V at slot {704 + i}")
+    written = np.any(kc != 0xFFFF, axis=(1, 2))
+    assert int(written.sum()) == 9
+
+
+def pin_prefix_example(lib):
+    """The caffein.top prefix-reuse example: [P1][P2][B3], 8 reused + 2 new tokens."""
+    g = _golden("prefix_reuse_example.json")
+    inst = g["inputs"]["instantiate"]
+    b = workloads.prefix_reuse_example(inst["P1"], inst["P2"], inst["B3"])
+    prep, groups = oracle.run_chain(b, lib=lib)
+    e = g["expected"]
+    _eq(prep["index_mapping"], e["index_mapping"], "index_mapping")
+    _eq(prep["query_start_loc"], e["query_start_loc"], "query_start_loc")
+    _eq(prep["seq_lens"], e["seq_lens"], "seq_lens")
+    _eq(prep["positions"], e["positions"], "positions")
+    bs = g["inputs"]["block_size"]
+    _eq(prep["positions"] // bs, e["logic_block"], "logic_block")
+    b3 = inst["B3"]
+    _eq(groups[0]["slot_mapping"], [bs * b3, bs * b3 + 1], "slot_mapping")
+    _eq(groups[0]["input_block_tables"], [[inst["P1"], inst["P2"], b3]], "input_block_tables")
+
+
+def pin_budget_tie_example(lib):
+    """The caffein.top budget example: equal counts, order fixed by the tie-break."""
+    g = _golden("budget_tie_example.json")
+    b = workloads.budget_tie_example()
+    prep, _ = oracle.run_chain(b, lib=lib)
+    e = g["expected"]
+    for key in ("index_mapping", "query_start_loc", "seq_lens", "positions"):
+        _eq(prep[key], e[key], key)
+
+
+# ---------------------------------------------------------------------------
+# brute force on tiny batches
+# ---------------------------------------------------------------------------
+
+def pin_bruteforce(lib, seeds=range(200)):
+    for seed in seeds:
+        b = workloads.random_tiny(seed, zero_counts=(seed % 5 == 4))
+        prep, groups = oracle.run_chain(b, lib=lib)
+        bf = brute_chain(b.sched_rows, b.num_scheduled, b.completed, b.token_ids,
+                         [(g.block_table.tolist(), g.block_size) for g in b.groups])
+        for key in ("index_mapping", "query_start_loc", "seq_lens", "positions", "input_ids"):
+            _eq(prep[key], bf[key], f"seed {seed} {key}")
+        assert prep["status"] == 0, f"seed {seed} status {prep['status']}"
+        for gi, (g, gr, bg) in enumerate(zip(b.groups, groups, bf["groups"])):
+            _eq(gr["slot_mapping"], bg["slot_mapping"], f"seed {seed} g{gi} slot_mapping")
+            for bi, vis in enumerate(bg["input_block_tables"]):
+                row = gr["input_block_tables"][bi]
+                _eq(row[:len(vis)], vis, f"seed {seed} g{gi} ibt row {bi}")
+                assert np.all(row[len(vis):] == oracle.IBT_UNWRITTEN), f"seed {seed} ibt tail"
+            assert gr["status"] == 0
+            # scatter: NumPy fancy-index assignment of the brute-force slots
+            kc = np.full_like(gr["k_cache"], 0xFFFF)
+            vc = np.full_like(gr["v_cache"], 0xFFFF)
+            s = np.asarray(bg["slot_mapping"], np.int64)
+            kc[s] = g.k
+            vc[s] = g.v
+            _eq(gr["k_cache"], kc, f"seed {seed} g{gi} k_cache")
+            _eq(gr["v_cache"], vc, f"seed {seed} g{gi} v_cache")
+
+
+# ---------------------------------------------------------------------------
+# library routines and closed forms on seeded configs
+# ---------------------------------------------------------------------------
+
+def _library_chain(b):
+    """The same outputs from NumPy routines: lexsort, cumsum, repeat, searchsorted."""
+    order = np.lexsort((b.sched_rows, b.num_scheduled))
+    im = b.sched_rows[order]
+    counts = b.num_scheduled[order].astype(np.int64)
+    qsl = np.concatenate([[0], np.cumsum(counts)])
+    T = int(qsl[-1])
+    owner = np.repeat(np.arange(im.size), counts)
+    assert np.array_equal(owner, np.searchsorted(qsl, np.arange(T), side="right") - 1)
+    pos = b.completed[im][owner] + (np.arange(T) - qsl[owner])
+    ids = b.token_ids[im[owner], pos]
+    seq = b.completed[im] + counts
+    return im, qsl, seq, pos, ids, owner
+
+
+def pin_library_routines(lib, names=("seeded_16req", "seeded_16req_decode50")):
+    for name in names:
+        b = workloads.make(name)
+        prep, groups = oracle.run_chain(b, lib=lib)
+        im, qsl, seq, pos, ids, owner = _library_chain(b)
+        _eq(prep["index_mapping"], im, f"{name} index_mapping")
+        _eq(prep["query_start_loc"], qsl, f"{name} query_start_loc")
+        _eq(prep["seq_lens"], seq, f"{name} seq_lens")
+        _eq(prep["positions"], pos, f"{name} positions")
+        _eq(prep["input_ids"], ids, f"{name} input_ids")
+        for g, gr in zip(b.groups, groups):
+            bt = g.block_table
+            bs = g.block_size
+            blk = bt[im[owner], pos // bs]
+            _eq(gr["slot_mapping"], blk * bs + pos % bs, f"{name} slot_mapping")
+            kc = np.full_like(gr["k_cache"], 0xFFFF)
+            kc[gr["slot_mapping"]] = g.k
+            _eq(gr["k_cache"], kc, f"{name} k_cache")
+
+
+def pin_closed_forms(lib):
+    """Identity token table and a contiguous block table (the textbook
+    unpaged cache: request r owns slots [r*MB*bs, (r+1)*MB*bs))."""
+    rng = np.random.default_rng(7)
+    for bs in (1, 3, 16):
+        R, n, L = 12, 9, 40
+        MB = -(-L // bs)
+        rows = rng.choice(R, n, replace=False).astype(np.int32)
+        counts = rng.integers(0, 7, n).astype(np.int32)
+        completed = np.zeros(R, np.int32)
+        completed[rows] = rng.integers(0, L - 7, n)
+        tok = (np.arange(R)[:, None] * L + np.arange(L)[None, :]).astype(np.int32)
+        prep = oracle.prepare_batch(rows, counts, completed, tok, lib=lib)
+        im, qsl = prep["index_mapping"], prep["query_start_loc"]
+        pos, ids = prep["positions"], prep["input_ids"]
+        T = int(qsl[-1])
+        assert T == int(counts.sum())
+        owner = np.searchsorted(qsl, np.arange(T), side="right") - 1
+        _eq(ids // L, im[owner], f"bs {bs} input_ids row code")
+        _eq(ids % L, pos, f"bs {bs} input_ids position code")
+        bt = (np.arange(R)[:, None] * MB + np.arange(MB)[None, :]).astype(np.int32)
+        sm = oracle.compute_slot_mapping(im, qsl, prep["seq_lens"], pos, bt, bs, R * MB, lib=lib)
+        _eq(sm["slot_mapping"], im[owner].astype(np.int64) * MB * bs + pos, f"bs {bs} contiguous")
+        if bs == 1:
+            _eq(sm["slot_mapping"], bt[im[owner], pos], "bs 1: slot = block_table[row][pos]")
+
+
+def pin_invariants(lib, names=("seeded_16req", "seeded_16req_decode50")):
+    for name in names:
+        b = workloads.make(name)
+        prep, groups = oracle.run_chain(b, lib=lib)
+        im, qsl, pos = prep["index_mapping"], prep["query_start_loc"], prep["positions"]
+        counts = np.diff(qsl)
+        assert sorted(im.tolist()) == sorted(b.sched_rows.tolist()), "permutation"
+        assert np.all(np.diff(counts) >= 0), "counts non-decreasing along the batch"
+        assert qsl[0] == 0 and qsl[-1] == b.T
+        # independent of the order the host lists the schedule in
+        perm = np.random.default_rng(3).permutation(b.n)
+        p2 = oracle.prepare_batch(b.sched_rows[perm], b.num_scheduled[perm], b.completed,
+                                  b.token_ids, lib=lib)
+        for key in ("index_mapping", "query_start_loc", "seq_lens", "positions", "input_ids"):
+            _eq(p2[key], prep[key], f"{name} shuffled {key}")
+        for bb in range(b.n):
+            seg = pos[qsl[bb]:qsl[bb + 1]]
+            _eq(seg, b.completed[im[bb]] + np.arange(counts[bb]), f"{name} run {bb}")
+        for g, gr in zip(b.groups, groups):
+            s = gr["slot_mapping"]
+            bs = g.block_size
+            assert np.unique(s).size == s.size, "slots unique"
+            _eq(s % bs, pos % bs, "offset kept")
+            owner = np.searchsorted(qsl, np.arange(b.T), side="right") - 1
+            for t in range(b.T):
+                vis = -(-int(prep["seq_lens"][owner[t]]) // bs)
+                assert s[t] // bs in g.block_table[im[owner[t]], :vis], "slot in a visible block"
+            _eq(gr["k_cache"][s], g.k, "gather by slot reproduces K")
+            _eq(gr["v_cache"][s], g.v, "gather by slot reproduces V")
+            nonsent = np.any(gr["k_cache"] != 0xFFFF, axis=(1, 2))
+            assert int(nonsent.sum()) == b.T, "no stray writes"
+
+
+def pin_error_semantics(lib):
+    """Data errors give the documented outputs and status bits (the readings of
+    what the pages leave open), and nothing is written for them."""
+    R, L, MB, bs, NB = 6, 10, 3, 4, 8
+    completed = np.array([0, 2, 3, 9, -1, 5], np.int32)
+    tok = (np.arange(R)[:, None] * 100 + np.arange(L)[None, :]).astype(np.int32)
+    # row 9 is out of range; count -2 reads as 0; row 3 runs past L; row 4 starts negative
+    rows = np.array([1, 9, 2, 3, 4], np.int32)
+    counts = np.array([2, 1, -2, 3, 1], np.int32)
+    prep = oracle.prepare_batch(rows, counts, completed, tok, T=9, lib=lib)
+    st = prep["status"]
+    assert st == (oracle.ST_BAD_ROW | oracle.ST_BAD_COUNT | oracle.ST_TOKEN_SUM | oracle.ST_POS_OOR), st
+    # order by (count, row): (0,2) (1,4) (1,9) (2,1) (3,3)
+    _eq(prep["index_mapping"], [2, 4, 9, 1, 3], "index_mapping")
+    _eq(prep["query_start_loc"], [0, 0, 1, 2, 4, 7], "query_start_loc")
+    _eq(prep["seq_lens"], [3, 0, -1, 4, 12], "seq_lens")
+    _eq(prep["positions"], [-1, -1, 2, 3, 9, 10, 11, -1, -1], "positions")
+    _eq(prep["input_ids"], [-1, -1, 102, 103, 309, -1, -1, -1, -1], "input_ids")
+    bt = np.array([[0, 1, 2], [3, -1, 9], [4, 5, 6], [7, -1, -1], [2, 2, 2], [1, 1, 1]], np.int32)
+    sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                     prep["seq_lens"], prep["positions"], bt, bs, NB, lib=lib)
+    # token 0: row 4, position -1 -> POS_OOR; token 1: row 9 -> BAD_ROW;
+    # tokens 2,3: row 1 positions 2,3 -> block 3 -> slots 14, 15;
+    # token 4: row 3 position 9 -> logic block 2 -> block -1 -> BLOCK_OOR;
+    # tokens 5,6: positions 10, 11 -> logic block 2 -> BLOCK_OOR; tokens 7, 8: no request
+    _eq(sm["slot_mapping"], [-1, -1, 14, 15, -1, -1, -1, -1, -1], "slot_mapping")
+    assert sm["status"] == (oracle.ST_BAD_ROW | oracle.ST_POS_OOR | oracle.ST_BLOCK_OOR), sm["status"]
+    # visible blocks: row 2 seq 3 -> 1: [4]; row 4 seq 0 -> none; row 9 skipped;
+    # row 1 seq 4 -> 1: [3]; row 3 seq 12 -> 3: [7, -1, -1] (BLOCK_OOR)
+    U = oracle.IBT_UNWRITTEN
+    _eq(sm["input_block_tables"], [[4, U, U], [U, U, U], [U, U, U], [3, U, U], [7, -1, -1]], "ibt")
+    # logic block beyond the table and seq_len beyond MB*bs
+    sm2 = oracle.compute_slot_mapping(np.array([2], np.int32), np.array([0, 1], np.int32),
+                                      np.array([13], np.int32), np.array([12], np.int32),
+                                      bt, bs, NB, lib=lib)
+    _eq(sm2["slot_mapping"], [-1], "lb >= MB")
+    assert sm2["status"] == oracle.ST_LB_OOR
+    _eq(sm2["input_block_tables"], [[4, 5, 6]], "ibt cut to MB")
+    # scatter: slot beyond the cache is flagged and skipped, negative slot skipped silently
+    k = np.arange(4 * 8, dtype=np.uint16).reshape(4, 8)
+    v = k + 1000
+    kc = np.zeros((5, 8), np.uint16)
+    vc = np.zeros((5, 8), np.uint16)
+    rc, st = oracle.scatter_kv(k, v, kc, vc, np.array([4, -1, 5, 0], np.int32), lib=lib)
+    assert rc == 0 and st == oracle.ST_SLOT_OOR
+    _eq(kc[4], k[0], "k slot 4")
+    _eq(kc[0], k[3], "k slot 0")
+    _eq(vc[0], v[3], "v slot 0")
+    assert not kc[1:4].any() and not vc[1:4].any()
+    # argument errors
+    assert oracle.prepare_batch(rows, counts, completed, tok, T=-1, lib=lib)["rc"] == oracle.EINVAL
+    assert oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                       prep["seq_lens"], prep["positions"], bt, 0, NB,
+                                       lib=lib)["rc"] == oracle.EINVAL
+
+
+def pin_strided_kv(lib):
+    """K/V as strided views of a wider per-token buffer (e.g. a fused QKV output)."""
+    rng = np.random.default_rng(5)
+    T, H, D = 7, 2, 8
+    qkv = rng.integers(0, 65535, size=(T, 3, H, D), dtype=np.uint16)
+    k, v = qkv[:, 1], qkv[:, 2]
+    slots = np.array([3, 0, 9, 4, 7, 1, 2], np.int32)
+    kc = np.zeros((10, H, D), np.uint16)
+    vc = np.zeros((10, H, D), np.uint16)
+    rc, st = oracle.scatter_kv(k, v, kc, vc, slots, lib=lib)
+    assert rc == 0 and st == 0
+    _eq(kc[slots], k, "strided K")
+    _eq(vc[slots], v, "strided V")
+
+
+ALL_PINS = [pin_pages_example, pin_prefix_example, pin_budget_tie_example, pin_bruteforce,
+            pin_library_routines, pin_closed_forms, pin_invariants, pin_error_semantics,
+            pin_strided_kv]

@@ -1,0 +1,100 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins
+catch every one (a dropped term, a wrong sign or index, a transposed operand).
+
+Each mutant is oracle.c with one textual substitution, compiled with gcc into a
+temporary directory; the real oracle is never modified.  Mutants are chosen so
+that they stay memory-safe (the pins then fail on values, not on a crash).
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "sort_descending": (
+        "return a->tokens_this_step < b->tokens_this_step ? -1 : 1;",
+        "return a->tokens_this_step < b->tokens_this_step ? 1 : -1;"),
+    "tie_break_reversed": (
+        "return a->request_state_index < b->request_state_index ? -1 : 1;",
+        "return a->request_state_index < b->request_state_index ? 1 : -1;"),
+    "no_tie_break": (
+        "    if (a->request_state_index != b->request_state_index)\n"
+        "        return a->request_state_index < b->request_state_index ? -1 : 1;\n",
+        ""),
+    "prefix_not_running": (
+        "running += batch[b].tokens_this_step;",
+        "running = batch[b].tokens_this_step;"),
+    "position_off_by_one": (
+        "int64_t position = (int64_t)completed[row] + j;",
+        "int64_t position = (int64_t)completed[row] + j + 1;"),
+    "position_drops_history": (
+        "int64_t position = (int64_t)completed[row] + j;",
+        "int64_t position = j;"),
+    "seq_len_drops_history": (
+        "int64_t len = (int64_t)completed[row] + batch[b].tokens_this_step;",
+        "int64_t len = batch[b].tokens_this_step;"),
+    "seq_len_drops_new": (
+        "int64_t len = (int64_t)completed[row] + batch[b].tokens_this_step;",
+        "int64_t len = (int64_t)completed[row];"),
+    "input_ids_shifted": (
+        "input_ids[flat_token_index] = token_ids[(int64_t)row * token_stride + position];",
+        "input_ids[flat_token_index] = token_ids[(int64_t)row * token_stride + (position > 0 ? position - 1 : 0)];"),
+    "slot_drops_scale": (
+        "slot_mapping[flat_token_index] = physical_block_id * block_size + offset;",
+        "slot_mapping[flat_token_index] = physical_block_id + offset;"),
+    "slot_drops_offset": (
+        "slot_mapping[flat_token_index] = physical_block_id * block_size + offset;",
+        "slot_mapping[flat_token_index] = physical_block_id * block_size;"),
+    "offset_fixed_16": (
+        "int32_t offset = position % block_size;",
+        "int32_t offset = position & 15;"),
+    "block_table_transposed": (
+        "block_table[(int64_t)request_state_index * MB + logic_block];",
+        "block_table[((int64_t)logic_block * R + request_state_index) % ((int64_t)R * MB)];"),
+    "logic_block_rounds_up": (
+        "int32_t logic_block = position / block_size;",
+        "int32_t logic_block = (position + block_size - 1) / block_size;\n"
+        "            if (logic_block >= MB) logic_block = MB - 1;"),
+    "visible_floor": (
+        "int64_t visible = seq_len <= 0 ? 0 : ((int64_t)seq_len + block_size - 1) / block_size;",
+        "int64_t visible = seq_len <= 0 ? 0 : (int64_t)seq_len / block_size;"),
+    "scatter_k_from_v": (
+        "memcpy(kdst + slot_id * row_bytes, ksrc + (int64_t)flat_token_index * k_stride,",
+        "memcpy(kdst + slot_id * row_bytes, vsrc + (int64_t)flat_token_index * v_stride,"),
+    "scatter_source_row_shift": (
+        "memcpy(vdst + slot_id * row_bytes, vsrc + (int64_t)flat_token_index * v_stride,",
+        "memcpy(vdst + slot_id * row_bytes, vsrc + (int64_t)(flat_token_index ? flat_token_index - 1 : 0) * v_stride,"),
+    "scatter_ignores_stride": (
+        "memcpy(kdst + slot_id * row_bytes, ksrc + (int64_t)flat_token_index * k_stride,",
+        "memcpy(kdst + slot_id * row_bytes, ksrc + (int64_t)flat_token_index * row_bytes,"),
+    "bad_row_not_flagged": (
+        "            st |= ORC_ST_BAD_ROW;\n            seq_lens[b] = -1;",
+        "            seq_lens[b] = -1;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} must be unique"
+    path = tmp_path / "oracle_mutant.c"
+    path.write_text(source.replace(old, new))
+    so = oracle.build(str(path), str(tmp_path / "liboracle_mutant.so"), strict=False)
+    lib = oracle.load(so)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except Exception:  # a wrong value, or a shape the pins cannot even build
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} survived every pin"
