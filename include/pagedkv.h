@@ -1,0 +1,175 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv, the MI355X (gfx950) library that turns one
+ * inference step's schedule into flat GPU inputs and writes the new tokens' K/V
+ * into a paged KV cache.
+ *
+ * The operations are those of "Deep Dive into vLLM's Scheduling Mechanism: The
+ * Complete CPU-to-GPU Mapping Pipeline" (kongchang.com/en; Chinese original
+ * "vLLM调度机制深度解析：CPU到GPU的完整映射流程", kongchang.com):
+ *   pkv_prepare_batch        -- "Batch Construction and Sequence Flattening",
+ *                               "Contiguous Token Sequence Processing", seq_lens
+ *                               of "Complete Input Preparation for the Attention
+ *                               Module";
+ *   pkv_compute_slot_mapping -- "Multi-Layer Coordinate Conversion Pipeline" and
+ *                               "Address Calculation Example", one call per
+ *                               KV-cache group, plus the group's visible pages
+ *                               (input_block_tables);
+ *   pkv_scatter_kv           -- the write of each new token's K/V at its slot,
+ *                               one call per KV-cache group and layer.
+ *
+ * Conventions shared by every call
+ *   - Pointers named as device pointers must point to device memory (HBM) that
+ *     the caller owns, sized as stated; the library never allocates, frees or
+ *     keeps them.  Scalars are passed by value.
+ *   - All index arrays are int32, contiguous, row-major.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it: it never synchronizes, never allocates and keeps no
+ *     global state, so calls are reentrant.  Outputs are ready once the stream
+ *     reaches the point after the call.
+ *   - The return value reports errors found on the host from the arguments
+ *     alone; then nothing is enqueued and no output is touched.
+ *   - Errors in the *data* (found by the kernels) are OR-ed into `*status`, a
+ *     device uint32 the caller zeroes (it may be NULL: checks still run, nothing
+ *     is reported).  The affected outputs get the documented -1 values; no
+ *     kernel ever reads or writes outside the buffers described here.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+/* Return codes. */
+#define PKV_OK            0
+#define PKV_EINVAL       (-1)  /* NULL where data is needed, negative size, block_size <= 0, ... */
+#define PKV_EALIGN       (-2)  /* K/V row, stride or pointer not a multiple of 16 bytes          */
+#define PKV_EUNSUPPORTED (-3)  /* beyond a documented limit (e.g. n > PKV_MAX_BATCH)             */
+#define PKV_EHIP         (-4)  /* the HIP runtime refused the launch                              */
+
+/* Device status bits, OR-ed into *status. */
+#define PKV_ST_BAD_ROW    0x01u /* request_state_index outside [0, R)                 */
+#define PKV_ST_BAD_COUNT  0x02u /* negative scheduled-token count (read as 0)          */
+#define PKV_ST_TOKEN_SUM  0x04u /* sum of scheduled counts != T                        */
+#define PKV_ST_POS_OOR    0x08u /* position < 0, or >= token-table width L             */
+#define PKV_ST_LB_OOR     0x10u /* logical block >= block-table width MB               */
+#define PKV_ST_BLOCK_OOR  0x20u /* physical block id < 0 or >= num_blocks              */
+#define PKV_ST_SLOT_OOR   0x40u /* slot id >= num_slots of the cache                   */
+
+/* Largest batch (scheduled requests per step) one call accepts: the batch is
+ * ordered inside one workgroup's LDS. */
+#define PKV_MAX_BATCH 4096
+
+/*
+ * pkv_prepare_batch -- batch assembly and flattening.
+ *
+ * Inputs (device):
+ *   sched_rows[n]     request_state_index of each scheduled request, in any order
+ *   num_scheduled[n]  tokens each request runs this step (0 allowed: an empty run)
+ *   completed[R]      tokens each state row has already processed, *before* this
+ *                     step (the request_state's completed_tokens)
+ *   token_ids[R * token_stride]  persistent token table: token_ids[row *
+ *                     token_stride + p] is the id of the row's token at position
+ *                     p, valid for p < L (token_stride >= L)
+ * Outputs (device):
+ *   index_mapping[n]      batch_index -> request_state_index.  The batch is sorted
+ *                         by tokens this step, ascending; equal counts by
+ *                         request_state_index, ascending.  The result depends
+ *                         only on the set of (row, count) pairs, not their order.
+ *   query_start_loc[n+1]  prefix sum of the counts in batch order: request b owns
+ *                         flat tokens [query_start_loc[b], query_start_loc[b+1]).
+ *                         query_start_loc[0] = 0; sums saturate at INT32_MAX.
+ *   seq_lens[n]           completed + count (history plus new tokens).
+ *   positions[T]          completed[row] + j for the j-th token of its request.
+ *   input_ids[T]          token_ids[row][position].  May be NULL (then token_ids
+ *                         is not read).
+ * Data errors: a row outside [0, R) flags BAD_ROW, keeps its place in the order,
+ *   gets seq_len -1 and its tokens position -1 / input id -1; a negative count
+ *   flags BAD_COUNT and reads as 0; sum of counts != T flags TOKEN_SUM (tokens
+ *   past the last request get position -1 / input id -1, tokens beyond T are
+ *   dropped); a position outside [0, L) flags POS_OOR and gets input id -1.
+ *   Positions and seq_lens hold the low 32 bits of completed + offset.
+ * Host errors: EINVAL for n < 0, T < 0, R < 0, L < 0, token_stride < L when
+ *   input_ids is given, or a NULL pointer an enabled output needs;
+ *   EUNSUPPORTED for n > PKV_MAX_BATCH.
+ */
+int pkv_prepare_batch(int32_t n, int32_t T,
+                      const int32_t* sched_rows, const int32_t* num_scheduled,
+                      const int32_t* completed, int32_t R,
+                      const int32_t* token_ids, int64_t token_stride, int32_t L,
+                      int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
+                      int32_t* positions, int32_t* input_ids,
+                      uint32_t* status, void* stream);
+
+/*
+ * pkv_compute_slot_mapping -- physical write slots and visible pages for ONE
+ * KV-cache group (each group has its own block table, block size and pool).
+ *
+ * Inputs (device), as produced by pkv_prepare_batch:
+ *   index_mapping[n], query_start_loc[n+1] (non-decreasing, [0] = 0),
+ *   seq_lens[n] (read only when input_block_tables is not NULL), positions[T]
+ *   block_table[R * MB]  block_table[row * MB + i] = physical block of the row's
+ *                        i-th logical block
+ *   block_size, num_blocks  this group's block size and pool size;
+ *                        num_blocks * block_size must fit in int32
+ * Outputs (device):
+ *   slot_mapping[T]      for token t of request b with row = index_mapping[b]:
+ *                        slot = block_table[row][pos / block_size] * block_size
+ *                               + pos % block_size,   pos = positions[t].
+ *   input_block_tables[n * MB]  (may be NULL) row b = the first
+ *                        ceil(seq_lens[b] / block_size) entries of the request's
+ *                        block-table row; entries past them are not written.
+ * Data errors give slot -1: row outside [0, R) (BAD_ROW), position < 0
+ *   (POS_OOR), logical block >= MB (LB_OOR), block id outside [0, num_blocks)
+ *   (BLOCK_OOR).  Tokens outside [query_start_loc[0], query_start_loc[n]) get
+ *   slot -1 unflagged.  In input_block_tables, visible entries are copied as they
+ *   are (an out-of-pool one flags BLOCK_OOR), a visible count above MB flags
+ *   LB_OOR and is cut to MB, a bad row's output row is not written.
+ * Host errors: EINVAL for n < 0, T < 0, R < 0, MB < 0, num_blocks < 0,
+ *   block_size <= 0, num_blocks * block_size > 2^31, or a NULL pointer an
+ *   enabled output needs; EUNSUPPORTED for n > PKV_MAX_BATCH.
+ */
+int pkv_compute_slot_mapping(int32_t n, int32_t T,
+                             const int32_t* index_mapping, const int32_t* query_start_loc,
+                             const int32_t* seq_lens, const int32_t* positions,
+                             const int32_t* block_table, int32_t R, int32_t MB,
+                             int32_t block_size, int32_t num_blocks,
+                             int32_t* slot_mapping, int32_t* input_block_tables,
+                             uint32_t* status, void* stream);
+
+/*
+ * pkv_scatter_kv -- write each new token's K and V rows into ONE group's paged
+ * caches for ONE layer.
+ *
+ *   k, v         device; token t's row of row_bytes bytes (H x D x element size)
+ *                starts at k + t * k_stride (bytes), likewise v
+ *   k_cache, v_cache  device, each [num_slots][row_bytes], slot-major: slot s
+ *                starts at byte s * row_bytes
+ *   slot_mapping[T]   device, from pkv_compute_slot_mapping
+ * The payload is copied bit for bit (never converted).  A slot < 0 is skipped
+ * silently (padding); a slot >= num_slots flags SLOT_OOR and is skipped.  Slots
+ * must be unique among tokens with slot >= 0 (two tokens on one slot race).
+ * Host errors: EINVAL for T < 0, row_bytes <= 0, num_slots < 0, a stride below
+ *   row_bytes, or a NULL pointer with T > 0; EALIGN unless row_bytes, both
+ *   strides and all four data pointers are multiples of 16 bytes.
+ */
+int pkv_scatter_kv(int32_t T, int64_t row_bytes,
+                   const void* k, int64_t k_stride, const void* v, int64_t v_stride,
+                   void* k_cache, void* v_cache, int64_t num_slots,
+                   const int32_t* slot_mapping, uint32_t* status, void* stream);
+
+/* Static text for a return code (never NULL). */
+const char* pkv_error_string(int code);
+
+/* PKV_ABI_VERSION of the built library. */
+int pkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,25 @@
+"""paged_kv_input_amd -- MI355X (gfx950) library for one inference step's flat
+input tensors and the paged K/V write.
+
+The work runs in hand-written HIP kernels behind a C ABI (``libpagedkv.so``,
+declared in ``include/pagedkv.h``).  This package is a thin binding with the
+same call names: ``prepare_batch``, ``compute_slot_mapping`` (one call per
+KV-cache group) and ``scatter_kv`` (one call per group and layer).  It takes
+torch tensors for device memory and uses torch's current HIP stream; every
+step of the path runs in the library's kernels.  Importing an entry point loads
+the library and raises if it is missing -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+_API = ("prepare_batch", "compute_slot_mapping", "scatter_kv", "PagedKVError", "library_path",
+        "abi_version", "error_string", "load_library", "ST_BITS", "MAX_BATCH")
+
+__all__ = list(_API)
+
+
+def __getattr__(name):
+    if name in _API:
+        from . import api
+
+        return getattr(api, name)
+    raise AttributeError(name)

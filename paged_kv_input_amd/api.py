@@ -1,0 +1,201 @@
+"""ctypes binding of libpagedkv: argument marshalling only.
+
+Each function takes torch tensors (device memory), checks dtypes and shapes on
+the host, passes raw pointers and sizes to the C entry point of the same name
+(``pkv_*`` in include/pagedkv.h) on torch's current HIP stream, and raises
+``PagedKVError`` on a non-zero return code.  Nothing here computes any part of
+the path.  The library is loaded at import; a missing library is an ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.environ.get("PAGEDKV_LIB", os.path.join(_HERE, "libpagedkv.so"))
+
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+ST_BITS = {
+    "BAD_ROW": 0x01, "BAD_COUNT": 0x02, "TOKEN_SUM": 0x04, "POS_OOR": 0x08,
+    "LB_OOR": 0x10, "BLOCK_OOR": 0x20, "SLOT_OOR": 0x40,
+}
+MAX_BATCH = 4096
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn}: {error_string(code)} (code {code})")
+        self.code = code
+
+
+def load_library(path: str = library_path) -> ctypes.CDLL:
+    """Load libpagedkv and declare its signatures.  torch is imported first so
+    the library binds to the HIP runtime torch already loaded."""
+    if not os.path.exists(path):
+        raise ImportError(
+            f"libpagedkv not built at {path}: run `python __graft_entry__.py` or "
+            "`python paged_kv_input_amd/build.py` (no CPU fallback exists)")
+    lib = ctypes.CDLL(path)
+    lib.pkv_prepare_batch.restype = ctypes.c_int
+    lib.pkv_prepare_batch.argtypes = [_I32, _I32, _P, _P, _P, _I32, _P, _I64, _I32,
+                                      _P, _P, _P, _P, _P, _P, _P]
+    lib.pkv_compute_slot_mapping.restype = ctypes.c_int
+    lib.pkv_compute_slot_mapping.argtypes = [_I32, _I32, _P, _P, _P, _P, _P, _I32, _I32,
+                                             _I32, _I32, _P, _P, _P, _P]
+    lib.pkv_scatter_kv.restype = ctypes.c_int
+    lib.pkv_scatter_kv.argtypes = [_I32, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _P, _P]
+    lib.pkv_error_string.restype = ctypes.c_char_p
+    lib.pkv_error_string.argtypes = [ctypes.c_int]
+    lib.pkv_abi_version.restype = ctypes.c_int
+    lib.pkv_abi_version.argtypes = []
+    return lib
+
+
+_lib = load_library()
+
+
+def abi_version() -> int:
+    return int(_lib.pkv_abi_version())
+
+
+def error_string(code: int) -> str:
+    return _lib.pkv_error_string(code).decode()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _idx(name: str, t: Optional[torch.Tensor], shape=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor on the GPU")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _check(fn: str, rc: int):
+    if rc != OK:
+        raise PagedKVError(fn, rc)
+
+
+def prepare_batch(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, completed: torch.Tensor,
+                  token_ids: Optional[torch.Tensor], num_tokens: int, *,
+                  index_mapping: torch.Tensor, query_start_loc: torch.Tensor,
+                  seq_lens: torch.Tensor, positions: torch.Tensor,
+                  input_ids: Optional[torch.Tensor] = None,
+                  status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Batch assembly and flattening into caller-owned output tensors.
+
+    sched_rows, num_scheduled: int32 [n]; completed: int32 [R]; token_ids: int32
+    [R, L] with unit stride along L (row stride may be larger); num_tokens = T is
+    the host's sum of num_scheduled.  Outputs: index_mapping [n],
+    query_start_loc [n+1], seq_lens [n], positions [T], input_ids [T] (optional).
+    """
+    n = sched_rows.shape[0]
+    T = int(num_tokens)
+    _idx("sched_rows", sched_rows, (n,))
+    _idx("num_scheduled", num_scheduled, (n,))
+    _idx("completed", completed)
+    _idx("index_mapping", index_mapping, (n,))
+    _idx("query_start_loc", query_start_loc, (n + 1,))
+    _idx("seq_lens", seq_lens, (n,))
+    _idx("positions", positions, (T,))
+    _idx("input_ids", input_ids, (T,), optional=True)
+    R = completed.shape[0]
+    L, stride = 0, 0
+    if token_ids is not None:
+        if token_ids.dtype != torch.int32 or not token_ids.is_cuda or token_ids.dim() != 2 \
+                or token_ids.stride(1) != 1 or token_ids.shape[0] != R:
+            raise ValueError("token_ids must be an int32 [R, L] GPU tensor with unit column stride")
+        L, stride = token_ids.shape[1], token_ids.stride(0)
+    elif input_ids is not None:
+        raise ValueError("input_ids needs token_ids")
+    if status is not None and (status.dtype != torch.int32 or not status.is_cuda
+                               or status.numel() < 1):
+        raise ValueError("status must be an int32 GPU tensor (bit pattern of a uint32)")
+    rc = _lib.pkv_prepare_batch(n, T, _ptr(sched_rows), _ptr(num_scheduled), _ptr(completed), R,
+                                _ptr(token_ids), stride, L, _ptr(index_mapping),
+                                _ptr(query_start_loc), _ptr(seq_lens), _ptr(positions),
+                                _ptr(input_ids), _ptr(status), _stream(stream))
+    _check("prepare_batch", rc)
+
+
+def compute_slot_mapping(index_mapping: torch.Tensor, query_start_loc: torch.Tensor,
+                         seq_lens: Optional[torch.Tensor], positions: torch.Tensor,
+                         block_table: torch.Tensor, block_size: int, num_blocks: int, *,
+                         slot_mapping: torch.Tensor,
+                         input_block_tables: Optional[torch.Tensor] = None,
+                         status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write slots (and optionally visible pages) of ONE KV-cache group.
+
+    block_table: int32 [R, MB] contiguous; slot_mapping: int32 [T];
+    input_block_tables: int32 [n, MB] or None.
+    """
+    n = index_mapping.shape[0]
+    T = positions.shape[0]
+    _idx("index_mapping", index_mapping, (n,))
+    _idx("query_start_loc", query_start_loc, (n + 1,))
+    _idx("positions", positions, (T,))
+    _idx("block_table", block_table)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [R, MB]")
+    R, MB = block_table.shape
+    _idx("slot_mapping", slot_mapping, (T,))
+    _idx("input_block_tables", input_block_tables, (n, MB), optional=True)
+    if input_block_tables is not None:
+        _idx("seq_lens", seq_lens, (n,))
+    rc = _lib.pkv_compute_slot_mapping(n, T, _ptr(index_mapping), _ptr(query_start_loc),
+                                       _ptr(seq_lens), _ptr(positions), _ptr(block_table), R, MB,
+                                       int(block_size), int(num_blocks), _ptr(slot_mapping),
+                                       _ptr(input_block_tables), _ptr(status), _stream(stream))
+    _check("compute_slot_mapping", rc)
+
+
+def scatter_kv(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               slot_mapping: torch.Tensor, *, status: Optional[torch.Tensor] = None,
+               stream=None) -> None:
+    """Write token t's K/V rows to slot slot_mapping[t] of ONE group's caches.
+
+    k, v: [T, ...] GPU tensors whose per-token rows are contiguous (the token
+    stride may be larger, e.g. a view into a fused QKV buffer); k_cache, v_cache:
+    contiguous [num_slots, ...] with the same row size.  Any dtype: the payload
+    is copied bit for bit.
+    """
+    T = slot_mapping.shape[0]
+    _idx("slot_mapping", slot_mapping, (T,))
+    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not c.is_cuda or not c.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    row_bytes = k_cache[0].numel() * k_cache.element_size() if k_cache.shape[0] else \
+        (k_cache.numel() // max(k_cache.shape[0], 1)) * k_cache.element_size()
+    if v_cache.shape != k_cache.shape or v_cache.element_size() != k_cache.element_size():
+        raise ValueError("k_cache and v_cache must have the same shape and element size")
+    strides = []
+    for name, x in (("k", k), ("v", v)):
+        if not x.is_cuda or x.shape[0] != T:
+            raise ValueError(f"{name} must be a GPU tensor with {T} rows")
+        if T and (x[0].numel() * x.element_size() != row_bytes or not x[0].is_contiguous()):
+            raise ValueError(f"{name} rows must be contiguous and {row_bytes} bytes")
+        strides.append(x.stride(0) * x.element_size() if T else row_bytes)
+    rc = _lib.pkv_scatter_kv(T, row_bytes, _ptr(k), strides[0], _ptr(v), strides[1],
+                             _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _ptr(slot_mapping),
+                             _ptr(status), _stream(stream))
+    _check("scatter_kv", rc)

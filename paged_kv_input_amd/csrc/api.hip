@@ -1,0 +1,107 @@
+// api.hip -- the extern "C" entry points of libpagedkv: argument checks on the
+// host, then one stream-ordered launch per call.  The contract of each entry
+// point (layouts, outputs, error behaviour) is stated in include/pagedkv.h.
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;   // work-items per grid dimension
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int pkv_prepare_batch(int32_t n, int32_t T, const int32_t* sched_rows,
+                      const int32_t* num_scheduled, const int32_t* completed, int32_t R,
+                      const int32_t* token_ids, int64_t token_stride, int32_t L,
+                      int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
+                      int32_t* positions, int32_t* input_ids, uint32_t* status, void* stream)
+{
+    if (n < 0 || T < 0 || R < 0 || L < 0)
+        return PKV_EINVAL;
+    if (query_start_loc == nullptr)
+        return PKV_EINVAL;
+    if (n > 0 && (sched_rows == nullptr || num_scheduled == nullptr || index_mapping == nullptr ||
+                  seq_lens == nullptr || (R > 0 && completed == nullptr)))
+        return PKV_EINVAL;
+    if (T > 0 && positions == nullptr)
+        return PKV_EINVAL;
+    if (input_ids != nullptr && T > 0 &&
+        ((R > 0 && L > 0 && token_ids == nullptr) || token_stride < L))
+        return PKV_EINVAL;
+    if (n > PKV_MAX_BATCH)
+        return PKV_EUNSUPPORTED;
+    return from_hip(pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
+                                        token_stride, L, index_mapping, query_start_loc, seq_lens,
+                                        positions, input_ids, status,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int pkv_compute_slot_mapping(int32_t n, int32_t T, const int32_t* index_mapping,
+                             const int32_t* query_start_loc, const int32_t* seq_lens,
+                             const int32_t* positions, const int32_t* block_table, int32_t R,
+                             int32_t MB, int32_t block_size, int32_t num_blocks,
+                             int32_t* slot_mapping, int32_t* input_block_tables,
+                             uint32_t* status, void* stream)
+{
+    if (n < 0 || T < 0 || R < 0 || MB < 0 || num_blocks < 0 || block_size <= 0)
+        return PKV_EINVAL;
+    if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX + 1)
+        return PKV_EINVAL;
+    if (query_start_loc == nullptr || (n > 0 && index_mapping == nullptr))
+        return PKV_EINVAL;
+    if (T > 0 && (positions == nullptr || slot_mapping == nullptr))
+        return PKV_EINVAL;
+    if ((n > 0 || T > 0) && R > 0 && MB > 0 && block_table == nullptr)
+        return PKV_EINVAL;
+    if (input_block_tables != nullptr && n > 0 && seq_lens == nullptr)
+        return PKV_EINVAL;
+    if (n > PKV_MAX_BATCH)
+        return PKV_EUNSUPPORTED;
+    return from_hip(pkv::launch_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,
+                                      block_table, R, MB, block_size, num_blocks, slot_mapping,
+                                      input_block_tables, status,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int pkv_scatter_kv(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride, const void* v,
+                   int64_t v_stride, void* k_cache, void* v_cache, int64_t num_slots,
+                   const int32_t* slot_mapping, uint32_t* status, void* stream)
+{
+    if (T < 0 || row_bytes <= 0 || num_slots < 0 || k_stride < row_bytes || v_stride < row_bytes)
+        return PKV_EINVAL;
+    if (T > 0 && (k == nullptr || v == nullptr || slot_mapping == nullptr ||
+                  (num_slots > 0 && (k_cache == nullptr || v_cache == nullptr))))
+        return PKV_EINVAL;
+    if ((row_bytes & 15) != 0 || (k_stride & 15) != 0 || (v_stride & 15) != 0 || !aligned16(k) ||
+        !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_EALIGN;
+    // One lane per 16-byte chunk, a quarter of the chunks per lane at most.
+    if ((int64_t)T * (row_bytes / 16) / 4 >= kMaxGridThreads)
+        return PKV_EUNSUPPORTED;
+    return from_hip(pkv::launch_scatter(T, row_bytes, k, k_stride, v, v_stride, k_cache, v_cache,
+                                        num_slots, slot_mapping, status,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+const char* pkv_error_string(int code)
+{
+    switch (code) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EALIGN: return "K/V rows, strides and pointers must be 16-byte aligned";
+    case PKV_EUNSUPPORTED: return "beyond a documented limit of the library";
+    case PKV_EHIP: return "HIP launch failed";
+    default: return "unknown pagedkv error code";
+    }
+}
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// scatter.hip -- write each new token's K and V rows into a paged cache.
+//
+// slot_mapping is the write destination of this step's new K/V ("Multi-Layer
+// Coordinate Conversion Pipeline" of "Deep Dive into vLLM's Scheduling
+// Mechanism: The Complete CPU-to-GPU Mapping Pipeline", kongchang.com/en); a
+// slot is one token's K and V over all heads ("Address Calculation Example"),
+// here two caches of [num_slots][row_bytes].
+//
+// Design (gfx950): a pure HBM stream, no arithmetic.  The grid walks the
+// T x (row_bytes / 16) 16-byte chunks in flat order, so each wavefront reads
+// 1 KiB of consecutive K (and V) bytes and writes whole cache rows.  Every
+// lane issues kScatterUnroll K loads and as many V loads before its first
+// store, keeping enough bytes in flight per CU for HBM3E; the slot load of a
+// token is shared by its lanes.  Loads and stores are non-temporal: the
+// payload is touched once and the cache rows are not read back by this step.
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kScatterThreads = 256;
+constexpr int kScatterUnroll = 4;
+constexpr int kChunksPerBlock = kScatterThreads * kScatterUnroll;
+
+template <bool kPow2Row, bool kFull>
+__device__ inline void scatter_chunks(int64_t base, int64_t total_chunks, int32_t chunks_per_row,
+                                      int32_t row_shift, const u32x4* __restrict__ k,
+                                      int64_t k_stride16, const u32x4* __restrict__ v,
+                                      int64_t v_stride16, u32x4* __restrict__ k_cache,
+                                      u32x4* __restrict__ v_cache, int64_t num_slots,
+                                      const int32_t* __restrict__ slot_mapping, uint32_t& flags)
+{
+    int32_t slot[kScatterUnroll];
+    int64_t chunk[kScatterUnroll];
+    u32x4 kv[kScatterUnroll];
+    u32x4 vv[kScatterUnroll];
+
+    // Issue every load (slot words and payload) before the first use of any.
+#pragma unroll
+    for (int u = 0; u < kScatterUnroll; ++u) {
+        int64_t idx = base + (int64_t)u * kScatterThreads;
+        const bool live = kFull || idx < total_chunks;
+        if (!live)
+            idx = 0;                    // a safe in-bounds address; result unused
+        const int64_t t = kPow2Row ? (idx >> row_shift) : idx / chunks_per_row;
+        chunk[u] = idx - t * chunks_per_row;
+        slot[u] = live ? slot_mapping[t] : -1;
+        kv[u] = __builtin_nontemporal_load(k + t * k_stride16 + chunk[u]);
+        vv[u] = __builtin_nontemporal_load(v + t * v_stride16 + chunk[u]);
+    }
+    // Pin the payload in registers here.  Without this the compiler sinks the
+    // loads into the store branches below, after the slot test, and the lane
+    // then has one load in flight at a time instead of 2 * kScatterUnroll.
+#pragma unroll
+    for (int u = 0; u < kScatterUnroll; ++u)
+        __asm__ volatile("" : "+v"(kv[u]), "+v"(vv[u]));
+#pragma unroll
+    for (int u = 0; u < kScatterUnroll; ++u) {
+        if (slot[u] < 0)
+            continue;                   // padding token: nothing to write
+        if ((int64_t)slot[u] >= num_slots) {
+            flags |= PKV_ST_SLOT_OOR;
+            continue;
+        }
+        const int64_t dst = (int64_t)slot[u] * chunks_per_row + chunk[u];
+        __builtin_nontemporal_store(kv[u], k_cache + dst);
+        __builtin_nontemporal_store(vv[u], v_cache + dst);
+    }
+}
+
+template <bool kPow2Row>
+__global__ __launch_bounds__(kScatterThreads) void k_scatter(
+    int64_t total_chunks, int32_t chunks_per_row, int32_t row_shift,
+    const u32x4* __restrict__ k, int64_t k_stride16, const u32x4* __restrict__ v,
+    int64_t v_stride16, u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
+    int64_t num_slots, const int32_t* __restrict__ slot_mapping, uint32_t* __restrict__ status)
+{
+    const int64_t block0 = (int64_t)blockIdx.x * kChunksPerBlock;
+    const int64_t base = block0 + threadIdx.x;
+    uint32_t flags = 0;
+    if (block0 + kChunksPerBlock <= total_chunks)
+        scatter_chunks<kPow2Row, true>(base, total_chunks, chunks_per_row, row_shift, k,
+                                       k_stride16, v, v_stride16, k_cache, v_cache, num_slots,
+                                       slot_mapping, flags);
+    else
+        scatter_chunks<kPow2Row, false>(base, total_chunks, chunks_per_row, row_shift, k,
+                                        k_stride16, v, v_stride16, k_cache, v_cache, num_slots,
+                                        slot_mapping, flags);
+    report_status(status, flags);
+}
+
+}  // namespace
+
+hipError_t launch_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride,
+                          const void* v, int64_t v_stride, void* k_cache, void* v_cache,
+                          int64_t num_slots, const int32_t* slot_mapping, uint32_t* status,
+                          hipStream_t stream)
+{
+    const int64_t chunks_per_row = row_bytes / 16;
+    const int64_t total = (int64_t)T * chunks_per_row;
+    if (total == 0)
+        return hipSuccess;
+    const int64_t blocks = (total + kChunksPerBlock - 1) / kChunksPerBlock;
+    const bool pow2 = (chunks_per_row & (chunks_per_row - 1)) == 0;
+    const int32_t shift = pow2 ? __builtin_ctzll((unsigned long long)chunks_per_row) : 0;
+    const u32x4* kp = static_cast<const u32x4*>(k);
+    const u32x4* vp = static_cast<const u32x4*>(v);
+    u32x4* kc = static_cast<u32x4*>(k_cache);
+    u32x4* vc = static_cast<u32x4*>(v_cache);
+    if (pow2)
+        k_scatter<true><<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(
+            total, (int32_t)chunks_per_row, shift, kp, k_stride / 16, vp, v_stride / 16, kc, vc,
+            num_slots, slot_mapping, status);
+    else
+        k_scatter<false><<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(
+            total, (int32_t)chunks_per_row, shift, kp, k_stride / 16, vp, v_stride / 16, kc, vc,
+            num_slots, slot_mapping, status);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,114 @@
+"""One step of the path on the GPU: prepare_batch, then per KV-cache group
+compute_slot_mapping and scatter_kv, into device buffers this object owns.
+
+It only allocates and holds torch tensors and calls the library's three entry
+points in order on one stream; every computation runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import api
+
+
+@dataclass
+class GroupSpec:
+    """Host description of one KV-cache group for a step."""
+
+    block_table: np.ndarray     # int32 [R, MB]
+    block_size: int
+    num_blocks: int
+    k: np.ndarray               # [T, H, D] payload words (any dtype, copied as bits)
+    v: np.ndarray
+
+
+class DeviceStep:
+    """Device-resident inputs, outputs and paged caches for one step."""
+
+    def __init__(self, sched_rows, num_scheduled, completed, token_ids,
+                 groups: Sequence[GroupSpec], *, device="cuda", cache_fill: Optional[int] = None,
+                 ibt_fill: Optional[int] = None, with_input_ids: bool = True,
+                 with_block_tables: bool = True):
+        dev = torch.device(device)
+
+        def up(a, dtype=None):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            if dtype is not None:
+                t = t.to(dtype)
+            return t.to(dev)
+
+        self.device = dev
+        self.sched_rows = up(np.asarray(sched_rows, np.int32))
+        self.num_scheduled = up(np.asarray(num_scheduled, np.int32))
+        self.completed = up(np.asarray(completed, np.int32))
+        self.token_ids = up(np.asarray(token_ids, np.int32)) if with_input_ids else None
+        self.n = int(self.sched_rows.shape[0])
+        self.T = int(np.maximum(np.asarray(num_scheduled, np.int64), 0).sum())
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.index_mapping = torch.empty(self.n, **i32)
+        self.query_start_loc = torch.empty(self.n + 1, **i32)
+        self.seq_lens = torch.empty(self.n, **i32)
+        self.positions = torch.empty(self.T, **i32)
+        self.input_ids = torch.empty(self.T, **i32) if with_input_ids else None
+        self.status = torch.zeros(1, **i32)
+        self.groups: List[dict] = []
+        for g in groups:
+            bt = up(np.asarray(g.block_table, np.int32))
+            k = up(np.ascontiguousarray(g.k).view(np.int16))
+            v = up(np.ascontiguousarray(g.v).view(np.int16))
+            row_shape = tuple(k.shape[1:])
+            num_slots = int(g.num_blocks) * int(g.block_size)
+            kc = torch.empty((num_slots, *row_shape), dtype=k.dtype, device=dev)
+            vc = torch.empty((num_slots, *row_shape), dtype=k.dtype, device=dev)
+            if cache_fill is not None:
+                kc.fill_(cache_fill)
+                vc.fill_(cache_fill)
+            ibt = None
+            if with_block_tables:
+                ibt = torch.empty((self.n, bt.shape[1]), **i32)
+                if ibt_fill is not None:
+                    ibt.fill_(ibt_fill)
+            self.groups.append(dict(block_table=bt, block_size=int(g.block_size),
+                                    num_blocks=int(g.num_blocks), k=k, v=v, k_cache=kc,
+                                    v_cache=vc, slot_mapping=torch.empty(self.T, **i32),
+                                    input_block_tables=ibt))
+
+    # -- the three calls -------------------------------------------------------
+    def prepare(self, stream=None):
+        api.prepare_batch(self.sched_rows, self.num_scheduled, self.completed, self.token_ids,
+                          self.T, index_mapping=self.index_mapping,
+                          query_start_loc=self.query_start_loc, seq_lens=self.seq_lens,
+                          positions=self.positions, input_ids=self.input_ids,
+                          status=self.status, stream=stream)
+
+    def slots(self, gi: int, stream=None):
+        g = self.groups[gi]
+        api.compute_slot_mapping(self.index_mapping, self.query_start_loc, self.seq_lens,
+                                 self.positions, g["block_table"], g["block_size"],
+                                 g["num_blocks"], slot_mapping=g["slot_mapping"],
+                                 input_block_tables=g["input_block_tables"], status=self.status,
+                                 stream=stream)
+
+    def scatter(self, gi: int, stream=None):
+        g = self.groups[gi]
+        api.scatter_kv(g["k"], g["v"], g["k_cache"], g["v_cache"], g["slot_mapping"],
+                       status=self.status, stream=stream)
+
+    def run(self, stream=None):
+        """One whole step: prepare, then every group's slots and scatter."""
+        self.prepare(stream)
+        for gi in range(len(self.groups)):
+            self.slots(gi, stream)
+        for gi in range(len(self.groups)):
+            self.scatter(gi, stream)
+
+    def status_bits(self) -> int:
+        return int(self.status.item()) & 0xFFFFFFFF
+
+    def host(self, name: str, gi: Optional[int] = None) -> np.ndarray:
+        t = self.groups[gi][name] if gi is not None else getattr(self, name)
+        return t.cpu().numpy()

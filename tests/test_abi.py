@@ -1,0 +1,101 @@
+"""The C-ABI library on the CPU host: it loads, exports every entry point the
+public header declares, and rejects bad arguments on the host before any HIP
+call (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+
+
+def declared_macros():
+    text = open(HEADER).read()
+    return dict((m, int(v, 0)) for m, v in re.findall(r"#define\s+(PKV_\w+)\s+\(?(-?\w+)u?\)?", text)
+                if re.fullmatch(r"-?(0x[0-9a-fA-F]+|\d+)", v.rstrip("u")) for v in [v.rstrip("u")])
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_input_amd import api
+
+    return api._lib
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == ["pkv_abi_version", "pkv_compute_slot_mapping", "pkv_error_string",
+                     "pkv_prepare_batch", "pkv_scatter_kv"]
+    for name in names:
+        assert hasattr(lib, name), name
+    so = os.path.join(ROOT, "paged_kv_input_amd", "libpagedkv.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", so], check=True, capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (pkv_\w+)", out))
+    assert exported == set(names), exported ^ set(names)
+
+
+def test_constants_match_binding(lib):
+    from paged_kv_input_amd import api
+    import oracle
+
+    m = declared_macros()
+    assert lib.pkv_abi_version() == m["PKV_ABI_VERSION"]
+    assert api.MAX_BATCH == m["PKV_MAX_BATCH"]
+    for name, bit in api.ST_BITS.items():
+        assert m["PKV_ST_" + name] == bit
+        assert getattr(oracle, "ST_" + name) == bit
+    for code in ("OK", "EINVAL", "EALIGN", "EUNSUPPORTED", "EHIP"):
+        assert m["PKV_" + code] == getattr(api, code)
+    for code in (0, -1, -2, -3, -4, 99):
+        assert api.error_string(code)
+
+
+def test_host_argument_errors(lib):
+    """Each of these returns before anything is enqueued (no HIP call)."""
+    N = None
+    P = ctypes.c_void_p
+    fake = P(0x1000)          # never dereferenced: validation fails first
+    EINVAL, EALIGN, EUNSUP = -1, -2, -3
+    prep = lib.pkv_prepare_batch
+    assert prep(-1, 0, fake, fake, fake, 1, fake, 1, 1, fake, fake, fake, fake, fake, N, N) == EINVAL
+    assert prep(1, -1, fake, fake, fake, 1, fake, 1, 1, fake, fake, fake, fake, fake, N, N) == EINVAL
+    assert prep(1, 1, fake, fake, fake, 1, fake, 1, 1, fake, N, fake, fake, fake, N, N) == EINVAL
+    assert prep(1, 1, N, fake, fake, 1, fake, 1, 1, fake, fake, fake, fake, fake, N, N) == EINVAL
+    assert prep(1, 1, fake, fake, fake, 1, fake, 1, 1, fake, fake, fake, N, fake, N, N) == EINVAL
+    assert prep(1, 1, fake, fake, fake, 1, fake, 3, 4, fake, fake, fake, fake, fake, N, N) == EINVAL
+    assert prep(4097, 1, fake, fake, fake, 1, fake, 1, 1, fake, fake, fake, fake, fake, N, N) == EUNSUP
+    slots = lib.pkv_compute_slot_mapping
+    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 0, 4, fake, N, N, N) == EINVAL
+    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 16, -1, fake, N, N, N) == EINVAL
+    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 1 << 16, 1 << 16, fake, N, N, N) == EINVAL
+    assert slots(1, 1, fake, fake, N, fake, fake, 1, 1, 16, 4, fake, fake, N, N) == EINVAL
+    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 16, 4, N, N, N, N) == EINVAL
+    assert slots(4097, 1, fake, fake, fake, fake, fake, 1, 1, 16, 4, fake, N, N, N) == EUNSUP
+    sc = lib.pkv_scatter_kv
+    assert sc(-1, 16, fake, 16, fake, 16, fake, fake, 4, fake, N, N) == EINVAL
+    assert sc(1, 16, fake, 8, fake, 16, fake, fake, 4, fake, N, N) == EINVAL
+    assert sc(1, 16, N, 16, fake, 16, fake, fake, 4, fake, N, N) == EINVAL
+    assert sc(1, 24, fake, 32, fake, 32, fake, fake, 4, fake, N, N) == EALIGN
+    assert sc(1, 16, P(0x1008), 16, fake, 16, fake, fake, 4, fake, N, N) == EALIGN
+    assert sc(1, 16, fake, 24, fake, 16, fake, fake, 4, fake, N, N) == EALIGN
+    assert sc(1, 16, fake, 16, fake, 16, fake, P(0x1004), 4, fake, N, N) == EALIGN
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import paged_kv_input_amd as pkv
+
+    x = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pkv.compute_slot_mapping(x, torch.zeros(4, dtype=torch.int32), x, x,
+                                 torch.zeros(2, 2, dtype=torch.int32), 16, 4, slot_mapping=x)

@@ -1,0 +1,179 @@
+"""HIP path against the CPU oracle, element by element, on seeded inputs.
+
+Index tensors and caches must be bit-exact: the path is integer index
+arithmetic plus a bit copy, so there is no tolerance anywhere.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import (SENTINEL16, assert_equal, compare_caches_at_slots, compare_caches_full,
+                      compare_indices, device_step, oracle_chain, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_input_amd  # noqa: F401  (raises if the library is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+def run_and_compare(batch, full_cache=True):
+    import torch
+
+    say(f"[case] {batch.name} seed={batch.seed} n={batch.n} T={batch.T} "
+        f"groups={[(g.block_size, g.num_blocks) for g in batch.groups]}")
+    step = device_step(batch)
+    step.run()
+    torch.cuda.synchronize()
+    prep, groups_o = oracle_chain(batch, lazy_caches=not full_cache)
+    compare_indices(step, prep, groups_o)
+    want = prep["status"]
+    for go in groups_o:
+        want |= go["status"] | go["scatter_status"]
+    assert step.status_bits() == want, (step.status_bits(), want)
+    if full_cache:
+        compare_caches_full(step, groups_o)
+    else:
+        compare_caches_at_slots(step, batch, groups_o)
+    return step, prep, groups_o
+
+
+def test_pages_example():
+    b = workloads.pages_example()
+    step, prep, go = run_and_compare(b)
+    # the values the article prints, read straight off the GPU
+    assert step.host("query_start_loc").tolist() == [0, 1, 9]
+    assert step.host("positions").tolist() == [31] + list(range(16, 24))
+    assert int(step.host("slot_mapping", 0)[0]) == 207
+    assert step.host("slot_mapping", 0)[1:].tolist() == list(range(704, 712))
+
+
+@pytest.mark.parametrize("maker", [workloads.prefix_reuse_example, workloads.budget_tie_example],
+                         ids=["prefix_reuse", "budget_tie"])
+def test_page_examples_other(maker):
+    run_and_compare(maker())
+
+
+@pytest.mark.parametrize("name", ["seeded_16req", "seeded_16req_decode50"])
+def test_seeded_small(name):
+    run_and_compare(workloads.make(name))
+
+
+@pytest.mark.parametrize("name", ["decode_256x1", "mixed_8192", "prefill_16x2048",
+                                  "two_groups_512req"])
+def test_reduced(name):
+    run_and_compare(workloads.make(name, reduced=True), full_cache=False)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_tiny_random(seed):
+    b = workloads.random_tiny(1000 + seed, zero_counts=(seed % 4 == 3))
+    run_and_compare(b)
+
+
+@pytest.mark.parametrize("name", ["decode_256x1", "mixed_8192", "prefill_16x2048",
+                                  "two_groups_512req"])
+def test_full_size(name):
+    """Full configuration sizes, the launch configuration the benchmark times."""
+    import torch
+
+    b = workloads.make(name)
+    run_and_compare(b, full_cache=False)
+    torch.cuda.empty_cache()
+
+
+def test_shuffled_schedule_same_outputs():
+    b = workloads.make("mixed_8192", reduced=True)
+    s1 = device_step(b)
+    s1.run()
+    perm = np.random.default_rng(9).permutation(b.n)
+    b.sched_rows, b.num_scheduled = b.sched_rows[perm], b.num_scheduled[perm]
+    s2 = device_step(b)
+    s2.run()
+    for key in ("index_mapping", "query_start_loc", "seq_lens", "positions", "input_ids"):
+        assert_equal(key, s2.host(key), s1.host(key))
+    assert_equal("slot_mapping", s2.host("slot_mapping", 0), s1.host("slot_mapping", 0))
+
+
+def test_max_batch():
+    """n = PKV_MAX_BATCH requests (the LDS sort's limit), counts 0..3, ties galore."""
+    import paged_kv_input_amd as pkv
+
+    rng = np.random.default_rng(21)
+    n, R, L, bs = pkv.MAX_BATCH, pkv.MAX_BATCH + 100, 64, 16
+    rows = rng.choice(R, n, replace=False).astype(np.int32)
+    counts = rng.integers(0, 4, n).astype(np.int32)
+    completed = np.zeros(R, np.int32)
+    completed[rows] = rng.integers(0, 60, n)
+    MB = L // bs
+    need = int(sum(max(0, -(-(int(completed[r]) + int(c)) // bs) - int(completed[r]) // bs)
+                   for r, c in zip(rows, counts)))
+    NB = need + 7
+    bt = workloads._block_table(rng, R, MB, NB, bs, rows, counts, completed)
+    T = int(counts.sum())
+    k = rng.integers(0, 65535, (T, 1, 8), dtype=np.uint16)
+    v = rng.integers(0, 65535, (T, 1, 8), dtype=np.uint16)
+    b = workloads.Batch("max_batch", 21, rows, counts, completed,
+                        rng.integers(0, 1000, (R, L), dtype=np.int32),
+                        [workloads.KVGroup(bs, NB, MB, bt, 1, 8, "fp16", k, v)])
+    run_and_compare(b)
+
+
+def test_empty_and_degenerate():
+    import torch
+    from paged_kv_input_amd.step import DeviceStep, GroupSpec
+
+    # n = 0, T = 0: only query_start_loc[0] = 0 is produced
+    bt = np.full((4, 2), -1, np.int32)
+    g = GroupSpec(bt, 16, 8, np.zeros((0, 1, 8), np.uint16), np.zeros((0, 1, 8), np.uint16))
+    s = DeviceStep(np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros(4, np.int32),
+                   np.zeros((4, 8), np.int32), [g], cache_fill=SENTINEL16)
+    s.query_start_loc.fill_(77)
+    s.run()
+    torch.cuda.synchronize()
+    assert s.host("query_start_loc").tolist() == [0]
+    assert s.status_bits() == 0
+    # every request with an empty run: rows ordered, no tokens, nothing written
+    b = workloads.random_tiny(5)
+    b.num_scheduled[:] = 0
+    for gg in b.groups:
+        gg.k, gg.v = gg.k[:0], gg.v[:0]
+    run_and_compare(b)
+
+
+def test_strided_kv_and_payload_widths():
+    """K/V as views into a fused per-token buffer; 1-, 2- and 4-byte payloads;
+    a row of 48 chunks (not a power of two) and a block size of 3."""
+    import torch
+    import paged_kv_input_amd as pkv
+
+    rng = np.random.default_rng(33)
+    for dtype, H, D, bs in ((torch.int8, 2, 64, 16), (torch.int16, 3, 128, 3),
+                            (torch.int32, 4, 32, 64)):
+        T = 300
+        NB = -(-400 // bs)
+        num_slots = NB * bs
+        say(f"[case] strided dtype={dtype} H={H} D={D} bs={bs}")
+        fused = torch.randint(-100, 100, (T, 3, H, D), dtype=torch.int32).to(dtype).cuda()
+        k, v = fused[:, 1], fused[:, 2]
+        slots = rng.choice(num_slots, T, replace=False).astype(np.int32)
+        slots[::17] = -1                             # padding tokens
+        kc = torch.zeros((num_slots, H, D), dtype=dtype, device="cuda")
+        vc = torch.zeros_like(kc)
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        pkv.scatter_kv(k, v, kc, vc, torch.from_numpy(slots).cuda(), status=st)
+        torch.cuda.synchronize()
+        ko = np.zeros((num_slots, H, D), dtype=kc.cpu().numpy().dtype)
+        vo = np.zeros_like(ko)
+        rc, ost = oracle.scatter_kv(k.cpu().numpy(), v.cpu().numpy(), ko, vo, slots)
+        assert rc == 0 and ost == 0 and int(st.item()) == 0
+        assert_equal("k_cache", kc.cpu().numpy(), ko)
+        assert_equal("v_cache", vc.cpu().numpy(), vo)
