@@ -75,14 +75,14 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(workload, kernel_src):
-    """HBM bytes per scatter launch from the committed rocprofv3 counter summary,
-    when it was taken on the current scatter source; else None."""
-    path = os.path.join(ROOT, "profiles", f"scatter_kv_{workload}_hbm_counters.md")
+def traffic_from_profile(kernel, workload, kernel_src):
+    """HBM bytes per launch of the kernel from the committed rocprofv3 counter
+    summary, when it was taken on the kernel's current source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m_src = re.search(r"scatter_source_sha256_16:\s*([0-9a-f]{16})", text)
+    m_src = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m_src and m_b) or m_src.group(1) != source_digest(kernel_src):
         return None
@@ -156,47 +156,79 @@ def main():
         torch.cuda.synchronize()
 
     ng = len(batch.groups)
-    for _ in range(args.warmup):
-        if not args.no_flush:
-            flush.fill_(1)
-        step.run(stream)
-    torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(1)
-        e = ev[i]
-        e[0].record(stream)
+    def timed(run_fn, marks):
+        """W warm-up steps, then exactly K timed steps (cache flush before each,
+        outside the events); returns per-step lists of event intervals."""
+        for _ in range(args.warmup):
+            if not args.no_flush:
+                flush.fill_(1)
+            run_fn(None)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)]
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for i in range(args.steps):
+            if not args.no_flush:
+                flush.fill_(1)
+            run_fn(ev[i])
+        torch.cuda.synchronize()
+        return ev, time.perf_counter() - w0
+
+    def calls(e):
+        # prepare_batch | compute_slot_mapping per group | scatter_kv per group
+        if e is not None:
+            e[0].record(stream)
         step.prepare(stream)
-        e[1].record(stream)
+        if e is not None:
+            e[1].record(stream)
         for gi in range(ng):
             step.slots(gi, stream)
-        e[2].record(stream)
+        if e is not None:
+            e[2].record(stream)
         for gi in range(ng):
             step.scatter(gi, stream)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+        if e is not None:
+            e[3].record(stream)
+
+    def fused(e):
+        if e is not None:
+            e[0].record(stream)
+        step.run_fused(stream)
+        if e is not None:
+            e[1].record(stream)
+
+    ev_c, wall_c = timed(calls, 4)
+    ev_f, wall_f = timed(fused, 2)
     if step.status_bits() != 0:
         raise RuntimeError(f"device status bits set: {step.status_bits():#x}")
 
-    step_ms = [e[0].elapsed_time(e[3]) for e in ev]
-    prep_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    slot_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    scat_ms = [e[2].elapsed_time(e[3]) for e in ev]
-    ms = statistics.fmean(step_ms)
+    calls_ms = [e[0].elapsed_time(e[3]) for e in ev_c]
+    prep_ms = [e[0].elapsed_time(e[1]) for e in ev_c]
+    slot_ms = [e[1].elapsed_time(e[2]) for e in ev_c]
+    scat_ms = [e[2].elapsed_time(e[3]) for e in ev_c]
+    fused_ms = [e[0].elapsed_time(e[1]) for e in ev_f]
     T = batch.T
     ab = algorithmic_bytes(batch)
+    use_fused = statistics.fmean(fused_ms) <= statistics.fmean(calls_ms)
+    step_ms = fused_ms if use_fused else calls_ms
+    ms = statistics.fmean(step_ms)
 
-    # Dominant kernel: scatter_kv (all but a few kB of the step's bytes).
-    scat_launch_ms = statistics.fmean(scat_ms) / ng
-    scat_bytes = statistics.fmean(scatter_bytes_per_launch(batch, gi) for gi in range(ng))
-    achieved = scat_bytes / (scat_launch_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(args.workload,
-                                   os.path.join(ROOT, "paged_kv_input_amd", "csrc", "scatter.hip"))
+    # Dominant kernel: the one launch of the fused step (all of the step's
+    # bytes), or scatter_kv when the separate calls are faster.
+    if use_fused:
+        kernel, launch_ms, kbytes = "pkv_step (k_step)", ms, ab["total"]
+        src = os.path.join(ROOT, "paged_kv_input_amd", "csrc", "step.hip")
+        prof_key = "step"
+    else:
+        kernel = "scatter_kv (k_scatter)"
+        launch_ms = statistics.fmean(scat_ms) / ng
+        kbytes = statistics.fmean(scatter_bytes_per_launch(batch, gi) for gi in range(ng))
+        src = os.path.join(ROOT, "paged_kv_input_amd", "csrc", "scatter.hip")
+        prof_key = "scatter_kv"
+    achieved = kbytes / (launch_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(prof_key, args.workload, src)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -225,27 +257,39 @@ def main():
             "cache_state": "cold (1 GiB rewrite before each step)" if not args.no_flush else "warm",
         },
         "step": {
+            "path": "pkv_step (one launch)" if use_fused else "three calls",
             "algorithmic_bytes": ab["total"],
             "hbm_gbs": ab["total"] / (ms * 1e-3) / 1e9,
             "frac_of_peak": ab["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "ms_median": statistics.median(step_ms),
             "ms_p10": sorted(step_ms)[len(step_ms) // 10],
             "ms_p90": sorted(step_ms)[(9 * len(step_ms)) // 10],
-            "prepare_ms": statistics.fmean(prep_ms),
-            "slot_mapping_ms": statistics.fmean(slot_ms),
-            "scatter_ms": statistics.fmean(scat_ms),
-            "wall_ms_per_step_incl_flush": wall * 1e3 / args.steps,
+            "wall_ms_per_step_incl_flush": (wall_f if use_fused else wall_c) * 1e3 / args.steps,
+        },
+        "three_calls": {
+            "ms_per_step": statistics.fmean(calls_ms),
+            "tokens_per_s": T / (statistics.fmean(calls_ms) * 1e-3),
+            "prepare_batch_ms": statistics.fmean(prep_ms),
+            "compute_slot_mapping_ms": statistics.fmean(slot_ms),
+            "scatter_kv_ms": statistics.fmean(scat_ms),
+            "scatter_kv_gbs": statistics.fmean(scatter_bytes_per_launch(batch, gi)
+                                               for gi in range(ng)) * ng
+            / (statistics.fmean(scat_ms) * 1e-3) / 1e9,
+        },
+        "fused": {
+            "ms_per_step": statistics.fmean(fused_ms),
+            "tokens_per_s": T / (statistics.fmean(fused_ms) * 1e-3),
         },
         "roofline": {
-            "kernel": "scatter_kv",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": scat_bytes,
-            "launch_ms": scat_launch_ms,
+            "algorithmic_bytes_per_launch": kbytes,
+            "launch_ms": launch_ms,
         },
         "cpu_baseline": ({k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
                          if cpu else None),

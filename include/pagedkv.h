@@ -55,7 +55,7 @@ extern "C" {
 #define PKV_ST_BAD_ROW    0x01u /* request_state_index outside [0, R)                 */
 #define PKV_ST_BAD_COUNT  0x02u /* negative scheduled-token count (read as 0)          */
 #define PKV_ST_TOKEN_SUM  0x04u /* sum of scheduled counts != T                        */
-#define PKV_ST_POS_OOR    0x08u /* position < 0, or >= token-table width L             */
+#define PKV_ST_POS_OOR    0x08u /* position < 0, or >= token-table width L (input_ids)  */
 #define PKV_ST_LB_OOR     0x10u /* logical block >= block-table width MB               */
 #define PKV_ST_BLOCK_OOR  0x20u /* physical block id < 0 or >= num_blocks              */
 #define PKV_ST_SLOT_OOR   0x40u /* slot id >= num_slots of the cache                   */
@@ -91,7 +91,8 @@ extern "C" {
  *   gets seq_len -1 and its tokens position -1 / input id -1; a negative count
  *   flags BAD_COUNT and reads as 0; sum of counts != T flags TOKEN_SUM (tokens
  *   past the last request get position -1 / input id -1, tokens beyond T are
- *   dropped); a position outside [0, L) flags POS_OOR and gets input id -1.
+ *   dropped); a negative position, or one >= L when input_ids is produced,
+ *   flags POS_OOR and gets input id -1.
  *   Positions and seq_lens hold the low 32 bits of completed + offset.
  * Host errors: EINVAL for n < 0, T < 0, R < 0, L < 0, token_stride < L when
  *   input_ids is given, or a NULL pointer an enabled output needs;
@@ -161,6 +162,56 @@ int pkv_scatter_kv(int32_t T, int64_t row_bytes,
                    const void* k, int64_t k_stride, const void* v, int64_t v_stride,
                    void* k_cache, void* v_cache, int64_t num_slots,
                    const int32_t* slot_mapping, uint32_t* status, void* stream);
+
+/*
+ * pkv_step -- a whole step in ONE call: pkv_prepare_batch, then for every
+ * KV-cache group pkv_compute_slot_mapping and pkv_scatter_kv (the first layer's
+ * K/V).  The outputs, status bits and return codes are exactly those of that
+ * sequence of calls; later layers reuse each group's slot_mapping with
+ * pkv_scatter_kv.  With n <= PKV_STEP_MAX_BATCH and 1 <= num_groups <=
+ * PKV_STEP_MAX_GROUPS everything runs in a single kernel launch; otherwise the
+ * call enqueues the separate kernels of that sequence.
+ *
+ * The schedule and per-request outputs are as for pkv_prepare_batch (R and the
+ * token table are shared by all groups).  groups is a HOST array of num_groups
+ * descriptors whose pointers are device pointers:
+ *   block_table[R * MB], block_size, num_blocks     as for pkv_compute_slot_mapping
+ *   slot_mapping[T] (out), input_block_tables[n * MB] (out, may be NULL)
+ *   k, k_stride, v, v_stride, k_cache, v_cache, num_slots, row_bytes
+ *                                                   as for pkv_scatter_kv
+ *   reserved                                        must be 0
+ * Host errors: those of the three calls for the same arguments; EINVAL also for
+ *   num_groups < 0, groups == NULL with num_groups > 0, or reserved != 0.
+ */
+#define PKV_STEP_MAX_BATCH 512
+#define PKV_STEP_MAX_GROUPS 4
+
+typedef struct pkv_group {
+    const int32_t* block_table;
+    int32_t* slot_mapping;
+    int32_t* input_block_tables;
+    const void* k;
+    const void* v;
+    void* k_cache;
+    void* v_cache;
+    int64_t k_stride;
+    int64_t v_stride;
+    int64_t num_slots;
+    int64_t row_bytes;
+    int32_t MB;
+    int32_t block_size;
+    int32_t num_blocks;
+    int32_t reserved;
+} pkv_group;
+
+int pkv_step(int32_t n, int32_t T,
+             const int32_t* sched_rows, const int32_t* num_scheduled,
+             const int32_t* completed, int32_t R,
+             const int32_t* token_ids, int64_t token_stride, int32_t L,
+             int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
+             int32_t* positions, int32_t* input_ids,
+             int32_t num_groups, const pkv_group* groups,
+             uint32_t* status, void* stream);
 
 /* Static text for a return code (never NULL). */
 const char* pkv_error_string(int code);

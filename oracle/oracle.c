@@ -97,9 +97,9 @@ static int by_tokens_then_row(const void* pa, const void* pb)
  *     its request in the batch order with seq_len -1 and its tokens at position
  *     -1 / input id -1; a negative count is read as 0; prefix sums saturate at
  *     INT32_MAX; tokens past the last request (sum < T) get position -1 and
- *     input id -1; tokens beyond T (sum > T) are dropped; a position outside
- *     [0, L) gets input id -1.  Positions and seq_lens keep the low 32 bits of
- *     the 64-bit sum.
+ *     input id -1; tokens beyond T (sum > T) are dropped; a negative position,
+ *     or one >= L when input_ids are produced, is flagged and gets input id -1.
+ *     Positions and seq_lens keep the low 32 bits of the 64-bit sum.
  */
 int orc_prepare_batch(int32_t n, int32_t T,
                       const int32_t* sched_rows, const int32_t* num_scheduled,
@@ -184,7 +184,7 @@ int orc_prepare_batch(int32_t n, int32_t T,
                 continue;                                /* flagged above */
             int64_t position = (int64_t)completed[row] + j;   /* R3 */
             positions[flat_token_index] = (int32_t)(uint32_t)(uint64_t)position;
-            if (position < 0 || position >= L) {
+            if (position < 0 || (input_ids != NULL && position >= L)) {
                 st |= ORC_ST_POS_OOR;
                 continue;
             }

@@ -29,6 +29,21 @@ _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 
 
+STEP_MAX_BATCH = 512
+STEP_MAX_GROUPS = 4
+
+
+class Group(ctypes.Structure):
+    """pkv_group: one KV-cache group's inputs and outputs for pkv_step."""
+
+    _fields_ = [
+        ("block_table", _P), ("slot_mapping", _P), ("input_block_tables", _P),
+        ("k", _P), ("v", _P), ("k_cache", _P), ("v_cache", _P),
+        ("k_stride", _I64), ("v_stride", _I64), ("num_slots", _I64), ("row_bytes", _I64),
+        ("MB", _I32), ("block_size", _I32), ("num_blocks", _I32), ("reserved", _I32),
+    ]
+
+
 class PagedKVError(RuntimeError):
     def __init__(self, fn: str, code: int):
         super().__init__(f"{fn}: {error_string(code)} (code {code})")
@@ -51,6 +66,9 @@ def load_library(path: str = library_path) -> ctypes.CDLL:
                                              _I32, _I32, _P, _P, _P, _P]
     lib.pkv_scatter_kv.restype = ctypes.c_int
     lib.pkv_scatter_kv.argtypes = [_I32, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _P, _P]
+    lib.pkv_step.restype = ctypes.c_int
+    lib.pkv_step.argtypes = [_I32, _I32, _P, _P, _P, _I32, _P, _I64, _I32, _P, _P, _P, _P, _P,
+                             _I32, ctypes.POINTER(Group), _P, _P]
     lib.pkv_error_string.restype = ctypes.c_char_p
     lib.pkv_error_string.argtypes = [ctypes.c_int]
     lib.pkv_abi_version.restype = ctypes.c_int
@@ -181,21 +199,80 @@ def scatter_kv(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache:
     """
     T = slot_mapping.shape[0]
     _idx("slot_mapping", slot_mapping, (T,))
-    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
-        if not c.is_cuda or not c.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
-    row_bytes = k_cache[0].numel() * k_cache.element_size() if k_cache.shape[0] else \
-        (k_cache.numel() // max(k_cache.shape[0], 1)) * k_cache.element_size()
-    if v_cache.shape != k_cache.shape or v_cache.element_size() != k_cache.element_size():
-        raise ValueError("k_cache and v_cache must have the same shape and element size")
-    strides = []
-    for name, x in (("k", k), ("v", v)):
-        if not x.is_cuda or x.shape[0] != T:
-            raise ValueError(f"{name} must be a GPU tensor with {T} rows")
-        if T and (x[0].numel() * x.element_size() != row_bytes or not x[0].is_contiguous()):
-            raise ValueError(f"{name} rows must be contiguous and {row_bytes} bytes")
-        strides.append(x.stride(0) * x.element_size() if T else row_bytes)
+    row_bytes, strides = _kv_layout("", k, v, k_cache, v_cache, T)
     rc = _lib.pkv_scatter_kv(T, row_bytes, _ptr(k), strides[0], _ptr(v), strides[1],
                              _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _ptr(slot_mapping),
                              _ptr(status), _stream(stream))
     _check("scatter_kv", rc)
+
+
+def _kv_layout(name_k, k, v, k_cache, v_cache, T):
+    """row_bytes and per-token byte strides of K/V (rows contiguous)."""
+    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not c.is_cuda or not c.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if v_cache.shape != k_cache.shape or v_cache.element_size() != k_cache.element_size():
+        raise ValueError("k_cache and v_cache must have the same shape and element size")
+    row_bytes = (k_cache.numel() // max(k_cache.shape[0], 1)) * k_cache.element_size() \
+        if k_cache.dim() > 1 else k_cache.element_size()
+    strides = []
+    for name, x in (("k", k), ("v", v)):
+        if not x.is_cuda or x.shape[0] != T:
+            raise ValueError(f"{name_k}{name} must be a GPU tensor with {T} rows")
+        if T and (x[0].numel() * x.element_size() != row_bytes or not x[0].is_contiguous()):
+            raise ValueError(f"{name_k}{name} rows must be contiguous and {row_bytes} bytes")
+        strides.append(x.stride(0) * x.element_size() if T else row_bytes)
+    return row_bytes, strides
+
+
+def step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, completed: torch.Tensor,
+         token_ids: Optional[torch.Tensor], num_tokens: int, groups, *,
+         index_mapping: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
+         positions: torch.Tensor, input_ids: Optional[torch.Tensor] = None,
+         status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """A whole step in one call (pkv_step): prepare_batch, then per group
+    compute_slot_mapping and scatter_kv, with identical results.
+
+    groups: sequence of dicts with keys block_table, block_size, num_blocks,
+    slot_mapping, input_block_tables (or None), k, v, k_cache, v_cache.
+    """
+    n = sched_rows.shape[0]
+    T = int(num_tokens)
+    _idx("sched_rows", sched_rows, (n,))
+    _idx("num_scheduled", num_scheduled, (n,))
+    _idx("completed", completed)
+    _idx("index_mapping", index_mapping, (n,))
+    _idx("query_start_loc", query_start_loc, (n + 1,))
+    _idx("seq_lens", seq_lens, (n,))
+    _idx("positions", positions, (T,))
+    _idx("input_ids", input_ids, (T,), optional=True)
+    R = completed.shape[0]
+    L, stride = 0, 0
+    if token_ids is not None:
+        if token_ids.dtype != torch.int32 or not token_ids.is_cuda or token_ids.dim() != 2 \
+                or token_ids.stride(1) != 1 or token_ids.shape[0] != R:
+            raise ValueError("token_ids must be an int32 [R, L] GPU tensor with unit column stride")
+        L, stride = token_ids.shape[1], token_ids.stride(0)
+    elif input_ids is not None:
+        raise ValueError("input_ids needs token_ids")
+    arr = (Group * max(len(groups), 1))()
+    for i, g in enumerate(groups):
+        bt = _idx(f"groups[{i}].block_table", g["block_table"])
+        if bt.dim() != 2 or bt.shape[0] != R:
+            raise ValueError(f"groups[{i}].block_table must be [R, MB]")
+        MB = bt.shape[1]
+        _idx(f"groups[{i}].slot_mapping", g["slot_mapping"], (T,))
+        _idx(f"groups[{i}].input_block_tables", g.get("input_block_tables"), (n, MB),
+             optional=True)
+        row_bytes, (ks, vs) = _kv_layout(f"groups[{i}].", g["k"], g["v"], g["k_cache"],
+                                         g["v_cache"], T)
+        arr[i] = Group(bt.data_ptr(), g["slot_mapping"].data_ptr(),
+                       _ptr(g.get("input_block_tables")), g["k"].data_ptr(), g["v"].data_ptr(),
+                       g["k_cache"].data_ptr(), g["v_cache"].data_ptr(), ks, vs,
+                       g["k_cache"].shape[0], row_bytes, MB, int(g["block_size"]),
+                       int(g["num_blocks"]), 0)
+    rc = _lib.pkv_step(n, T, _ptr(sched_rows), _ptr(num_scheduled), _ptr(completed), R,
+                       _ptr(token_ids), stride, L, _ptr(index_mapping), _ptr(query_start_loc),
+                       _ptr(seq_lens), _ptr(positions), _ptr(input_ids), len(groups), arr,
+                       _ptr(status), _stream(stream))
+    _check("step", rc)

@@ -1,6 +1,6 @@
 // api.hip -- the extern "C" entry points of libpagedkv: argument checks on the
-// host, then one stream-ordered launch per call.  The contract of each entry
-// point (layouts, outputs, error behaviour) is stated in include/pagedkv.h.
+// host, then stream-ordered launches.  The contract of each entry point
+// (layouts, outputs, error behaviour) is stated in include/pagedkv.h.
 #include <stdint.h>
 
 #include "internal.h"
@@ -13,15 +13,11 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline int from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_EHIP; }
 
-}  // namespace
-
-extern "C" {
-
-int pkv_prepare_batch(int32_t n, int32_t T, const int32_t* sched_rows,
-                      const int32_t* num_scheduled, const int32_t* completed, int32_t R,
-                      const int32_t* token_ids, int64_t token_stride, int32_t L,
-                      int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
-                      int32_t* positions, int32_t* input_ids, uint32_t* status, void* stream)
+int check_prepare(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num_scheduled,
+                  const int32_t* completed, int32_t R, const int32_t* token_ids,
+                  int64_t token_stride, int32_t L, const int32_t* index_mapping,
+                  const int32_t* query_start_loc, const int32_t* seq_lens,
+                  const int32_t* positions, const int32_t* input_ids)
 {
     if (n < 0 || T < 0 || R < 0 || L < 0)
         return PKV_EINVAL;
@@ -37,18 +33,14 @@ int pkv_prepare_batch(int32_t n, int32_t T, const int32_t* sched_rows,
         return PKV_EINVAL;
     if (n > PKV_MAX_BATCH)
         return PKV_EUNSUPPORTED;
-    return from_hip(pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
-                                        token_stride, L, index_mapping, query_start_loc, seq_lens,
-                                        positions, input_ids, status,
-                                        static_cast<hipStream_t>(stream)));
+    return PKV_OK;
 }
 
-int pkv_compute_slot_mapping(int32_t n, int32_t T, const int32_t* index_mapping,
-                             const int32_t* query_start_loc, const int32_t* seq_lens,
-                             const int32_t* positions, const int32_t* block_table, int32_t R,
-                             int32_t MB, int32_t block_size, int32_t num_blocks,
-                             int32_t* slot_mapping, int32_t* input_block_tables,
-                             uint32_t* status, void* stream)
+int check_slots(int32_t n, int32_t T, const int32_t* index_mapping,
+                const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
+                const int32_t* block_table, int32_t R, int32_t MB, int32_t block_size,
+                int32_t num_blocks, const int32_t* slot_mapping,
+                const int32_t* input_block_tables)
 {
     if (n < 0 || T < 0 || R < 0 || MB < 0 || num_blocks < 0 || block_size <= 0)
         return PKV_EINVAL;
@@ -64,15 +56,12 @@ int pkv_compute_slot_mapping(int32_t n, int32_t T, const int32_t* index_mapping,
         return PKV_EINVAL;
     if (n > PKV_MAX_BATCH)
         return PKV_EUNSUPPORTED;
-    return from_hip(pkv::launch_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,
-                                      block_table, R, MB, block_size, num_blocks, slot_mapping,
-                                      input_block_tables, status,
-                                      static_cast<hipStream_t>(stream)));
+    return PKV_OK;
 }
 
-int pkv_scatter_kv(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride, const void* v,
-                   int64_t v_stride, void* k_cache, void* v_cache, int64_t num_slots,
-                   const int32_t* slot_mapping, uint32_t* status, void* stream)
+int check_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride, const void* v,
+                  int64_t v_stride, const void* k_cache, const void* v_cache, int64_t num_slots,
+                  const int32_t* slot_mapping)
 {
     if (T < 0 || row_bytes <= 0 || num_slots < 0 || k_stride < row_bytes || v_stride < row_bytes)
         return PKV_EINVAL;
@@ -85,9 +74,111 @@ int pkv_scatter_kv(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride
     // One lane per 16-byte chunk, a quarter of the chunks per lane at most.
     if ((int64_t)T * (row_bytes / 16) / 4 >= kMaxGridThreads)
         return PKV_EUNSUPPORTED;
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_prepare_batch(int32_t n, int32_t T, const int32_t* sched_rows,
+                      const int32_t* num_scheduled, const int32_t* completed, int32_t R,
+                      const int32_t* token_ids, int64_t token_stride, int32_t L,
+                      int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
+                      int32_t* positions, int32_t* input_ids, uint32_t* status, void* stream)
+{
+    const int rc = check_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
+                                 token_stride, L, index_mapping, query_start_loc, seq_lens,
+                                 positions, input_ids);
+    if (rc != PKV_OK)
+        return rc;
+    return from_hip(pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
+                                        token_stride, L, index_mapping, query_start_loc, seq_lens,
+                                        positions, input_ids, status,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int pkv_compute_slot_mapping(int32_t n, int32_t T, const int32_t* index_mapping,
+                             const int32_t* query_start_loc, const int32_t* seq_lens,
+                             const int32_t* positions, const int32_t* block_table, int32_t R,
+                             int32_t MB, int32_t block_size, int32_t num_blocks,
+                             int32_t* slot_mapping, int32_t* input_block_tables,
+                             uint32_t* status, void* stream)
+{
+    const int rc = check_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,
+                               block_table, R, MB, block_size, num_blocks, slot_mapping,
+                               input_block_tables);
+    if (rc != PKV_OK)
+        return rc;
+    return from_hip(pkv::launch_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,
+                                      block_table, R, MB, block_size, num_blocks, slot_mapping,
+                                      input_block_tables, status,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int pkv_scatter_kv(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride, const void* v,
+                   int64_t v_stride, void* k_cache, void* v_cache, int64_t num_slots,
+                   const int32_t* slot_mapping, uint32_t* status, void* stream)
+{
+    const int rc = check_scatter(T, row_bytes, k, k_stride, v, v_stride, k_cache, v_cache,
+                                 num_slots, slot_mapping);
+    if (rc != PKV_OK)
+        return rc;
     return from_hip(pkv::launch_scatter(T, row_bytes, k, k_stride, v, v_stride, k_cache, v_cache,
                                         num_slots, slot_mapping, status,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num_scheduled,
+             const int32_t* completed, int32_t R, const int32_t* token_ids, int64_t token_stride,
+             int32_t L, int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
+             int32_t* positions, int32_t* input_ids, int32_t num_groups, const pkv_group* groups,
+             uint32_t* status, void* stream)
+{
+    if (num_groups < 0 || (num_groups > 0 && groups == nullptr))
+        return PKV_EINVAL;
+    int rc = check_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids, token_stride,
+                           L, index_mapping, query_start_loc, seq_lens, positions, input_ids);
+    if (rc != PKV_OK)
+        return rc;
+    for (int i = 0; i < num_groups; ++i) {
+        const pkv_group& g = groups[i];
+        if (g.reserved != 0)
+            return PKV_EINVAL;
+        rc = check_slots(n, T, index_mapping, query_start_loc, seq_lens, positions, g.block_table,
+                         R, g.MB, g.block_size, g.num_blocks, g.slot_mapping,
+                         g.input_block_tables);
+        if (rc != PKV_OK)
+            return rc;
+        rc = check_scatter(T, g.row_bytes, g.k, g.k_stride, g.v, g.v_stride, g.k_cache,
+                           g.v_cache, g.num_slots, g.slot_mapping);
+        if (rc != PKV_OK)
+            return rc;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool fused = n <= PKV_STEP_MAX_BATCH && num_groups >= 1 &&
+                       num_groups <= PKV_STEP_MAX_GROUPS &&
+                       pkv::step_grid_blocks(n, T, num_groups, groups) * 512 < kMaxGridThreads;
+    if (fused)
+        return from_hip(pkv::launch_step(n, T, sched_rows, num_scheduled, completed, R, token_ids,
+                                         token_stride, L, index_mapping, query_start_loc,
+                                         seq_lens, positions, input_ids, num_groups, groups,
+                                         status, s));
+    hipError_t e = pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
+                                       token_stride, L, index_mapping, query_start_loc, seq_lens,
+                                       positions, input_ids, status, s);
+    for (int i = 0; e == hipSuccess && i < num_groups; ++i) {
+        const pkv_group& g = groups[i];
+        e = pkv::launch_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,
+                              g.block_table, R, g.MB, g.block_size, g.num_blocks, g.slot_mapping,
+                              g.input_block_tables, status, s);
+    }
+    for (int i = 0; e == hipSuccess && i < num_groups; ++i) {
+        const pkv_group& g = groups[i];
+        e = pkv::launch_scatter(T, g.row_bytes, g.k, g.k_stride, g.v, g.v_stride, g.k_cache,
+                                g.v_cache, g.num_slots, g.slot_mapping, status, s);
+    }
+    return from_hip(e);
 }
 
 const char* pkv_error_string(int code)

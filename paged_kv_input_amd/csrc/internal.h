@@ -60,6 +60,273 @@ __device__ inline int owner_of(const int32_t* qsl, int n, int64_t t)
     return lo;
 }
 
+// Ascending order of (count, row) as unsigned 64-bit keys: the count (>= 0) in
+// the high word, the row with its sign bit flipped in the low word so that
+// signed row order equals unsigned key order.
+__device__ inline uint64_t sort_key(int32_t count, int32_t row)
+{
+    return ((uint64_t)(uint32_t)count << 32) | (uint32_t)(row ^ INT32_MIN);
+}
+__device__ inline int32_t key_count(uint64_t key) { return (int32_t)(key >> 32); }
+__device__ inline int32_t key_row(uint64_t key) { return (int32_t)((uint32_t)key ^ 0x80000000u); }
+
+// LDS working set of order_batch for up to kMaxN requests.  The keys are dead
+// once ordered, so the per-request rows and completed counts reuse them.
+template <int kMaxN, int kWaves, bool kCounts = false>
+struct BatchLds {
+    uint64_t key[kMaxN];
+    int32_t qsl[kMaxN + 1];
+    int32_t count[kCounts ? kMaxN : 1];     // clamped counts in batch order (kCounts only)
+    int64_t wave_total[kWaves];
+    __device__ int32_t* row() { return reinterpret_cast<int32_t*>(key); }
+    __device__ int32_t* done() { return reinterpret_cast<int32_t*>(key) + kMaxN; }
+};
+
+// Batch assembly inside one workgroup ("Batch Construction and Sequence
+// Flattening" of the kongchang.com article): gather the n scheduled requests
+// as (count, row) keys, bitonic-sort them ascending in LDS, prefix-sum the
+// sorted counts (wave-level scan plus one cross-wave pass, saturating at
+// INT32_MAX) and fetch each request's completed count.  On return, after a
+// barrier, lds.qsl[0..n], lds.row()[0..n) and lds.done()[0..n) describe the
+// batch in order (and lds.count[0..n) when kCounts).  A writer workgroup also
+// stores index_mapping,
+// query_start_loc and seq_lens and collects BAD_ROW / TOKEN_SUM; every caller
+// gets BAD_COUNT for negative counts (read as 0).  n <= kMaxN.
+template <int kThreads, int kMaxN, bool kCounts>
+__device__ inline void order_batch(BatchLds<kMaxN, kThreads / kWave, kCounts>& lds, int32_t n,
+                                   int32_t T,
+                                   const int32_t* __restrict__ sched_rows,
+                                   const int32_t* __restrict__ num_scheduled,
+                                   const int32_t* __restrict__ completed, int32_t R, bool writer,
+                                   int32_t* __restrict__ index_mapping,
+                                   int32_t* __restrict__ query_start_loc,
+                                   int32_t* __restrict__ seq_lens, uint32_t& flags)
+{
+    constexpr int kWaves = kThreads / kWave;
+    constexpr int kPer = kMaxN / kThreads;       // batch rows per thread in the scan
+    static_assert(kMaxN % kThreads == 0, "batch rows split evenly over threads");
+    const int tid = threadIdx.x;
+
+    int n_pad = 1;
+    while (n_pad < n)
+        n_pad <<= 1;
+    for (int i = tid; i < n_pad; i += kThreads) {
+        uint64_t key = ~0ull;                       // padding sorts last
+        if (i < n) {
+            int32_t c = num_scheduled[i];
+            if (c < 0) {
+                flags |= PKV_ST_BAD_COUNT;
+                c = 0;
+            }
+            key = sort_key(c, sched_rows[i]);
+        }
+        lds.key[i] = key;
+    }
+    __syncthreads();
+
+    // Bitonic sort, ascending.  Pair i of a stage with distance j compares
+    // element lo (bit log2(j) cleared) with lo + j; the sub-sequence direction
+    // comes from bit log2(k) of lo.
+    for (int k = 2; k <= n_pad; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < (n_pad >> 1); i += kThreads) {
+                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+                const int hi = lo + j;
+                const bool ascending = (lo & k) == 0;
+                const uint64_t a = lds.key[lo];
+                const uint64_t b = lds.key[hi];
+                if ((a > b) == ascending) {
+                    lds.key[lo] = b;
+                    lds.key[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // Each thread owns kPer consecutive batch rows.
+    uint64_t keys[kPer];
+    int64_t local = 0;
+    const int first = tid * kPer;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int b = first + e;
+        keys[e] = b < n ? lds.key[b] : 0ull;
+        local += b < n ? key_count(keys[e]) : 0;
+    }
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int64_t incl = wave_inclusive_scan(local);
+    if (lane == kWave - 1)
+        lds.wave_total[wave] = incl;
+    __syncthreads();      // also: every key is in registers, lds.key may be reused
+    if (wave == 0) {
+        int64_t w = lane < kWaves ? lds.wave_total[lane] : 0;
+        w = wave_inclusive_scan(w);
+        if (lane < kWaves)
+            lds.wave_total[lane] = w;
+    }
+    __syncthreads();
+    int64_t run = (wave > 0 ? lds.wave_total[wave - 1] : 0) + incl - local;
+    const int64_t total = lds.wave_total[kWaves - 1];
+
+    int32_t* s_row = lds.row();
+    int32_t* s_done = lds.done();
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int b = first + e;
+        if (b >= n)
+            break;
+        const int32_t c = key_count(keys[e]);
+        const int32_t row = key_row(keys[e]);
+        run += c;
+        const int32_t end = run > INT32_MAX ? INT32_MAX : (int32_t)run;
+        lds.qsl[b + 1] = end;
+        const bool row_ok = row >= 0 && row < R;
+        const int32_t done = row_ok ? completed[row] : 0;
+        s_row[b] = row;
+        s_done[b] = done;
+        if (kCounts)
+            lds.count[b] = c;
+        if (writer) {
+            index_mapping[b] = row;
+            query_start_loc[b + 1] = end;
+            if (row_ok) {
+                seq_lens[b] = (int32_t)(uint32_t)(uint64_t)((int64_t)done + c);
+            } else {
+                seq_lens[b] = -1;
+                flags |= PKV_ST_BAD_ROW;
+            }
+        }
+    }
+    if (tid == 0) {
+        lds.qsl[0] = 0;
+        if (writer) {
+            query_start_loc[0] = 0;
+            if (total != (int64_t)T)
+                flags |= PKV_ST_TOKEN_SUM;
+        }
+    }
+    __syncthreads();
+}
+
+// Orders LDS accesses between the lanes of one wavefront (no s_barrier: the
+// other wavefronts of the workgroup are not involved).
+__device__ inline void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// order_batch done by ONE wavefront of the workgroup, synchronizing only
+// itself, so that the workgroup's other wavefronts can keep their own memory
+// traffic in flight meanwhile.  Same results and flags as order_batch; the
+// caller must __syncthreads() before other wavefronts read the LDS outputs.
+template <int kMaxN>
+__device__ inline void order_batch_wave(BatchLds<kMaxN, 1, true>& lds, int32_t n, int32_t T,
+                                        const int32_t* __restrict__ sched_rows,
+                                        const int32_t* __restrict__ num_scheduled,
+                                        const int32_t* __restrict__ completed, int32_t R,
+                                        bool writer, int32_t* __restrict__ index_mapping,
+                                        int32_t* __restrict__ query_start_loc,
+                                        int32_t* __restrict__ seq_lens, uint32_t& flags)
+{
+    constexpr int kPer = kMaxN / kWave;
+    static_assert(kMaxN % kWave == 0, "batch rows split evenly over lanes");
+    const int lane = threadIdx.x & (kWave - 1);
+
+    int n_pad = 1;
+    while (n_pad < n)
+        n_pad <<= 1;
+    for (int i = lane; i < n_pad; i += kWave) {
+        uint64_t key = ~0ull;                       // padding sorts last
+        if (i < n) {
+            int32_t c = num_scheduled[i];
+            if (c < 0) {
+                flags |= PKV_ST_BAD_COUNT;
+                c = 0;
+            }
+            key = sort_key(c, sched_rows[i]);
+        }
+        lds.key[i] = key;
+    }
+    wave_sync();
+    for (int k = 2; k <= n_pad; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = lane; i < (n_pad >> 1); i += kWave) {
+                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+                const int hi = lo + j;
+                const bool ascending = (lo & k) == 0;
+                const uint64_t a = lds.key[lo];
+                const uint64_t b = lds.key[hi];
+                if ((a > b) == ascending) {
+                    lds.key[lo] = b;
+                    lds.key[hi] = a;
+                }
+            }
+            wave_sync();
+        }
+    }
+    uint64_t keys[kPer];
+    int64_t local = 0;
+    const int first = lane * kPer;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int b = first + e;
+        keys[e] = b < n ? lds.key[b] : 0ull;
+        local += b < n ? key_count(keys[e]) : 0;
+    }
+    const int64_t incl = wave_inclusive_scan(local);
+    const uint32_t total_lo = __shfl((uint32_t)(uint64_t)incl, kWave - 1, kWave);
+    const uint32_t total_hi = __shfl((uint32_t)((uint64_t)incl >> 32), kWave - 1, kWave);
+    const int64_t total = (int64_t)(((uint64_t)total_hi << 32) | total_lo);
+    int64_t run = incl - local;
+    wave_sync();          // every key is in registers: lds.key may be reused
+    int32_t* s_row = lds.row();
+    int32_t* s_done = lds.done();
+    int32_t done_v[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int b = first + e;
+        const int32_t row = key_row(keys[e]);
+        done_v[e] = (b < n && row >= 0 && row < R) ? completed[row] : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int b = first + e;
+        if (b >= n)
+            break;
+        const int32_t c = key_count(keys[e]);
+        const int32_t row = key_row(keys[e]);
+        run += c;
+        const int32_t end = run > INT32_MAX ? INT32_MAX : (int32_t)run;
+        const bool row_ok = row >= 0 && row < R;
+        lds.qsl[b + 1] = end;
+        s_row[b] = row;
+        s_done[b] = done_v[e];
+        lds.count[b] = c;
+        if (writer) {
+            index_mapping[b] = row;
+            query_start_loc[b + 1] = end;
+            if (row_ok) {
+                seq_lens[b] = (int32_t)(uint32_t)(uint64_t)((int64_t)done_v[e] + c);
+            } else {
+                seq_lens[b] = -1;
+                flags |= PKV_ST_BAD_ROW;
+            }
+        }
+    }
+    if (lane == 0) {
+        lds.qsl[0] = 0;
+        if (writer) {
+            query_start_loc[0] = 0;
+            if (total != (int64_t)T)
+                flags |= PKV_ST_TOKEN_SUM;
+        }
+    }
+}
+
 // Launchers (host side).  Arguments are already validated; each returns a
 // hipError_t from the launch.
 hipError_t launch_prepare(int32_t n, int32_t T, const int32_t* sched_rows,
@@ -75,6 +342,16 @@ hipError_t launch_slots(int32_t n, int32_t T, const int32_t* index_mapping,
                         int32_t MB, int32_t block_size, int32_t num_blocks,
                         int32_t* slot_mapping, int32_t* input_block_tables, uint32_t* status,
                         hipStream_t stream);
+
+hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
+                       const int32_t* num_scheduled, const int32_t* completed, int32_t R,
+                       const int32_t* token_ids, int64_t token_stride, int32_t L,
+                       int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
+                       int32_t* positions, int32_t* input_ids, int32_t num_groups,
+                       const pkv_group* groups, uint32_t* status, hipStream_t stream);
+
+// Workgroups launch_step would use (0 when it would launch its lone workgroup).
+int64_t step_grid_blocks(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
 
 hipError_t launch_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride,
                           const void* v, int64_t v_stride, void* k_cache, void* v_cache,

@@ -20,9 +20,40 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kScatterThreads = 256;
-constexpr int kScatterUnroll = 4;
+#ifndef PKV_SCATTER_THREADS
+#define PKV_SCATTER_THREADS 256
+#endif
+#ifndef PKV_SCATTER_UNROLL
+#define PKV_SCATTER_UNROLL 4
+#endif
+#ifndef PKV_SCATTER_NT_LOAD
+#define PKV_SCATTER_NT_LOAD 1
+#endif
+#ifndef PKV_SCATTER_NT_STORE
+#define PKV_SCATTER_NT_STORE 1
+#endif
+
+constexpr int kScatterThreads = PKV_SCATTER_THREADS;
+constexpr int kScatterUnroll = PKV_SCATTER_UNROLL;
 constexpr int kChunksPerBlock = kScatterThreads * kScatterUnroll;
+
+__device__ inline u32x4 load16(const u32x4* p)
+{
+#if PKV_SCATTER_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ inline void store16(u32x4 x, u32x4* p)
+{
+#if PKV_SCATTER_NT_STORE
+    __builtin_nontemporal_store(x, p);
+#else
+    *p = x;
+#endif
+}
 
 template <bool kPow2Row, bool kFull>
 __device__ inline void scatter_chunks(int64_t base, int64_t total_chunks, int32_t chunks_per_row,
@@ -47,8 +78,8 @@ __device__ inline void scatter_chunks(int64_t base, int64_t total_chunks, int32_
         const int64_t t = kPow2Row ? (idx >> row_shift) : idx / chunks_per_row;
         chunk[u] = idx - t * chunks_per_row;
         slot[u] = live ? slot_mapping[t] : -1;
-        kv[u] = __builtin_nontemporal_load(k + t * k_stride16 + chunk[u]);
-        vv[u] = __builtin_nontemporal_load(v + t * v_stride16 + chunk[u]);
+        kv[u] = load16(k + t * k_stride16 + chunk[u]);
+        vv[u] = load16(v + t * v_stride16 + chunk[u]);
     }
     // Pin the payload in registers here.  Without this the compiler sinks the
     // loads into the store branches below, after the slot test, and the lane
@@ -65,8 +96,8 @@ __device__ inline void scatter_chunks(int64_t base, int64_t total_chunks, int32_
             continue;
         }
         const int64_t dst = (int64_t)slot[u] * chunks_per_row + chunk[u];
-        __builtin_nontemporal_store(kv[u], k_cache + dst);
-        __builtin_nontemporal_store(vv[u], v_cache + dst);
+        store16(kv[u], k_cache + dst);
+        store16(vv[u], v_cache + dst);
     }
 }
 

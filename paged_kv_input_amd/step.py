@@ -32,7 +32,7 @@ class DeviceStep:
     def __init__(self, sched_rows, num_scheduled, completed, token_ids,
                  groups: Sequence[GroupSpec], *, device="cuda", cache_fill: Optional[int] = None,
                  ibt_fill: Optional[int] = None, with_input_ids: bool = True,
-                 with_block_tables: bool = True):
+                 with_block_tables: bool = True, num_tokens: Optional[int] = None):
         dev = torch.device(device)
 
         def up(a, dtype=None):
@@ -47,7 +47,8 @@ class DeviceStep:
         self.completed = up(np.asarray(completed, np.int32))
         self.token_ids = up(np.asarray(token_ids, np.int32)) if with_input_ids else None
         self.n = int(self.sched_rows.shape[0])
-        self.T = int(np.maximum(np.asarray(num_scheduled, np.int64), 0).sum())
+        self.T = int(np.maximum(np.asarray(num_scheduled, np.int64), 0).sum()) \
+            if num_tokens is None else int(num_tokens)
         i32 = dict(dtype=torch.int32, device=dev)
         self.index_mapping = torch.empty(self.n, **i32)
         self.query_start_loc = torch.empty(self.n + 1, **i32)
@@ -105,6 +106,17 @@ class DeviceStep:
             self.slots(gi, stream)
         for gi in range(len(self.groups)):
             self.scatter(gi, stream)
+
+    def run_fused(self, stream=None):
+        """The same step through the single pkv_step entry point."""
+        api.step(self.sched_rows, self.num_scheduled, self.completed, self.token_ids, self.T,
+                 [dict(block_table=g["block_table"], block_size=g["block_size"],
+                       num_blocks=g["num_blocks"], slot_mapping=g["slot_mapping"],
+                       input_block_tables=g["input_block_tables"], k=g["k"], v=g["v"],
+                       k_cache=g["k_cache"], v_cache=g["v_cache"]) for g in self.groups],
+                 index_mapping=self.index_mapping, query_start_loc=self.query_start_loc,
+                 seq_lens=self.seq_lens, positions=self.positions, input_ids=self.input_ids,
+                 status=self.status, stream=stream)
 
     def status_bits(self) -> int:
         return int(self.status.item()) & 0xFFFFFFFF

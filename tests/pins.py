@@ -275,6 +275,11 @@ def pin_error_semantics(lib):
     _eq(kc[0], k[3], "k slot 0")
     _eq(vc[0], v[3], "v slot 0")
     assert not kc[1:4].any() and not vc[1:4].any()
+    # without a token table the width L bounds nothing: only negative positions flag
+    p3 = oracle.prepare_batch(np.array([3], np.int32), np.array([3], np.int32), completed, tok,
+                              T=3, lib=lib, with_input_ids=False)
+    assert p3["status"] == 0, p3["status"]
+    _eq(p3["positions"], [9, 10, 11], "positions without input_ids")
     # argument errors
     assert oracle.prepare_batch(rows, counts, completed, tok, T=-1, lib=lib)["rc"] == oracle.EINVAL
     assert oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],

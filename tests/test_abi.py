@@ -34,7 +34,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["pkv_abi_version", "pkv_compute_slot_mapping", "pkv_error_string",
-                     "pkv_prepare_batch", "pkv_scatter_kv"]
+                     "pkv_prepare_batch", "pkv_scatter_kv", "pkv_step"]
     for name in names:
         assert hasattr(lib, name), name
     so = os.path.join(ROOT, "paged_kv_input_amd", "libpagedkv.so")
@@ -51,6 +51,9 @@ def test_constants_match_binding(lib):
     m = declared_macros()
     assert lib.pkv_abi_version() == m["PKV_ABI_VERSION"]
     assert api.MAX_BATCH == m["PKV_MAX_BATCH"]
+    assert api.STEP_MAX_BATCH == m["PKV_STEP_MAX_BATCH"]
+    assert api.STEP_MAX_GROUPS == m["PKV_STEP_MAX_GROUPS"]
+    assert ctypes.sizeof(api.Group) == 104
     for name, bit in api.ST_BITS.items():
         assert m["PKV_ST_" + name] == bit
         assert getattr(oracle, "ST_" + name) == bit
@@ -89,6 +92,31 @@ def test_host_argument_errors(lib):
     assert sc(1, 16, P(0x1008), 16, fake, 16, fake, fake, 4, fake, N, N) == EALIGN
     assert sc(1, 16, fake, 24, fake, 16, fake, fake, 4, fake, N, N) == EALIGN
     assert sc(1, 16, fake, 16, fake, 16, fake, P(0x1004), 4, fake, N, N) == EALIGN
+
+
+def test_step_host_argument_errors(lib):
+    from paged_kv_input_amd import api
+
+    P = ctypes.c_void_p
+    fake = 0x1000
+    g = api.Group(fake, fake, None, fake, fake, fake, fake, 16, 16, 4, 16, 2, 16, 4, 0)
+    arr = (api.Group * 1)(g)
+    st = lib.pkv_step
+    args = [1, 1, fake, fake, fake, 1, fake, 1, 1, fake, fake, fake, fake, fake]
+    assert st(*args, -1, arr, None, None) == -1          # num_groups < 0
+    assert st(*args, 1, None, None, None) == -1          # groups NULL
+    arr[0].reserved = 1
+    assert st(*args, 1, arr, None, None) == -1           # reserved must be 0
+    arr[0].reserved = 0
+    arr[0].block_size = 0
+    assert st(*args, 1, arr, None, None) == -1           # group's block size
+    arr[0].block_size = 16
+    arr[0].row_bytes = 24
+    arr[0].k_stride = arr[0].v_stride = 32
+    assert st(*args, 1, arr, None, None) == -2           # row not a multiple of 16 bytes
+    args[0] = 4097
+    arr[0].row_bytes = 16
+    assert st(*args, 1, arr, None, None) == -3           # beyond PKV_MAX_BATCH
 
 
 def test_binding_rejects_cpu_tensors():

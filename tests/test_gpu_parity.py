@@ -25,13 +25,19 @@ def gpu():
     torch.cuda.synchronize()
 
 
-def run_and_compare(batch, full_cache=True):
+MODES = ["calls", "fused"]
+
+
+def run_and_compare(batch, full_cache=True, mode="calls"):
     import torch
 
-    say(f"[case] {batch.name} seed={batch.seed} n={batch.n} T={batch.T} "
+    say(f"[case] {batch.name} seed={batch.seed} n={batch.n} T={batch.T} mode={mode} "
         f"groups={[(g.block_size, g.num_blocks) for g in batch.groups]}")
     step = device_step(batch)
-    step.run()
+    if mode == "fused":
+        step.run_fused()
+    else:
+        step.run()
     torch.cuda.synchronize()
     prep, groups_o = oracle_chain(batch, lazy_caches=not full_cache)
     compare_indices(step, prep, groups_o)
@@ -46,9 +52,10 @@ def run_and_compare(batch, full_cache=True):
     return step, prep, groups_o
 
 
-def test_pages_example():
+@pytest.mark.parametrize("mode", MODES)
+def test_pages_example(mode):
     b = workloads.pages_example()
-    step, prep, go = run_and_compare(b)
+    step, prep, go = run_and_compare(b, mode=mode)
     # the values the article prints, read straight off the GPU
     assert step.host("query_start_loc").tolist() == [0, 1, 9]
     assert step.host("positions").tolist() == [31] + list(range(16, 24))
@@ -58,35 +65,40 @@ def test_pages_example():
 
 @pytest.mark.parametrize("maker", [workloads.prefix_reuse_example, workloads.budget_tie_example],
                          ids=["prefix_reuse", "budget_tie"])
-def test_page_examples_other(maker):
-    run_and_compare(maker())
+@pytest.mark.parametrize("mode", MODES)
+def test_page_examples_other(maker, mode):
+    run_and_compare(maker(), mode=mode)
 
 
 @pytest.mark.parametrize("name", ["seeded_16req", "seeded_16req_decode50"])
-def test_seeded_small(name):
-    run_and_compare(workloads.make(name))
+@pytest.mark.parametrize("mode", MODES)
+def test_seeded_small(name, mode):
+    run_and_compare(workloads.make(name), mode=mode)
 
 
 @pytest.mark.parametrize("name", ["decode_256x1", "mixed_8192", "prefill_16x2048",
                                   "two_groups_512req"])
-def test_reduced(name):
-    run_and_compare(workloads.make(name, reduced=True), full_cache=False)
+@pytest.mark.parametrize("mode", MODES)
+def test_reduced(name, mode):
+    run_and_compare(workloads.make(name, reduced=True), full_cache=False, mode=mode)
 
 
 @pytest.mark.parametrize("seed", range(32))
-def test_tiny_random(seed):
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_random(seed, mode):
     b = workloads.random_tiny(1000 + seed, zero_counts=(seed % 4 == 3))
-    run_and_compare(b)
+    run_and_compare(b, mode=mode)
 
 
 @pytest.mark.parametrize("name", ["decode_256x1", "mixed_8192", "prefill_16x2048",
                                   "two_groups_512req"])
-def test_full_size(name):
+@pytest.mark.parametrize("mode", MODES)
+def test_full_size(name, mode):
     """Full configuration sizes, the launch configuration the benchmark times."""
     import torch
 
     b = workloads.make(name)
-    run_and_compare(b, full_cache=False)
+    run_and_compare(b, full_cache=False, mode=mode)
     torch.cuda.empty_cache()
 
 
@@ -103,8 +115,10 @@ def test_shuffled_schedule_same_outputs():
     assert_equal("slot_mapping", s2.host("slot_mapping", 0), s1.host("slot_mapping", 0))
 
 
-def test_max_batch():
-    """n = PKV_MAX_BATCH requests (the LDS sort's limit), counts 0..3, ties galore."""
+@pytest.mark.parametrize("mode", MODES)
+def test_max_batch(mode):
+    """n = PKV_MAX_BATCH requests (the LDS sort's limit), counts 0..3, ties galore;
+    in fused mode this exceeds the one-launch limit and takes the separate kernels."""
     import paged_kv_input_amd as pkv
 
     rng = np.random.default_rng(21)
@@ -124,7 +138,7 @@ def test_max_batch():
     b = workloads.Batch("max_batch", 21, rows, counts, completed,
                         rng.integers(0, 1000, (R, L), dtype=np.int32),
                         [workloads.KVGroup(bs, NB, MB, bt, 1, 8, "fp16", k, v)])
-    run_and_compare(b)
+    run_and_compare(b, mode=mode)
 
 
 def test_empty_and_degenerate():
@@ -177,3 +191,93 @@ def test_strided_kv_and_payload_widths():
         assert rc == 0 and ost == 0 and int(st.item()) == 0
         assert_equal("k_cache", kc.cpu().numpy(), ko)
         assert_equal("v_cache", vc.cpu().numpy(), vo)
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 511, 512, 513])
+def test_fused_batch_sizes(n):
+    """Batch sizes around the one-wave sort's lane multiples and the fused limit."""
+    rng = np.random.default_rng(100 + n)
+    R, L, bs = n + 37, 96, 16
+    rows = rng.choice(R, n, replace=False).astype(np.int32)
+    counts = rng.integers(0, 40, n).astype(np.int32)
+    counts[rng.random(n) < 0.4] = 1
+    completed = np.zeros(R, np.int32)
+    completed[rows] = rng.integers(0, 50, n)
+    MB = L // bs
+    need = int(sum(max(0, -(-(int(completed[r]) + int(c)) // bs) - int(completed[r]) // bs)
+                   for r, c in zip(rows, counts)))
+    NB = need + 11
+    bt = workloads._block_table(rng, R, MB, NB, bs, rows, counts, completed)
+    T = int(counts.sum())
+    k = rng.integers(0, 65535, (T, 2, 64), dtype=np.uint16)
+    v = rng.integers(0, 65535, (T, 2, 64), dtype=np.uint16)
+    b = workloads.Batch(f"fused_n{n}", 100 + n, rows, counts, completed,
+                        rng.integers(0, 1000, (R, L), dtype=np.int32),
+                        [workloads.KVGroup(bs, NB, MB, bt, 2, 64, "fp16", k, v)])
+    run_and_compare(b, mode="fused")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_error_inputs_match_oracle(mode):
+    """Bad rows, negative counts, a token-sum mismatch, positions past the table,
+    missing blocks and a short cache: same outputs and status bits as the oracle,
+    and nothing written out of bounds (every access is bounds-checked)."""
+    R, L, MB, bs, NB = 6, 10, 3, 4, 8
+    completed = np.array([0, 2, 3, 9, -1, 5], np.int32)
+    tok = (np.arange(R)[:, None] * 100 + np.arange(L)[None, :]).astype(np.int32)
+    rows = np.array([1, 9, 2, 3, 4], np.int32)
+    counts = np.array([2, 1, -2, 3, 1], np.int32)
+    bt = np.array([[0, 1, 2], [3, -1, 9], [4, 5, 6], [7, -1, -1], [2, 2, 2], [1, 1, 1]], np.int32)
+    T = 9
+    rng = np.random.default_rng(4)
+    k = rng.integers(0, 65000, (T, 1, 8), dtype=np.uint16)
+    v = rng.integers(0, 65000, (T, 1, 8), dtype=np.uint16)
+    import torch
+    from paged_kv_input_amd.step import DeviceStep, GroupSpec
+
+    # T is the host's count, deliberately larger than the counts' sum (7)
+    step = DeviceStep(rows, counts, completed, tok, [GroupSpec(bt, bs, NB, k, v)],
+                      cache_fill=SENTINEL16, ibt_fill=oracle.IBT_UNWRITTEN, num_tokens=T)
+    if mode == "fused":
+        step.run_fused()
+    else:
+        step.run()
+    torch.cuda.synchronize()
+    prep = oracle.prepare_batch(rows, counts, completed, tok, T=T)
+    go = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                     prep["seq_lens"], prep["positions"], bt, bs, NB)
+    kc = np.full((NB * bs, 1, 8), 0xFFFF, np.uint16)
+    vc = kc.copy()
+    rc, sst = oracle.scatter_kv(k, v, kc, vc, go["slot_mapping"])
+    for key in ("index_mapping", "query_start_loc", "seq_lens", "positions", "input_ids"):
+        assert_equal(key, step.host(key), prep[key])
+    assert_equal("slot_mapping", step.host("slot_mapping", 0), go["slot_mapping"])
+    assert_equal("input_block_tables", step.host("input_block_tables", 0),
+                 go["input_block_tables"])
+    assert_equal("k_cache", step.host("k_cache", 0).view(np.uint16), kc)
+    assert_equal("v_cache", step.host("v_cache", 0).view(np.uint16), vc)
+    assert step.status_bits() == prep["status"] | go["status"] | sst, \
+        (step.status_bits(), prep["status"], go["status"], sst)
+
+
+def test_scatter_skips_negative_and_flags_out_of_range_slots():
+    import torch
+    import paged_kv_input_amd as pkv
+
+    rng = np.random.default_rng(8)
+    T, H, D, num_slots = 40, 2, 16, 64
+    k = torch.from_numpy(rng.integers(-30000, 30000, (T, H, D), dtype=np.int16)).cuda()
+    v = torch.from_numpy(rng.integers(-30000, 30000, (T, H, D), dtype=np.int16)).cuda()
+    slots = rng.choice(num_slots, T, replace=False).astype(np.int32)
+    slots[3], slots[11], slots[20] = -1, num_slots, num_slots + 1000
+    kc = torch.zeros((num_slots, H, D), dtype=torch.int16, device="cuda")
+    vc = torch.zeros_like(kc)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.scatter_kv(k, v, kc, vc, torch.from_numpy(slots).cuda(), status=st)
+    torch.cuda.synchronize()
+    ko = np.zeros((num_slots, H, D), np.int16)
+    vo = np.zeros_like(ko)
+    rc, ost = oracle.scatter_kv(k.cpu().numpy(), v.cpu().numpy(), ko, vo, slots)
+    assert rc == 0 and ost == oracle.ST_SLOT_OOR == int(st.item())
+    assert_equal("k_cache", kc.cpu().numpy(), ko)
+    assert_equal("v_cache", vc.cpu().numpy(), vo)
