@@ -1,19 +1,23 @@
-"""Benchmark of one step of the paged-KV input path on one MI355X.
+"""Benchmark of the paged-KV input path on one MI355X.
 
 A step is the whole path on one synthetic batch: prepare_batch, then for every
-KV-cache group compute_slot_mapping and scatter_kv (one layer), on one stream
-with every input already resident in HBM.  Default workload: 16 requests x
-2048 new tokens (32768 tokens) from an empty history, block size 32, a
-131072-block pool, K/V of 8 heads x 128 in bf16.
+KV-cache group compute_slot_mapping and scatter_kv (one layer), with every
+input already resident in HBM.  Default workload: 16 requests x 2048 new
+tokens (32768 tokens) from an empty history, block size 32, a 131072-block
+pool, K/V of 8 heads x 128 in bf16.
 
-Timing: W untimed warm-up steps, then exactly K timed steps.  Before each
-timed step a 1 GiB buffer is rewritten (outside the timed interval) so the
-step starts with L2 and the 256 MB Infinity Cache holding none of its data;
-HIP events recorded on the launch stream around each call give the per-call
-and per-step device times.  The whole K-step loop is bracketed by
-torch.cuda.synchronize() on both sides.
+Timing: the step inputs come in ROTATE independent seeded batches of the same
+shape (own K/V payload, rows and random block tables; one shared pair of
+caches), so consecutive steps never find each other's data in L2 or the
+256 MB Infinity Cache (a cycle touches over 1 GB).  W untimed warm-up steps,
+then exactly K timed steps back to back, bracketed by torch.cuda.synchronize()
+on both sides and by HIP events on the launch stream; ms_per_step is the
+event interval / K.  The step runs through pkv_step (one launch) and, timed
+the same way, through the three separate calls.  Secondary figures: the
+per-call split of the three calls and a single-step cold measurement (a 1 GiB
+rewrite before each step, events around it).
 
-Prints one JSON line (rank 0, N = 1 only: this build runs on one GPU).
+Prints one JSON line (N = 1 only: this build runs on one GPU).
 """
 from __future__ import annotations
 
@@ -32,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "scheduled tokens/sec (prep+slot_mapping+KV scatter); HBM GB/s % of peak"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
 FLUSH_BYTES = 1 << 30
+ROTATE = 4
 
 
 def algorithmic_bytes(batch):
@@ -70,12 +75,21 @@ def scatter_bytes_per_launch(batch, gi):
     return batch.T * (4 * g.row_bytes + 4)
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel, workload, kernel_src):
+def kernel_sources(kernel):
+    csrc = os.path.join(ROOT, "paged_kv_input_amd", "csrc")
+    files = {"step": ["step.hip", "internal.h"], "scatter_kv": ["scatter.hip", "internal.h"]}
+    return [os.path.join(csrc, f) for f in files[kernel]]
+
+
+def traffic_from_profile(kernel, workload):
     """HBM bytes per launch of the kernel from the committed rocprofv3 counter
     summary, when it was taken on the kernel's current source; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.md")
@@ -84,7 +98,7 @@ def traffic_from_profile(kernel, workload, kernel_src):
     text = open(path).read()
     m_src = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_src and m_b) or m_src.group(1) != source_digest(kernel_src):
+    if not (m_src and m_b) or m_src.group(1) != source_digest(kernel_sources(kernel)):
         return None
     return float(m_b.group(1))
 
@@ -108,17 +122,15 @@ def cpu_baseline(batch, budget_s):
             break
     return dict(value=batch.T * reps / el, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"the full {batch.name} step (T={batch.T}) repeated {reps} times, "
-                       f"{el:.1f} s on one host thread (plain C oracle, gcc -O2)",
-                seconds=el, reps=reps)
+                       f"{el:.1f} s on one host thread (plain C oracle, gcc -O2)")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_16x2048")
-    ap.add_argument("--no-flush", action="store_true", help="back-to-back steps (warm caches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -131,110 +143,110 @@ def main():
               f"(WORLD_SIZE {world}) is not supported", file=sys.stderr, flush=True)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import workloads
     from paged_kv_input_amd.step import DeviceStep, GroupSpec
 
     torch.cuda.set_device(0)
-    batch = workloads.make(args.workload)
-    groups = [GroupSpec(g.block_table, g.block_size, g.num_blocks, g.k, g.v) for g in batch.groups]
-    step = DeviceStep(batch.sched_rows, batch.num_scheduled, batch.completed, batch.token_ids,
-                      groups)
+    default_seed = workloads.CONFIGS[args.workload][1]
+    batches = [workloads.make(args.workload, seed=default_seed + 1000 * i) for i in range(ROTATE)]
+    batch = batches[0]
+    steps, caches = [], None
+    for b in batches:
+        st = DeviceStep(b.sched_rows, b.num_scheduled, b.completed, b.token_ids,
+                        [GroupSpec(g.block_table, g.block_size, g.num_blocks, g.k, g.v)
+                         for g in b.groups], caches=caches)
+        caches = [(g["k_cache"], g["v_cache"]) for g in st.groups]
+        steps.append(st)
     stream = torch.cuda.current_stream()
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
-    print(f"[bench] {batch.name}: n={batch.n} T={batch.T} groups={len(batch.groups)}",
-          file=sys.stderr, flush=True)
+    print(f"[bench] {batch.name}: n={batch.n} T={batch.T} groups={len(batch.groups)} "
+          f"rotating {ROTATE} batches", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
-            flush.fill_(1)
             dst.copy_(src)
         torch.cuda.synchronize()
 
     ng = len(batch.groups)
+    T = batch.T
 
-    def timed(run_fn, marks):
-        """W warm-up steps, then exactly K timed steps (cache flush before each,
-        outside the events); returns per-step lists of event intervals."""
-        for _ in range(args.warmup):
-            if not args.no_flush:
-                flush.fill_(1)
-            run_fn(None)
+    def back_to_back(run):
+        for i in range(args.warmup):
+            run(steps[i % ROTATE])
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)]
-              for _ in range(args.steps)]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
+        e0.record(stream)
         for i in range(args.steps):
-            if not args.no_flush:
-                flush.fill_(1)
-            run_fn(ev[i])
+            run(steps[i % ROTATE])
+        e1.record(stream)
         torch.cuda.synchronize()
-        return ev, time.perf_counter() - w0
+        wall = time.perf_counter() - w0
+        return e0.elapsed_time(e1) / args.steps, wall * 1e3 / args.steps
 
-    def calls(e):
-        # prepare_batch | compute_slot_mapping per group | scatter_kv per group
-        if e is not None:
-            e[0].record(stream)
-        step.prepare(stream)
-        if e is not None:
-            e[1].record(stream)
+    fused_ms, fused_wall = back_to_back(lambda s: s.run_fused(stream))
+    calls_ms, calls_wall = back_to_back(lambda s: s.run(stream))
+
+    # Per-call split of the three calls (events between the calls add their own
+    # overhead; for attribution only).
+    split = {"prepare_batch": [], "compute_slot_mapping": [], "scatter_kv": []}
+    reps = min(args.steps, 60)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for i in range(reps):
+        s, e = steps[i % ROTATE], marks[i]
+        e[0].record(stream)
+        s.prepare(stream)
+        e[1].record(stream)
         for gi in range(ng):
-            step.slots(gi, stream)
-        if e is not None:
-            e[2].record(stream)
+            s.slots(gi, stream)
+        e[2].record(stream)
         for gi in range(ng):
-            step.scatter(gi, stream)
-        if e is not None:
-            e[3].record(stream)
+            s.scatter(gi, stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    for e in marks:
+        split["prepare_batch"].append(e[0].elapsed_time(e[1]))
+        split["compute_slot_mapping"].append(e[1].elapsed_time(e[2]))
+        split["scatter_kv"].append(e[2].elapsed_time(e[3]))
 
-    def fused(e):
-        if e is not None:
-            e[0].record(stream)
-        step.run_fused(stream)
-        if e is not None:
-            e[1].record(stream)
+    # Single cold step: 1 GiB rewrite, then events around one fused step.
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    cold = []
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps):
+        flush.fill_(1)
+        cev[i][0].record(stream)
+        steps[i % ROTATE].run_fused(stream)
+        cev[i][1].record(stream)
+    torch.cuda.synchronize()
+    cold = [e[0].elapsed_time(e[1]) for e in cev]
+    del flush
 
-    ev_c, wall_c = timed(calls, 4)
-    ev_f, wall_f = timed(fused, 2)
-    if step.status_bits() != 0:
-        raise RuntimeError(f"device status bits set: {step.status_bits():#x}")
+    for s in steps:
+        if s.status_bits() != 0:
+            raise RuntimeError(f"device status bits set: {s.status_bits():#x}")
 
-    calls_ms = [e[0].elapsed_time(e[3]) for e in ev_c]
-    prep_ms = [e[0].elapsed_time(e[1]) for e in ev_c]
-    slot_ms = [e[1].elapsed_time(e[2]) for e in ev_c]
-    scat_ms = [e[2].elapsed_time(e[3]) for e in ev_c]
-    fused_ms = [e[0].elapsed_time(e[1]) for e in ev_f]
-    T = batch.T
     ab = algorithmic_bytes(batch)
-    use_fused = statistics.fmean(fused_ms) <= statistics.fmean(calls_ms)
-    step_ms = fused_ms if use_fused else calls_ms
-    ms = statistics.fmean(step_ms)
-
-    # Dominant kernel: the one launch of the fused step (all of the step's
-    # bytes), or scatter_kv when the separate calls are faster.
+    use_fused = fused_ms <= calls_ms
+    ms = fused_ms if use_fused else calls_ms
     if use_fused:
-        kernel, launch_ms, kbytes = "pkv_step (k_step)", ms, ab["total"]
-        src = os.path.join(ROOT, "paged_kv_input_amd", "csrc", "step.hip")
-        prof_key = "step"
+        kernel, launch_ms, kbytes, prof_key = "pkv_step (k_step)", fused_ms, ab["total"], "step"
     else:
         kernel = "scatter_kv (k_scatter)"
-        launch_ms = statistics.fmean(scat_ms) / ng
+        launch_ms = statistics.fmean(split["scatter_kv"]) / ng
         kbytes = statistics.fmean(scatter_bytes_per_launch(batch, gi) for gi in range(ng))
-        src = os.path.join(ROOT, "paged_kv_input_amd", "csrc", "scatter.hip")
         prof_key = "scatter_kv"
     achieved = kbytes / (launch_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(prof_key, args.workload, src)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(batch, args.cpu_seconds)
 
-    g0 = batch.groups[0]
     out = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -253,32 +265,23 @@ def main():
             "block_size": [g.block_size for g in batch.groups],
             "num_blocks": [g.num_blocks for g in batch.groups],
             "kv_row": [f"{g.num_heads}x{g.head_dim} {g.dtype}" for g in batch.groups],
-            "kv_groups": ng, "layers": 1,
-            "cache_state": "cold (1 GiB rewrite before each step)" if not args.no_flush else "warm",
+            "kv_groups": ng, "layers": 1, "rotating_batches": ROTATE,
         },
         "step": {
             "path": "pkv_step (one launch)" if use_fused else "three calls",
             "algorithmic_bytes": ab["total"],
             "hbm_gbs": ab["total"] / (ms * 1e-3) / 1e9,
             "frac_of_peak": ab["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "ms_median": statistics.median(step_ms),
-            "ms_p10": sorted(step_ms)[len(step_ms) // 10],
-            "ms_p90": sorted(step_ms)[(9 * len(step_ms)) // 10],
-            "wall_ms_per_step_incl_flush": (wall_f if use_fused else wall_c) * 1e3 / args.steps,
+            "wall_ms_per_step": fused_wall if use_fused else calls_wall,
         },
+        "fused": {"ms_per_step": fused_ms, "tokens_per_s": T / (fused_ms * 1e-3)},
         "three_calls": {
-            "ms_per_step": statistics.fmean(calls_ms),
-            "tokens_per_s": T / (statistics.fmean(calls_ms) * 1e-3),
-            "prepare_batch_ms": statistics.fmean(prep_ms),
-            "compute_slot_mapping_ms": statistics.fmean(slot_ms),
-            "scatter_kv_ms": statistics.fmean(scat_ms),
-            "scatter_kv_gbs": statistics.fmean(scatter_bytes_per_launch(batch, gi)
-                                               for gi in range(ng)) * ng
-            / (statistics.fmean(scat_ms) * 1e-3) / 1e9,
+            "ms_per_step": calls_ms, "tokens_per_s": T / (calls_ms * 1e-3),
+            "split_ms_with_events_between_calls": {k: statistics.fmean(v) for k, v in split.items()},
         },
-        "fused": {
-            "ms_per_step": statistics.fmean(fused_ms),
-            "tokens_per_s": T / (statistics.fmean(fused_ms) * 1e-3),
+        "cold_single_step": {
+            "ms_median": statistics.median(cold),
+            "note": "1 GiB rewrite before each step; HIP events around the single launch",
         },
         "roofline": {
             "kernel": kernel,
@@ -287,12 +290,11 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": traffic,
+            "traffic": traffic_from_profile(prof_key, args.workload),
             "algorithmic_bytes_per_launch": kbytes,
             "launch_ms": launch_ms,
         },
-        "cpu_baseline": ({k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
-                         if cpu else None),
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

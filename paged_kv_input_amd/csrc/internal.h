@@ -80,6 +80,8 @@ struct BatchLds {
     int64_t wave_total[kWaves];
     __device__ int32_t* row() { return reinterpret_cast<int32_t*>(key); }
     __device__ int32_t* done() { return reinterpret_cast<int32_t*>(key) + kMaxN; }
+    __device__ const int32_t* row() const { return reinterpret_cast<const int32_t*>(key); }
+    __device__ const int32_t* done() const { return reinterpret_cast<const int32_t*>(key) + kMaxN; }
 };
 
 // Batch assembly inside one workgroup ("Batch Construction and Sequence
@@ -223,8 +225,19 @@ __device__ inline void wave_sync()
 // itself, so that the workgroup's other wavefronts can keep their own memory
 // traffic in flight meanwhile.  Same results and flags as order_batch; the
 // caller must __syncthreads() before other wavefronts read the LDS outputs.
+// Each request's completed count is fetched right after its row arrives,
+// before the sort, and the sort carries every key's original index along so
+// the count can be found afterwards: the fetch overlaps the sort instead of
+// adding a dependent round trip after it.
 template <int kMaxN>
-__device__ inline void order_batch_wave(BatchLds<kMaxN, 1, true>& lds, int32_t n, int32_t T,
+struct WaveBatchLds {
+    BatchLds<kMaxN, 1, true> b;
+    int16_t idx[kMaxN];          // original index of each key during the sort
+    int32_t done_by_i[kMaxN];    // completed count by original index
+};
+
+template <int kMaxN>
+__device__ inline void order_batch_wave(WaveBatchLds<kMaxN>& w, int32_t n, int32_t T,
                                         const int32_t* __restrict__ sched_rows,
                                         const int32_t* __restrict__ num_scheduled,
                                         const int32_t* __restrict__ completed, int32_t R,
@@ -234,22 +247,52 @@ __device__ inline void order_batch_wave(BatchLds<kMaxN, 1, true>& lds, int32_t n
 {
     constexpr int kPer = kMaxN / kWave;
     static_assert(kMaxN % kWave == 0, "batch rows split evenly over lanes");
+    static_assert(kMaxN <= 32768, "original indices are kept in 16 bits");
+    BatchLds<kMaxN, 1, true>& lds = w.b;
     const int lane = threadIdx.x & (kWave - 1);
 
     int n_pad = 1;
     while (n_pad < n)
         n_pad <<= 1;
-    for (int i = lane; i < n_pad; i += kWave) {
+    // Gather: rows and counts, then at once each row's completed count.  The
+    // loads are unconditional, from a clamped in-bounds address where the
+    // value is not needed, so that each group of them is issued back to back
+    // (a load under a divergent branch is issued only after a full wait).
+    int32_t row_i[kPer];
+    int32_t cnt_i[kPer];
+    int32_t done_i[kPer];
+    const int nparts = (n + kWave - 1) / kWave;          // uniform
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int i = e * kWave + lane;
+        const int ic = i < n ? i : n - 1;
+        row_i[e] = e < nparts ? sched_rows[ic] : 0;
+        cnt_i[e] = e < nparts ? num_scheduled[ic] : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int i = e * kWave + lane;
+        const bool ok = i < n && row_i[e] >= 0 && row_i[e] < R;
+        done_i[e] = (e < nparts && R > 0) ? completed[ok ? row_i[e] : 0] : 0;
+        if (!ok)
+            done_i[e] = 0;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int i = e * kWave + lane;
+        if (i >= n_pad)
+            break;
         uint64_t key = ~0ull;                       // padding sorts last
         if (i < n) {
-            int32_t c = num_scheduled[i];
+            int32_t c = cnt_i[e];
             if (c < 0) {
                 flags |= PKV_ST_BAD_COUNT;
                 c = 0;
             }
-            key = sort_key(c, sched_rows[i]);
+            key = sort_key(c, row_i[e]);
         }
         lds.key[i] = key;
+        w.idx[i] = (int16_t)i;
     }
     wave_sync();
     for (int k = 2; k <= n_pad; k <<= 1) {
@@ -263,10 +306,20 @@ __device__ inline void order_batch_wave(BatchLds<kMaxN, 1, true>& lds, int32_t n
                 if ((a > b) == ascending) {
                     lds.key[lo] = b;
                     lds.key[hi] = a;
+                    const int16_t t = w.idx[lo];
+                    w.idx[lo] = w.idx[hi];
+                    w.idx[hi] = t;
                 }
             }
             wave_sync();
         }
+    }
+    // The completed counts have had the whole sort to arrive.
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int i = e * kWave + lane;
+        if (i < n)
+            w.done_by_i[i] = done_i[e];
     }
     uint64_t keys[kPer];
     int64_t local = 0;
@@ -282,16 +335,16 @@ __device__ inline void order_batch_wave(BatchLds<kMaxN, 1, true>& lds, int32_t n
     const uint32_t total_hi = __shfl((uint32_t)((uint64_t)incl >> 32), kWave - 1, kWave);
     const int64_t total = (int64_t)(((uint64_t)total_hi << 32) | total_lo);
     int64_t run = incl - local;
-    wave_sync();          // every key is in registers: lds.key may be reused
-    int32_t* s_row = lds.row();
-    int32_t* s_done = lds.done();
+    wave_sync();          // done_by_i is written; every key is in registers
     int32_t done_v[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
         const int b = first + e;
-        const int32_t row = key_row(keys[e]);
-        done_v[e] = (b < n && row >= 0 && row < R) ? completed[row] : 0;
+        done_v[e] = b < n ? w.done_by_i[w.idx[b]] : 0;
     }
+    wave_sync();          // lds.key is dead: row() / done() may overwrite it
+    int32_t* s_row = lds.row();
+    int32_t* s_done = lds.done();
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
         const int b = first + e;
@@ -304,7 +357,7 @@ __device__ inline void order_batch_wave(BatchLds<kMaxN, 1, true>& lds, int32_t n
         const bool row_ok = row >= 0 && row < R;
         lds.qsl[b + 1] = end;
         s_row[b] = row;
-        s_done[b] = done_v[e];
+        s_done[b] = row_ok ? done_v[e] : 0;
         lds.count[b] = c;
         if (writer) {
             index_mapping[b] = row;
@@ -325,6 +378,30 @@ __device__ inline void order_batch_wave(BatchLds<kMaxN, 1, true>& lds, int32_t n
                 flags |= PKV_ST_TOKEN_SUM;
         }
     }
+}
+
+#ifndef PKV_XCD_REMAP
+#define PKV_XCD_REMAP 0
+#endif
+constexpr int kXcds = 8;   // MI355X: 8 accelerator dies, workgroups dealt round-robin
+
+// Tile of workgroup `blk` among `tiles` tiles so that each XCD (which receives
+// workgroups blk = x, x + 8, x + 16, ...) walks one contiguous range of tiles:
+// neighbouring tiles share cache lines, block-table words and destination
+// pages, and now share them inside one XCD's L2 and translation caches.  A
+// bijection on [0, tiles) for any tile count.
+__device__ inline int64_t xcd_tile(int64_t blk, int64_t tiles)
+{
+#if PKV_XCD_REMAP
+    const int64_t x = blk % kXcds;
+    const int64_t k = blk / kXcds;
+    const int64_t q = tiles / kXcds;
+    const int64_t r = tiles % kXcds;
+    return x * q + (x < r ? x : r) + k;
+#else
+    (void)tiles;
+    return blk;
+#endif
 }
 
 // Launchers (host side).  Arguments are already validated; each returns a
@@ -350,8 +427,12 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
                        int32_t* positions, int32_t* input_ids, int32_t num_groups,
                        const pkv_group* groups, uint32_t* status, hipStream_t stream);
 
-// Workgroups launch_step would use (0 when it would launch its lone workgroup).
-int64_t step_grid_blocks(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
+// Work-items of the grid launch_step would launch.
+int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
+
+// Batch-ordering work of all of launch_step's workgroups together (each orders
+// the batch itself), in compare-exchanges up to a constant.
+int64_t step_sort_cost(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
 
 hipError_t launch_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride,
                           const void* v, int64_t v_stride, void* k_cache, void* v_cache,

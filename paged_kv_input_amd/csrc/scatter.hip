@@ -108,7 +108,8 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(
     int64_t v_stride16, u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
     int64_t num_slots, const int32_t* __restrict__ slot_mapping, uint32_t* __restrict__ status)
 {
-    const int64_t block0 = (int64_t)blockIdx.x * kChunksPerBlock;
+    const int64_t tiles = (total_chunks + kChunksPerBlock - 1) / kChunksPerBlock;
+    const int64_t block0 = xcd_tile(blockIdx.x, tiles) * kChunksPerBlock;
     const int64_t base = block0 + threadIdx.x;
     uint32_t flags = 0;
     if (block0 + kChunksPerBlock <= total_chunks)

@@ -28,13 +28,25 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCopyThreads = 256;                         // four copy wavefronts
+#ifndef PKV_STEP_COPY_WAVES
+#define PKV_STEP_COPY_WAVES 3
+#endif
+#ifndef PKV_STEP_UNROLL
+#define PKV_STEP_UNROLL 8
+#endif
+
+#ifndef PKV_STEP_WGS_PER_GROUP
+#define PKV_STEP_WGS_PER_GROUP 1536
+#endif
+
+constexpr int kCopyThreads = PKV_STEP_COPY_WAVES * kWave; // copy wavefronts
 constexpr int kStepThreads = kCopyThreads + kWave;        // plus one index wavefront
-constexpr int kStepUnroll = 8;
+constexpr int kStepUnroll = PKV_STEP_UNROLL;
 constexpr int kStepChunks = kCopyThreads * kStepUnroll;   // 16-byte chunks per round
 constexpr int kStepMaxTile = 256;                         // tokens per tile, at most
 constexpr int kTokensPerLane = kStepMaxTile / kWave;
 constexpr int kPageRows = kCopyThreads / kWave;           // batch rows per page workgroup
+constexpr int kTileWorkgroups = PKV_STEP_WGS_PER_GROUP;  // persistent tile workgroups per group
 
 struct StepGroup {
     const int32_t* block_table;
@@ -56,7 +68,8 @@ struct StepGroup {
     int32_t tile_tokens;
     int32_t rounds;          // ceil(tile_tokens * chunks_per_row / kStepChunks)
     int32_t first_block;     // first workgroup of this group's tiles
-    int32_t tile_blocks;
+    int32_t tiles;           // ceil(T / tile_tokens)
+    int32_t tile_blocks;     // persistent workgroups walking those tiles
     int32_t page_blocks;
 };
 
@@ -139,7 +152,7 @@ __device__ inline void store_round(const StepGroup& g, const int32_t* s_slot,
 // pkv_prepare_batch and pkv_compute_slot_mapping.  All of a lane's
 // block-table and token-table loads are issued together.
 __device__ inline void tile_tokens(const StepArgs& a, const StepGroup& g, bool first_group,
-                                   BatchLds<PKV_STEP_MAX_BATCH, 1, true>& lds, int64_t t0,
+                                   const BatchLds<PKV_STEP_MAX_BATCH, 1, true>& lds, int64_t t0,
                                    int tile_len, int32_t* s_slot, uint32_t& flags)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -187,12 +200,22 @@ __device__ inline void tile_tokens(const StepArgs& a, const StepGroup& g, bool f
         }
         bt_src[u] = (int64_t)row * g.MB + lb;
     }
+    // Unconditional loads from clamped in-bounds addresses (see
+    // order_batch_wave), so all of a lane's lookups are in flight together.
+    // A valid source exists only when the table is non-empty (uniform test).
+    const int parts = (tile_len + kWave - 1) / kWave;      // uniform
+    const bool have_bt = a.R > 0 && g.MB > 0;
+    const bool have_ids = a.input_ids != nullptr && a.R > 0 && a.L > 0;
     int32_t blk[kTokensPerLane];
     int32_t ids[kTokensPerLane];
 #pragma unroll
     for (int u = 0; u < kTokensPerLane; ++u) {
-        blk[u] = bt_src[u] >= 0 ? g.block_table[bt_src[u]] : -1;
-        ids[u] = id_src[u] >= 0 ? a.token_ids[id_src[u]] : -1;
+        blk[u] = (u < parts && have_bt) ? g.block_table[bt_src[u] >= 0 ? bt_src[u] : 0] : -1;
+        ids[u] = (u < parts && have_ids) ? a.token_ids[id_src[u] >= 0 ? id_src[u] : 0] : -1;
+        if (bt_src[u] < 0)
+            blk[u] = -1;
+        if (id_src[u] < 0)
+            ids[u] = -1;
     }
 #pragma unroll
     for (int u = 0; u < kTokensPerLane; ++u) {
@@ -258,8 +281,9 @@ __device__ inline void copy_pages(const StepArgs& a, const StepGroup& g,
 
 __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a)
 {
-    __shared__ BatchLds<PKV_STEP_MAX_BATCH, 1, true> lds;
-    __shared__ int32_t s_slot[kStepMaxTile];
+    __shared__ WaveBatchLds<PKV_STEP_MAX_BATCH> wlds;
+    BatchLds<PKV_STEP_MAX_BATCH, 1, true>& lds = wlds.b;
+    __shared__ int32_t s_slot[2 * kStepMaxTile];
 
     const int tid = threadIdx.x;
     const int blk = blockIdx.x;
@@ -284,36 +308,57 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a)
     }
 
     if (gi >= 0 && !page) {
+        // Persistent: this workgroup walks tiles local, local + G, ... of its
+        // group (G = tile_blocks), so at any moment the workgroups work on
+        // neighbouring tiles.  The index wavefront orders the batch once, then
+        // computes tile i+1's slots while the copy wavefronts write tile i and
+        // fetch tile i+1; the slot buffer is double-buffered across barriers.
         const StepGroup& g = a.g[gi];
-        const int64_t t0 = (int64_t)local * g.tile_tokens;
-        const int tile_len = (int)(a.T - t0 < g.tile_tokens ? a.T - t0 : g.tile_tokens);
+        const int64_t G = g.tile_blocks;
+        int64_t tile = local;
         u32x4 kv[kStepUnroll];
         u32x4 vv[kStepUnroll];
         int32_t tl[kStepUnroll];
         int32_t ch[kStepUnroll];
+        auto tile_len = [&](int64_t t) {
+            const int64_t t0 = t * g.tile_tokens;
+            return (int)(a.T - t0 < g.tile_tokens ? a.T - t0 : g.tile_tokens);
+        };
         if (!index_wave) {
-            load_round(g, t0, tile_len, 0, kv, vv, tl, ch);
+            load_round(g, tile * g.tile_tokens, tile_len(tile), 0, kv, vv, tl, ch);
         } else {
-            order_batch_wave<PKV_STEP_MAX_BATCH>(lds, a.n, a.T, a.sched_rows, a.num_scheduled,
+            order_batch_wave<PKV_STEP_MAX_BATCH>(wlds, a.n, a.T, a.sched_rows, a.num_scheduled,
                                                  a.completed, a.R, blk == 0, a.index_mapping,
                                                  a.query_start_loc, a.seq_lens, flags);
             if (blk != 0)
                 flags &= ~(uint32_t)PKV_ST_BAD_COUNT;   // per-request flags: workgroup 0 only
             wave_sync();
-            tile_tokens(a, g, gi == 0, lds, t0, tile_len, s_slot, flags);
+            tile_tokens(a, g, gi == 0, lds, tile * g.tile_tokens, tile_len(tile), s_slot, flags);
         }
         __syncthreads();
-        if (!index_wave) {
-            store_round(g, s_slot, kv, vv, tl, ch, flags);
-            for (int r = 1; r < g.rounds; ++r) {
-                load_round(g, t0, tile_len, r, kv, vv, tl, ch);
-                store_round(g, s_slot, kv, vv, tl, ch, flags);
+        int buf = 0;
+        for (; tile < g.tiles; tile += G) {
+            const int64_t next = tile + G;
+            if (!index_wave) {
+                const int32_t* slots = s_slot + buf * kStepMaxTile;
+                store_round(g, slots, kv, vv, tl, ch, flags);
+                for (int r = 1; r < g.rounds; ++r) {
+                    load_round(g, tile * g.tile_tokens, tile_len(tile), r, kv, vv, tl, ch);
+                    store_round(g, slots, kv, vv, tl, ch, flags);
+                }
+                if (next < g.tiles)
+                    load_round(g, next * g.tile_tokens, tile_len(next), 0, kv, vv, tl, ch);
+            } else if (next < g.tiles) {
+                tile_tokens(a, g, gi == 0, lds, next * g.tile_tokens, tile_len(next),
+                            s_slot + (buf ^ 1) * kStepMaxTile, flags);
             }
+            __syncthreads();
+            buf ^= 1;
         }
     } else {
         // Page workgroups, and the lone workgroup of a step with nothing else.
         if (index_wave) {
-            order_batch_wave<PKV_STEP_MAX_BATCH>(lds, a.n, a.T, a.sched_rows, a.num_scheduled,
+            order_batch_wave<PKV_STEP_MAX_BATCH>(wlds, a.n, a.T, a.sched_rows, a.num_scheduled,
                                                  a.completed, a.R, blk == 0, a.index_mapping,
                                                  a.query_start_loc, a.seq_lens, flags);
             if (blk != 0)
@@ -379,7 +424,8 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
         g.tile_tokens = (int32_t)tile;
         g.rounds = (int32_t)((tile * cpr + kStepChunks - 1) / kStepChunks);
         g.first_block = (int32_t)blocks;
-        g.tile_blocks = (int32_t)(((int64_t)T + tile - 1) / tile);
+        g.tiles = (int32_t)(((int64_t)T + tile - 1) / tile);
+        g.tile_blocks = g.tiles < kTileWorkgroups ? g.tiles : kTileWorkgroups;
         g.page_blocks = in.input_block_tables != nullptr ? (n + kPageRows - 1) / kPageRows : 0;
         blocks += (int64_t)g.tile_blocks + g.page_blocks;
     }
@@ -389,7 +435,19 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
     return hipGetLastError();
 }
 
-int64_t step_grid_blocks(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups)
+int64_t step_sort_cost(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups)
+{
+    // Every fused workgroup orders the batch itself: a bitonic sort of n_pad
+    // keys costs about n_pad * log2(n_pad)^2 / 2 compare-exchanges.
+    int64_t n_pad = 1, lg = 0;
+    while (n_pad < n) {
+        n_pad <<= 1;
+        ++lg;
+    }
+    return (step_grid_threads(n, T, num_groups, groups) / kStepThreads) * n_pad * lg * lg;
+}
+
+int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups)
 {
     int64_t blocks = 0;
     for (int i = 0; i < num_groups; ++i) {
@@ -397,11 +455,12 @@ int64_t step_grid_blocks(int32_t n, int32_t T, int32_t num_groups, const pkv_gro
         int64_t tile = cpr >= kStepChunks ? 1 : kStepChunks / cpr;
         if (tile > kStepMaxTile)
             tile = kStepMaxTile;
-        blocks += ((int64_t)T + tile - 1) / tile;
+        const int64_t tiles = ((int64_t)T + tile - 1) / tile;
+        blocks += tiles < kTileWorkgroups ? tiles : kTileWorkgroups;
         if (groups[i].input_block_tables != nullptr)
             blocks += (n + kPageRows - 1) / kPageRows;
     }
-    return blocks;
+    return (blocks > 0 ? blocks : 1) * kStepThreads;
 }
 
 }  // namespace pkv

@@ -32,7 +32,8 @@ class DeviceStep:
     def __init__(self, sched_rows, num_scheduled, completed, token_ids,
                  groups: Sequence[GroupSpec], *, device="cuda", cache_fill: Optional[int] = None,
                  ibt_fill: Optional[int] = None, with_input_ids: bool = True,
-                 with_block_tables: bool = True, num_tokens: Optional[int] = None):
+                 with_block_tables: bool = True, num_tokens: Optional[int] = None,
+                 caches: Optional[Sequence] = None):
         dev = torch.device(device)
 
         def up(a, dtype=None):
@@ -63,8 +64,12 @@ class DeviceStep:
             v = up(np.ascontiguousarray(g.v).view(np.int16))
             row_shape = tuple(k.shape[1:])
             num_slots = int(g.num_blocks) * int(g.block_size)
-            kc = torch.empty((num_slots, *row_shape), dtype=k.dtype, device=dev)
-            vc = torch.empty((num_slots, *row_shape), dtype=k.dtype, device=dev)
+            if caches is not None:       # shared with another step (same pool and layout)
+                kc, vc = caches[len(self.groups)]
+                assert kc.shape == (num_slots, *row_shape) and kc.dtype == k.dtype
+            else:
+                kc = torch.empty((num_slots, *row_shape), dtype=k.dtype, device=dev)
+                vc = torch.empty((num_slots, *row_shape), dtype=k.dtype, device=dev)
             if cache_fill is not None:
                 kc.fill_(cache_fill)
                 vc.fill_(cache_fill)
