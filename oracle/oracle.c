@@ -90,8 +90,8 @@ static int by_tokens_then_row(const void* pa, const void* pb)
  *
  * R3: a position starts at completed_tokens, the value *before* this step
  *     (31 done -> position 31; 16 done -> positions 16..23 in the example).
- * R4: input_ids[t] = token_ids[row][position]: the "corresponding positions" of
- *     the request's token list, kept as a persistent per-row table.
+ * R4: input_ids[t] = token_ids[row][position]: the request's token list read at
+ *     the token's own position, kept as a persistent per-row table.
  * R5: seq_lens[b] = completed + tokens this step (history plus new).
  * R6 (data errors, never out-of-bounds accesses): a row outside [0, R) leaves
  *     its request in the batch order with seq_len -1 and its tokens at position
