@@ -168,11 +168,10 @@ int pkv_scatter_kv(int32_t T, int64_t row_bytes,
  * KV-cache group pkv_compute_slot_mapping and pkv_scatter_kv (the first layer's
  * K/V).  The outputs, status bits and return codes are exactly those of that
  * sequence of calls; later layers reuse each group's slot_mapping with
- * pkv_scatter_kv.  With n <= PKV_STEP_MAX_BATCH, 1 <= num_groups <=
- * PKV_STEP_MAX_GROUPS and a batch small enough for every workgroup to order
- * it cheaply (workgroups x n log^2 n under a fixed budget), everything runs in
- * a single kernel launch; otherwise the call enqueues the separate kernels of
- * that sequence.  Either way the results are the same.
+ * pkv_scatter_kv.  With n <= PKV_STEP_MAX_BATCH and 1 <= num_groups <=
+ * PKV_STEP_MAX_GROUPS everything runs in a single kernel launch; otherwise the
+ * call enqueues the separate kernels of that sequence.  Either way the results
+ * are the same.
  *
  * The schedule and per-request outputs are as for pkv_prepare_batch (R and the
  * token table are shared by all groups).  groups is a HOST array of num_groups

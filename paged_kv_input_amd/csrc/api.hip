@@ -156,16 +156,11 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
             return rc;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // One launch unless the batch is too large to order inside every
-    // workgroup cheaply: then the separate kernels (one ordering in total,
-    // back-to-back launches) are faster.  Measured on MI355X: 16 and 72
-    // requests and 256 decodes gain 9-11 us from fusing; 512 requests over
-    // 68k tokens in two groups lose 85 us.
-    constexpr int64_t kMaxFusedSortCost = (int64_t)1 << 24;
+    // One launch whenever the batch fits the in-LDS ordering of every
+    // workgroup and the group count fits the kernel arguments.
     const bool fused = n <= PKV_STEP_MAX_BATCH && num_groups >= 1 &&
                        num_groups <= PKV_STEP_MAX_GROUPS &&
-                       pkv::step_grid_threads(n, T, num_groups, groups) < kMaxGridThreads &&
-                       pkv::step_sort_cost(n, T, num_groups, groups) <= kMaxFusedSortCost;
+                       pkv::step_grid_threads(n, T, num_groups, groups) < kMaxGridThreads;
     if (fused)
         return from_hip(pkv::launch_step(n, T, sched_rows, num_scheduled, completed, R, token_ids,
                                          token_stride, L, index_mapping, query_start_loc,

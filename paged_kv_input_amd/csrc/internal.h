@@ -174,6 +174,18 @@ __device__ inline void order_batch(BatchLds<kMaxN, kThreads / kWave, kCounts>& l
 
     int32_t* s_row = lds.row();
     int32_t* s_done = lds.done();
+    // All of a thread's completed counts in one round trip: unconditional
+    // loads from a clamped in-bounds row (a load under a divergent branch is
+    // issued only after a full wait).
+    int32_t done_v[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int32_t row = key_row(keys[e]);
+        const bool ok = first + e < n && row >= 0 && row < R;
+        done_v[e] = R > 0 ? completed[ok ? row : 0] : 0;
+        if (!ok)
+            done_v[e] = 0;
+    }
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
         const int b = first + e;
@@ -185,7 +197,7 @@ __device__ inline void order_batch(BatchLds<kMaxN, kThreads / kWave, kCounts>& l
         const int32_t end = run > INT32_MAX ? INT32_MAX : (int32_t)run;
         lds.qsl[b + 1] = end;
         const bool row_ok = row >= 0 && row < R;
-        const int32_t done = row_ok ? completed[row] : 0;
+        const int32_t done = done_v[e];
         s_row[b] = row;
         s_done[b] = done;
         if (kCounts)
@@ -221,14 +233,22 @@ __device__ inline void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// order_batch done by ONE wavefront of the workgroup, synchronizing only
-// itself, so that the workgroup's other wavefronts can keep their own memory
-// traffic in flight meanwhile.  Same results and flags as order_batch; the
-// caller must __syncthreads() before other wavefronts read the LDS outputs.
-// Each request's completed count is fetched right after its row arrives,
-// before the sort, and the sort carries every key's original index along so
-// the count can be found afterwards: the fetch overlaps the sort instead of
-// adding a dependent round trip after it.
+// Batch ordering inside a workgroup whose global loads are all made by ONE
+// wavefront (the "index" wavefront), so that the workgroup's other wavefronts
+// can keep their own memory traffic in flight meanwhile (a wavefront's loads
+// complete in issue order).  Same results and flags as order_batch.  Three
+// phases:
+//   wave_gather  (index wavefront) loads rows and counts, then at once each
+//                row's completed count, and writes the keys and their original
+//                indices to LDS; the completed counts stay in registers;
+//   sort         bitonic sort of the keys, carrying the indices: by the index
+//                wavefront alone (wave_sort, n <= 64) or by every wavefront of
+//                the workgroup (block_sort, LDS traffic only, so the other
+//                wavefronts' loads stay in flight);
+//   wave_finish  (index wavefront) prefix sums, rows, completed counts and the
+//                per-request outputs.
+// The fetch of the completed counts thus overlaps the sort instead of adding a
+// dependent round trip after it.
 template <int kMaxN>
 struct WaveBatchLds {
     BatchLds<kMaxN, 1, true> b;
@@ -237,30 +257,36 @@ struct WaveBatchLds {
 };
 
 template <int kMaxN>
-__device__ inline void order_batch_wave(WaveBatchLds<kMaxN>& w, int32_t n, int32_t T,
-                                        const int32_t* __restrict__ sched_rows,
-                                        const int32_t* __restrict__ num_scheduled,
-                                        const int32_t* __restrict__ completed, int32_t R,
-                                        bool writer, int32_t* __restrict__ index_mapping,
-                                        int32_t* __restrict__ query_start_loc,
-                                        int32_t* __restrict__ seq_lens, uint32_t& flags)
-{
-    constexpr int kPer = kMaxN / kWave;
-    static_assert(kMaxN % kWave == 0, "batch rows split evenly over lanes");
-    static_assert(kMaxN <= 32768, "original indices are kept in 16 bits");
-    BatchLds<kMaxN, 1, true>& lds = w.b;
-    const int lane = threadIdx.x & (kWave - 1);
+struct WaveGather {
+    static constexpr int kPer = kMaxN / kWave;
+    int32_t done_i[kPer];        // completed count of request e * 64 + lane
+};
 
+__device__ inline int pad_pow2(int n)
+{
     int n_pad = 1;
     while (n_pad < n)
         n_pad <<= 1;
-    // Gather: rows and counts, then at once each row's completed count.  The
-    // loads are unconditional, from a clamped in-bounds address where the
-    // value is not needed, so that each group of them is issued back to back
-    // (a load under a divergent branch is issued only after a full wait).
+    return n_pad;
+}
+
+template <int kMaxN>
+__device__ inline void wave_gather(WaveBatchLds<kMaxN>& w, WaveGather<kMaxN>& gth, int32_t n,
+                                   const int32_t* __restrict__ sched_rows,
+                                   const int32_t* __restrict__ num_scheduled,
+                                   const int32_t* __restrict__ completed, int32_t R,
+                                   uint32_t& flags)
+{
+    constexpr int kPer = WaveGather<kMaxN>::kPer;
+    static_assert(kMaxN % kWave == 0, "batch rows split evenly over lanes");
+    static_assert(kMaxN <= 32768, "original indices are kept in 16 bits");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n_pad = pad_pow2(n);
+    // Unconditional loads from a clamped in-bounds address where the value is
+    // not needed, so each group of them is issued back to back (a load under a
+    // divergent branch is issued only after a full wait).
     int32_t row_i[kPer];
     int32_t cnt_i[kPer];
-    int32_t done_i[kPer];
     const int nparts = (n + kWave - 1) / kWave;          // uniform
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
@@ -273,9 +299,9 @@ __device__ inline void order_batch_wave(WaveBatchLds<kMaxN>& w, int32_t n, int32
     for (int e = 0; e < kPer; ++e) {
         const int i = e * kWave + lane;
         const bool ok = i < n && row_i[e] >= 0 && row_i[e] < R;
-        done_i[e] = (e < nparts && R > 0) ? completed[ok ? row_i[e] : 0] : 0;
+        gth.done_i[e] = (e < nparts && R > 0) ? completed[ok ? row_i[e] : 0] : 0;
         if (!ok)
-            done_i[e] = 0;
+            gth.done_i[e] = 0;
     }
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
@@ -291,35 +317,76 @@ __device__ inline void order_batch_wave(WaveBatchLds<kMaxN>& w, int32_t n, int32
             }
             key = sort_key(c, row_i[e]);
         }
-        lds.key[i] = key;
+        w.b.key[i] = key;
         w.idx[i] = (int16_t)i;
     }
-    wave_sync();
-    for (int k = 2; k <= n_pad; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = lane; i < (n_pad >> 1); i += kWave) {
-                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-                const int hi = lo + j;
-                const bool ascending = (lo & k) == 0;
-                const uint64_t a = lds.key[lo];
-                const uint64_t b = lds.key[hi];
-                if ((a > b) == ascending) {
-                    lds.key[lo] = b;
-                    lds.key[hi] = a;
-                    const int16_t t = w.idx[lo];
-                    w.idx[lo] = w.idx[hi];
-                    w.idx[hi] = t;
-                }
-            }
-            wave_sync();
+}
+
+// One bitonic compare-exchange pass (distance j inside sequences of size k)
+// over pairs first, first + step, ... of the n_pad / 2 pairs.
+template <int kMaxN>
+__device__ inline void bitonic_pass(WaveBatchLds<kMaxN>& w, int n_pad, int k, int j, int first,
+                                    int step)
+{
+    for (int i = first; i < (n_pad >> 1); i += step) {
+        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const int hi = lo + j;
+        const bool ascending = (lo & k) == 0;
+        const uint64_t a = w.b.key[lo];
+        const uint64_t b = w.b.key[hi];
+        if ((a > b) == ascending) {
+            w.b.key[lo] = b;
+            w.b.key[hi] = a;
+            const int16_t t = w.idx[lo];
+            w.idx[lo] = w.idx[hi];
+            w.idx[hi] = t;
         }
     }
+}
+
+// Sort by the index wavefront alone (call from that wavefront only).
+template <int kMaxN>
+__device__ inline void wave_sort(WaveBatchLds<kMaxN>& w, int32_t n)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n_pad = pad_pow2(n);
+    wave_sync();
+    for (int k = 2; k <= n_pad; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            bitonic_pass(w, n_pad, k, j, lane, kWave);
+            wave_sync();
+        }
+}
+
+// Sort by all kThreads threads of the workgroup (call from every thread).
+template <int kThreads, int kMaxN>
+__device__ inline void block_sort(WaveBatchLds<kMaxN>& w, int32_t n)
+{
+    const int n_pad = pad_pow2(n);
+    __syncthreads();
+    for (int k = 2; k <= n_pad; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            bitonic_pass(w, n_pad, k, j, (int)threadIdx.x, kThreads);
+            __syncthreads();
+        }
+}
+
+template <int kMaxN>
+__device__ inline void wave_finish(WaveBatchLds<kMaxN>& w, const WaveGather<kMaxN>& gth,
+                                   int32_t n, int32_t T, int32_t R, bool writer,
+                                   int32_t* __restrict__ index_mapping,
+                                   int32_t* __restrict__ query_start_loc,
+                                   int32_t* __restrict__ seq_lens, uint32_t& flags)
+{
+    constexpr int kPer = WaveGather<kMaxN>::kPer;
+    BatchLds<kMaxN, 1, true>& lds = w.b;
+    const int lane = threadIdx.x & (kWave - 1);
     // The completed counts have had the whole sort to arrive.
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
         const int i = e * kWave + lane;
         if (i < n)
-            w.done_by_i[i] = done_i[e];
+            w.done_by_i[i] = gth.done_i[e];
     }
     uint64_t keys[kPer];
     int64_t local = 0;
@@ -429,10 +496,6 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
 
 // Work-items of the grid launch_step would launch.
 int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
-
-// Batch-ordering work of all of launch_step's workgroups together (each orders
-// the batch itself), in compare-exchanges up to a constant.
-int64_t step_sort_cost(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
 
 hipError_t launch_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride,
                           const void* v, int64_t v_stride, void* k_cache, void* v_cache,

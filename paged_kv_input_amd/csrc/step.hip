@@ -7,12 +7,14 @@
 // coordinate-conversion pipeline and the K/V write at slot_mapping).
 //
 // Design (gfx950): the grid is the K/V copy.  Each workgroup owns a tile of
-// flat tokens of one group and has four copy wavefronts plus one index
-// wavefront.  The copy wavefronts issue the tile's K/V loads at once (32 KiB of
-// each per round; they depend on nothing) and wait at a single barrier.
+// flat tokens of one group and has three copy wavefronts plus one index
+// wavefront, one per SIMD.  The copy wavefronts issue the tile's K/V loads at
+// once (24 KiB of each per round; they depend on nothing) and wait at a
+// single barrier.
 // Meanwhile the index wavefront orders the batch itself in LDS
-// (order_batch_wave: a bitonic sort of at most PKV_STEP_MAX_BATCH keys and a
-// scan, synchronizing only itself), resolves the tile's tokens to requests by
+// (wave_gather / wave_sort or block_sort / wave_finish: a bitonic sort of at
+// most PKV_STEP_MAX_BATCH keys, done by the index wavefront alone for small
+// batches and by every wavefront for large ones, and a wave-level scan), resolves the tile's tokens to requests by
 // binary search, and computes positions, input ids and slots.  After the
 // barrier the copy wavefronts write the held rows to their slots.  Splitting
 // the roles across wavefronts matters: a wavefront's loads complete in issue
@@ -32,11 +34,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define PKV_STEP_COPY_WAVES 3
 #endif
 #ifndef PKV_STEP_UNROLL
-#define PKV_STEP_UNROLL 8
+#define PKV_STEP_UNROLL 6
 #endif
 
 #ifndef PKV_STEP_WGS_PER_GROUP
-#define PKV_STEP_WGS_PER_GROUP 1536
+#define PKV_STEP_WGS_PER_GROUP 1536        // persistent tile workgroups per group, n <= 64
+#endif
+#ifndef PKV_STEP_WGS_PER_GROUP_BIG
+#define PKV_STEP_WGS_PER_GROUP_BIG 1024    // n > 64: fewer workgroups, fewer sorts
 #endif
 
 constexpr int kCopyThreads = PKV_STEP_COPY_WAVES * kWave; // copy wavefronts
@@ -46,7 +51,13 @@ constexpr int kStepChunks = kCopyThreads * kStepUnroll;   // 16-byte chunks per 
 constexpr int kStepMaxTile = 256;                         // tokens per tile, at most
 constexpr int kTokensPerLane = kStepMaxTile / kWave;
 constexpr int kPageRows = kCopyThreads / kWave;           // batch rows per page workgroup
-constexpr int kTileWorkgroups = PKV_STEP_WGS_PER_GROUP;  // persistent tile workgroups per group
+// Persistent tile workgroups per group: every workgroup orders the batch once,
+// so large batches use fewer of them (measured on MI355X: 1536 is best for a
+// 16-request prefill, 512-1024 for 72-512 requests).
+__host__ inline int64_t tile_workgroups(int32_t n)
+{
+    return n <= kWave ? PKV_STEP_WGS_PER_GROUP : PKV_STEP_WGS_PER_GROUP_BIG;
+}
 
 struct StepGroup {
     const int32_t* block_table;
@@ -96,34 +107,46 @@ struct StepArgs {
 __device__ inline u32x4 nt_load(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ inline void nt_store(u32x4 x, u32x4* p) { __builtin_nontemporal_store(x, p); }
 
-// Issue one round of a tile's K/V loads.  tl[u] is the token within the tile
-// of lane chunk u, or -1 past the tile (then a harmless load of the tile's
-// first chunk keeps the code branch-free).
-__device__ inline void load_round(const StepGroup& g, int64_t t0, int tile_len, int round,
-                                  u32x4 (&kv)[kStepUnroll], u32x4 (&vv)[kStepUnroll],
-                                  int32_t (&tl)[kStepUnroll], int32_t (&ch)[kStepUnroll])
+// Token within the tile and 16-byte chunk within its row of lane chunk u of a
+// round; tok = -1 past the tile.  Recomputed where needed instead of kept in
+// registers.
+template <bool kPow2Row>
+__device__ inline void chunk_of(const StepGroup& g, int tile_len, int round, int u, int& tok,
+                                int& c)
 {
-#pragma unroll
-    for (int u = 0; u < kStepUnroll; ++u) {
-        const int idx = round * kStepChunks + u * kCopyThreads + (int)threadIdx.x;
-        int tok = g.row_shift >= 0 ? (idx >> g.row_shift) : idx / g.chunks_per_row;
-        int c = idx - tok * g.chunks_per_row;
-        if (tok >= tile_len) {
-            tok = -1;
-            c = 0;
-        }
-        const int64_t t = t0 + (tok >= 0 ? tok : 0);
-        kv[u] = nt_load(g.k + t * g.k_stride16 + c);
-        vv[u] = nt_load(g.v + t * g.v_stride16 + c);
-        tl[u] = tok;
-        ch[u] = c;
+    const int idx = round * kStepChunks + u * kCopyThreads + (int)threadIdx.x;
+    tok = kPow2Row ? (idx >> g.row_shift) : idx / g.chunks_per_row;
+    c = idx - tok * g.chunks_per_row;
+    if (tok >= tile_len) {
+        tok = -1;
+        c = 0;
     }
 }
 
-__device__ inline void store_round(const StepGroup& g, const int32_t* s_slot,
-                                   u32x4 (&kv)[kStepUnroll], u32x4 (&vv)[kStepUnroll],
-                                   const int32_t (&tl)[kStepUnroll],
-                                   const int32_t (&ch)[kStepUnroll], uint32_t& flags)
+// Issue one round of a tile's K/V loads; chunks past the tile load the
+// tile's first chunk instead (harmless, keeps the code branch-free).
+template <bool kPow2Row>
+__device__ inline void load_round(const StepGroup& g, int64_t t0, int tile_len, int round,
+                                  u32x4 (&kv)[kStepUnroll], u32x4 (&vv)[kStepUnroll])
+{
+    // Uniform tile bases plus 32-bit offsets (the host keeps a tile's span
+    // under 4 GiB): one address register per load instead of two.
+    const u32x4* kb = g.k + t0 * g.k_stride16;
+    const u32x4* vb = g.v + t0 * g.v_stride16;
+#pragma unroll
+    for (int u = 0; u < kStepUnroll; ++u) {
+        int tok, c;
+        chunk_of<kPow2Row>(g, tile_len, round, u, tok, c);
+        const uint32_t t = (uint32_t)(tok >= 0 ? tok : 0);
+        kv[u] = nt_load(kb + (t * (uint32_t)g.k_stride16 + (uint32_t)c));
+        vv[u] = nt_load(vb + (t * (uint32_t)g.v_stride16 + (uint32_t)c));
+    }
+}
+
+template <bool kPow2Row>
+__device__ inline void store_round(const StepGroup& g, const int32_t* s_slot, int tile_len,
+                                   int round, u32x4 (&kv)[kStepUnroll], u32x4 (&vv)[kStepUnroll],
+                                   uint32_t& flags)
 {
     // Pin the payload in registers here, so the loads stay ahead of the slot
     // tests instead of being sunk into the store branches.
@@ -132,16 +155,18 @@ __device__ inline void store_round(const StepGroup& g, const int32_t* s_slot,
         __asm__ volatile("" : "+v"(kv[u]), "+v"(vv[u]));
 #pragma unroll
     for (int u = 0; u < kStepUnroll; ++u) {
-        if (tl[u] < 0)
+        int tok, c;
+        chunk_of<kPow2Row>(g, tile_len, round, u, tok, c);
+        if (tok < 0)
             continue;
-        const int32_t slot = s_slot[tl[u]];
+        const int32_t slot = s_slot[tok];
         if (slot < 0)
             continue;
         if ((int64_t)slot >= g.num_slots) {
             flags |= PKV_ST_SLOT_OOR;
             continue;
         }
-        const int64_t dst = (int64_t)slot * g.chunks_per_row + ch[u];
+        const int64_t dst = (int64_t)slot * g.chunks_per_row + c;
         nt_store(kv[u], g.k_cache + dst);
         nt_store(vv[u], g.v_cache + dst);
     }
@@ -201,7 +226,7 @@ __device__ inline void tile_tokens(const StepArgs& a, const StepGroup& g, bool f
         bt_src[u] = (int64_t)row * g.MB + lb;
     }
     // Unconditional loads from clamped in-bounds addresses (see
-    // order_batch_wave), so all of a lane's lookups are in flight together.
+    // wave_gather), so all of a lane's lookups are in flight together.
     // A valid source exists only when the table is non-empty (uniform test).
     const int parts = (tile_len + kWave - 1) / kWave;      // uniform
     const bool have_bt = a.R > 0 && g.MB > 0;
@@ -279,15 +304,27 @@ __device__ inline void copy_pages(const StepArgs& a, const StepGroup& g,
     }
 }
 
+// Role of the calling wavefront as a scalar (SGPR) value, so that branches on
+// it are uniform jumps: each wavefront runs exactly one role's code, and each
+// role's code has the same sequence of barriers.  Keeping the roles in
+// separate code paths also lets the copy payload and the index temporaries
+// share registers.
+__device__ inline bool is_index_wave()
+{
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)) == PKV_STEP_COPY_WAVES;
+}
+
+template <bool kPow2Row>
 __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a)
 {
     __shared__ WaveBatchLds<PKV_STEP_MAX_BATCH> wlds;
-    BatchLds<PKV_STEP_MAX_BATCH, 1, true>& lds = wlds.b;
     __shared__ int32_t s_slot[2 * kStepMaxTile];
+    BatchLds<PKV_STEP_MAX_BATCH, 1, true>& lds = wlds.b;
 
     const int tid = threadIdx.x;
     const int blk = blockIdx.x;
-    const bool index_wave = tid >= kCopyThreads;
+    const bool index_wave = is_index_wave();
+    const bool big = pad_pow2(a.n) > kWave;      // sort by every wavefront
     uint32_t flags = 0;
 
     // Which group and which part of it this workgroup serves (uniform).
@@ -313,60 +350,83 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a)
         // neighbouring tiles.  The index wavefront orders the batch once, then
         // computes tile i+1's slots while the copy wavefronts write tile i and
         // fetch tile i+1; the slot buffer is double-buffered across barriers.
+        // Barriers per role: [block_sort's when big], then one per tile.
         const StepGroup& g = a.g[gi];
         const int64_t G = g.tile_blocks;
-        int64_t tile = local;
-        u32x4 kv[kStepUnroll];
-        u32x4 vv[kStepUnroll];
-        int32_t tl[kStepUnroll];
-        int32_t ch[kStepUnroll];
         auto tile_len = [&](int64_t t) {
             const int64_t t0 = t * g.tile_tokens;
             return (int)(a.T - t0 < g.tile_tokens ? a.T - t0 : g.tile_tokens);
         };
         if (!index_wave) {
-            load_round(g, tile * g.tile_tokens, tile_len(tile), 0, kv, vv, tl, ch);
+            u32x4 kv[kStepUnroll];
+            u32x4 vv[kStepUnroll];
+            int64_t tile = local;
+            load_round<kPow2Row>(g, tile * g.tile_tokens, tile_len(tile), 0, kv, vv);
+            if (big)
+                block_sort<kStepThreads>(wlds, a.n);    // LDS only: the payload stays in flight
+            __syncthreads();                             // tile's slots are ready
+            int buf = 0;
+            for (; tile < g.tiles; tile += G) {
+                const int64_t next = tile + G;
+                const int32_t* slots = s_slot + buf * kStepMaxTile;
+                const int len = tile_len(tile);
+                store_round<kPow2Row>(g, slots, len, 0, kv, vv, flags);
+                for (int r = 1; r < g.rounds; ++r) {
+                    load_round<kPow2Row>(g, tile * g.tile_tokens, len, r, kv, vv);
+                    store_round<kPow2Row>(g, slots, len, r, kv, vv, flags);
+                }
+                if (next < g.tiles)
+                    load_round<kPow2Row>(g, next * g.tile_tokens, tile_len(next), 0, kv, vv);
+                __syncthreads();
+                buf ^= 1;
+            }
         } else {
-            order_batch_wave<PKV_STEP_MAX_BATCH>(wlds, a.n, a.T, a.sched_rows, a.num_scheduled,
-                                                 a.completed, a.R, blk == 0, a.index_mapping,
-                                                 a.query_start_loc, a.seq_lens, flags);
+            WaveGather<PKV_STEP_MAX_BATCH> gth;
+            wave_gather(wlds, gth, a.n, a.sched_rows, a.num_scheduled, a.completed, a.R, flags);
+            if (big)
+                block_sort<kStepThreads>(wlds, a.n);
+            else
+                wave_sort(wlds, a.n);
+            wave_finish(wlds, gth, a.n, a.T, a.R, blk == 0, a.index_mapping, a.query_start_loc,
+                        a.seq_lens, flags);
             if (blk != 0)
                 flags &= ~(uint32_t)PKV_ST_BAD_COUNT;   // per-request flags: workgroup 0 only
             wave_sync();
+            int64_t tile = local;
             tile_tokens(a, g, gi == 0, lds, tile * g.tile_tokens, tile_len(tile), s_slot, flags);
-        }
-        __syncthreads();
-        int buf = 0;
-        for (; tile < g.tiles; tile += G) {
-            const int64_t next = tile + G;
-            if (!index_wave) {
-                const int32_t* slots = s_slot + buf * kStepMaxTile;
-                store_round(g, slots, kv, vv, tl, ch, flags);
-                for (int r = 1; r < g.rounds; ++r) {
-                    load_round(g, tile * g.tile_tokens, tile_len(tile), r, kv, vv, tl, ch);
-                    store_round(g, slots, kv, vv, tl, ch, flags);
-                }
+            __syncthreads();                             // tile's slots are ready
+            int buf = 0;
+            for (; tile < g.tiles; tile += G) {
+                const int64_t next = tile + G;
                 if (next < g.tiles)
-                    load_round(g, next * g.tile_tokens, tile_len(next), 0, kv, vv, tl, ch);
-            } else if (next < g.tiles) {
-                tile_tokens(a, g, gi == 0, lds, next * g.tile_tokens, tile_len(next),
-                            s_slot + (buf ^ 1) * kStepMaxTile, flags);
+                    tile_tokens(a, g, gi == 0, lds, next * g.tile_tokens, tile_len(next),
+                                s_slot + (buf ^ 1) * kStepMaxTile, flags);
+                __syncthreads();
+                buf ^= 1;
             }
-            __syncthreads();
-            buf ^= 1;
         }
     } else {
         // Page workgroups, and the lone workgroup of a step with nothing else.
-        if (index_wave) {
-            order_batch_wave<PKV_STEP_MAX_BATCH>(wlds, a.n, a.T, a.sched_rows, a.num_scheduled,
-                                                 a.completed, a.R, blk == 0, a.index_mapping,
-                                                 a.query_start_loc, a.seq_lens, flags);
+        // Barriers per role: [block_sort's when big], then one.
+        if (!index_wave) {
+            if (big)
+                block_sort<kStepThreads>(wlds, a.n);
+            __syncthreads();
+            if (gi >= 0)
+                copy_pages(a, a.g[gi], lds, local * kPageRows + tid / kWave, flags);
+        } else {
+            WaveGather<PKV_STEP_MAX_BATCH> gth;
+            wave_gather(wlds, gth, a.n, a.sched_rows, a.num_scheduled, a.completed, a.R, flags);
+            if (big)
+                block_sort<kStepThreads>(wlds, a.n);
+            else
+                wave_sort(wlds, a.n);
+            wave_finish(wlds, gth, a.n, a.T, a.R, blk == 0, a.index_mapping, a.query_start_loc,
+                        a.seq_lens, flags);
             if (blk != 0)
                 flags &= ~(uint32_t)PKV_ST_BAD_COUNT;
+            __syncthreads();
         }
-        __syncthreads();
-        if (gi >= 0 && !index_wave)
-            copy_pages(a, a.g[gi], lds, local * kPageRows + tid / kWave, flags);
     }
     report_status(a.status, flags);
 }
@@ -425,26 +485,20 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
         g.rounds = (int32_t)((tile * cpr + kStepChunks - 1) / kStepChunks);
         g.first_block = (int32_t)blocks;
         g.tiles = (int32_t)(((int64_t)T + tile - 1) / tile);
-        g.tile_blocks = g.tiles < kTileWorkgroups ? g.tiles : kTileWorkgroups;
+        g.tile_blocks = (int32_t)(g.tiles < tile_workgroups(n) ? g.tiles : tile_workgroups(n));
         g.page_blocks = in.input_block_tables != nullptr ? (n + kPageRows - 1) / kPageRows : 0;
         blocks += (int64_t)g.tile_blocks + g.page_blocks;
     }
     if (blocks == 0)
         blocks = 1;      // still order the batch and write its per-request outputs
-    k_step<<<dim3((unsigned)blocks), dim3(kStepThreads), 0, stream>>>(a);
+    bool pow2 = true;
+    for (int i = 0; i < num_groups; ++i)
+        pow2 = pow2 && a.g[i].row_shift >= 0;
+    if (pow2)
+        k_step<true><<<dim3((unsigned)blocks), dim3(kStepThreads), 0, stream>>>(a);
+    else
+        k_step<false><<<dim3((unsigned)blocks), dim3(kStepThreads), 0, stream>>>(a);
     return hipGetLastError();
-}
-
-int64_t step_sort_cost(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups)
-{
-    // Every fused workgroup orders the batch itself: a bitonic sort of n_pad
-    // keys costs about n_pad * log2(n_pad)^2 / 2 compare-exchanges.
-    int64_t n_pad = 1, lg = 0;
-    while (n_pad < n) {
-        n_pad <<= 1;
-        ++lg;
-    }
-    return (step_grid_threads(n, T, num_groups, groups) / kStepThreads) * n_pad * lg * lg;
 }
 
 int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups)
@@ -456,7 +510,7 @@ int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_gr
         if (tile > kStepMaxTile)
             tile = kStepMaxTile;
         const int64_t tiles = ((int64_t)T + tile - 1) / tile;
-        blocks += tiles < kTileWorkgroups ? tiles : kTileWorkgroups;
+        blocks += tiles < tile_workgroups(n) ? tiles : tile_workgroups(n);
         if (groups[i].input_block_tables != nullptr)
             blocks += (n + kPageRows - 1) / kPageRows;
     }

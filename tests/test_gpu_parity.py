@@ -199,8 +199,8 @@ def test_fused_batch_sizes(n):
     rng = np.random.default_rng(100 + n)
     R, L, bs = n + 37, 96, 16
     rows = rng.choice(R, n, replace=False).astype(np.int32)
-    # short runs for large batches keep the workgroup count (and so the
-    # one-launch sort budget) small enough that the single launch is taken
+    # n > 64 sorts with every wavefront of the workgroup, n > 512 takes the
+    # separate kernels; short runs keep the large cases quick
     counts = rng.integers(0, 40 if n < 256 else 3, n).astype(np.int32)
     counts[rng.random(n) < 0.4] = 1
     completed = np.zeros(R, np.int32)
