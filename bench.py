@@ -68,6 +68,32 @@ def algorithmic_bytes(batch):
                 total=kv + tok + req + table + pages)
 
 
+def call_bytes(batch):
+    """Algorithmic bytes of each separate call on its own (inputs read once,
+    outputs written once):
+      prepare_batch         12 n (rows, counts, completed) + 4 T (token table)
+                            + 12 n + 4 (index_mapping, seq_lens, query_start_loc)
+                            + 8 T (positions, input_ids)
+      compute_slot_mapping  per group: 4 T (positions) + 4 T (slots) + 8 n + 4 (index
+                            mapping, query_start_loc) + 4 n (seq_lens) + 4 per touched
+                            block + 8 per visible block
+      scatter_kv            per group: T (4 row_bytes + 4)
+    """
+    import numpy as np
+
+    T, n = batch.T, batch.n
+    done = batch.completed[batch.sched_rows].astype(np.int64)
+    cnt = batch.num_scheduled.astype(np.int64)
+    prep = 24 * n + 4 + 12 * T
+    slots = 0
+    for g in batch.groups:
+        bs = g.block_size
+        touched = np.where(cnt > 0, (done + cnt - 1) // bs - done // bs + 1, 0)
+        slots += 8 * T + 12 * n + 4 + 4 * int(touched.sum()) + 8 * int((-(-(done + cnt) // bs)).sum())
+    scat = sum(scatter_bytes_per_launch(batch, gi) for gi in range(len(batch.groups)))
+    return dict(prepare_batch=prep, compute_slot_mapping=slots, scatter_kv=scat)
+
+
 def scatter_bytes_per_launch(batch, gi):
     """Algorithmic bytes of one scatter_kv launch: per token, read K and V rows,
     write both cache rows, read the slot (4 * row_bytes + 4)."""
@@ -232,6 +258,7 @@ def main():
             raise RuntimeError(f"device status bits set: {s.status_bits():#x}")
 
     ab = algorithmic_bytes(batch)
+    cb = call_bytes(batch)
     use_fused = fused_ms <= calls_ms
     ms = fused_ms if use_fused else calls_ms
     if use_fused:
@@ -277,7 +304,14 @@ def main():
         "fused": {"ms_per_step": fused_ms, "tokens_per_s": T / (fused_ms * 1e-3)},
         "three_calls": {
             "ms_per_step": calls_ms, "tokens_per_s": T / (calls_ms * 1e-3),
-            "split_ms_with_events_between_calls": {k: statistics.fmean(v) for k, v in split.items()},
+            "per_call": {
+                k: {"ms": statistics.fmean(v), "algorithmic_bytes": cb[k],
+                    "gbs": cb[k] / (statistics.fmean(v) * 1e-3) / 1e9,
+                    "frac_of_peak": cb[k] / (statistics.fmean(v) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                    "bound": "hbm" if k == "scatter_kv" else "latency"}
+                for k, v in split.items()},
+            "per_call_note": "events between the calls; prepare and slot mapping move under "
+                             "1 MB here, so their time is launch and memory latency",
         },
         "cold_single_step": {
             "ms_median": statistics.median(cold),

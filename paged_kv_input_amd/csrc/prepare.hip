@@ -10,7 +10,9 @@
 // bitonic sort of 64-bit keys (count << 32 | biased row), at most
 // PKV_MAX_BATCH keys), scans the sorted counts with a wave-level scan plus a
 // cross-wave pass, and then expands its own slice of flat tokens by binary
-// search over query_start_loc held in LDS.  Redoing the small sort per
+// search over query_start_loc held in LDS.  Each lane's dependent loads are
+// issued together, so the kernel's time is about three memory round trips
+// (schedule, completed counts, token table) plus the launch.  Redoing the small sort per
 // workgroup costs a few microseconds at most and removes the grid-wide barrier
 // that would otherwise need a second launch or a device-side counter.
 // Workgroup 0 alone writes the per-request outputs and the per-request flags.
@@ -67,10 +69,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
         else if (input_ids != nullptr)
             src[u] = (int64_t)row * token_stride + p;
     }
+    const bool have_ids = input_ids != nullptr && R > 0 && L > 0;
     int32_t id_out[kPrepTokensPerThread];
 #pragma unroll
-    for (int u = 0; u < kPrepTokensPerThread; ++u)
-        id_out[u] = src[u] >= 0 ? token_ids[src[u]] : -1;
+    for (int u = 0; u < kPrepTokensPerThread; ++u) {
+        id_out[u] = have_ids ? token_ids[src[u] >= 0 ? src[u] : 0] : -1;
+        if (src[u] < 0)
+            id_out[u] = -1;
+    }
 #pragma unroll
     for (int u = 0; u < kPrepTokensPerThread; ++u) {
         const int64_t t = t0 + (int64_t)u * kPrepThreads;

@@ -43,10 +43,12 @@ __global__ __launch_bounds__(kSlotThreads) void k_slots(
     if ((int)blockIdx.x < token_blocks) {
         const int64_t t0 = (int64_t)blockIdx.x * kSlotTokensPerBlock + tid;
         int32_t pos[kSlotTokensPerThread];
+        // Unconditional loads from clamped in-bounds addresses throughout: a
+        // load under a divergent branch is issued only after a full wait.
 #pragma unroll
         for (int u = 0; u < kSlotTokensPerThread; ++u) {
             const int64_t t = t0 + u * kSlotThreads;
-            pos[u] = t < T ? positions[t] : -1;
+            pos[u] = positions[t < T ? t : T - 1];
         }
         for (int i = tid; i <= n; i += kSlotThreads)
             s_qsl[i] = query_start_loc[i];
@@ -54,33 +56,52 @@ __global__ __launch_bounds__(kSlotThreads) void k_slots(
             s_row[i] = index_mapping[i];
         __syncthreads();
 
+        int64_t src[kSlotTokensPerThread];
+        int32_t off[kSlotTokensPerThread];
+#pragma unroll
+        for (int u = 0; u < kSlotTokensPerThread; ++u) {
+            const int64_t t = t0 + u * kSlotThreads;
+            src[u] = -1;
+            off[u] = 0;
+            if (t >= T)
+                continue;
+            const int b = owner_of(s_qsl, n, t);
+            if (b < 0 || b >= n)
+                continue;                                   // no request: slot -1
+            const int32_t row = s_row[b];
+            const int32_t p = pos[u];
+            if (row < 0 || row >= R) {
+                flags |= PKV_ST_BAD_ROW;
+            } else if (p < 0) {
+                flags |= PKV_ST_POS_OOR;
+            } else {
+                const int32_t lb = bs_shift >= 0 ? (p >> bs_shift) : p / block_size;
+                off[u] = p - lb * block_size;
+                if (lb >= MB)
+                    flags |= PKV_ST_LB_OOR;
+                else
+                    src[u] = (int64_t)row * MB + lb;
+            }
+        }
+        const bool have_bt = R > 0 && MB > 0;                // uniform
+        int32_t blk[kSlotTokensPerThread];
+#pragma unroll
+        for (int u = 0; u < kSlotTokensPerThread; ++u) {
+            blk[u] = have_bt ? block_table[src[u] >= 0 ? src[u] : 0] : -1;
+            if (src[u] < 0)
+                blk[u] = -1;
+        }
 #pragma unroll
         for (int u = 0; u < kSlotTokensPerThread; ++u) {
             const int64_t t = t0 + u * kSlotThreads;
             if (t >= T)
-                break;
+                continue;
             int32_t slot = -1;
-            const int b = owner_of(s_qsl, n, t);
-            if (b >= 0 && b < n) {
-                const int32_t row = s_row[b];
-                const int32_t p = pos[u];
-                if (row < 0 || row >= R) {
-                    flags |= PKV_ST_BAD_ROW;
-                } else if (p < 0) {
-                    flags |= PKV_ST_POS_OOR;
-                } else {
-                    const int32_t lb = bs_shift >= 0 ? (p >> bs_shift) : p / block_size;
-                    const int32_t off = bs_shift >= 0 ? (p & (block_size - 1)) : p - lb * block_size;
-                    if (lb >= MB) {
-                        flags |= PKV_ST_LB_OOR;
-                    } else {
-                        const int32_t blk = block_table[(int64_t)row * MB + lb];
-                        if (blk < 0 || blk >= num_blocks)
-                            flags |= PKV_ST_BLOCK_OOR;
-                        else
-                            slot = blk * block_size + off;
-                    }
-                }
+            if (src[u] >= 0) {
+                if (blk[u] < 0 || blk[u] >= num_blocks)
+                    flags |= PKV_ST_BLOCK_OOR;
+                else
+                    slot = blk[u] * block_size + off[u];
             }
             slot_mapping[t] = slot;
         }
@@ -106,7 +127,7 @@ __global__ __launch_bounds__(kSlotThreads) void k_slots(
 #pragma unroll
                     for (int u = 0; u < kPageUnroll; ++u) {
                         const int64_t i = i0 + u * kWave + lane;
-                        v[u] = i < visible ? src[i] : 0;
+                        v[u] = src[i < visible ? i : visible - 1];   // clamped, unconditional
                     }
 #pragma unroll
                     for (int u = 0; u < kPageUnroll; ++u) {
