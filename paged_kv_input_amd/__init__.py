@@ -12,7 +12,8 @@ the library and raises if it is missing -- there is no CPU fallback.
 """
 from __future__ import annotations
 
-_API = ("prepare_batch", "compute_slot_mapping", "scatter_kv", "step", "PagedKVError",
+_API = ("prepare_batch", "compute_slot_mapping", "scatter_kv", "step", "prepared_prepare_batch",
+        "prepared_compute_slot_mapping", "prepared_scatter_kv", "prepared_step", "PagedKVError",
         "library_path", "abi_version", "error_string", "load_library", "ST_BITS", "MAX_BATCH",
         "STEP_MAX_BATCH", "STEP_MAX_GROUPS")
 

@@ -3,8 +3,10 @@
 Each function takes torch tensors (device memory), checks dtypes and shapes on
 the host, passes raw pointers and sizes to the C entry point of the same name
 (``pkv_*`` in include/pagedkv.h) on torch's current HIP stream, and raises
-``PagedKVError`` on a non-zero return code.  Nothing here computes any part of
-the path.  The library is loaded at import; a missing library is an ImportError.
+``PagedKVError`` on a non-zero return code.  ``prepared_<name>`` does the checks
+and marshalling once and returns a ``launch(stream=None)`` function for loops
+that repeat a call on the same tensors.  Nothing here computes any part of the
+path.  The library is loaded at import; a missing library is an ImportError.
 """
 from __future__ import annotations
 
@@ -109,17 +111,32 @@ def _idx(name: str, t: Optional[torch.Tensor], shape=None, optional=False):
     return t
 
 
-def _check(fn: str, rc: int):
-    if rc != OK:
-        raise PagedKVError(fn, rc)
+def _prepared(name: str, fn, args: tuple, keep: tuple):
+    """A launcher for one checked, marshalled call: ``launch(stream=None)``.
+    ``keep`` holds the tensors whose pointers are baked into ``args``."""
+
+    def launch(stream=None, _keep=keep):
+        rc = fn(*args, _stream(stream))
+        if rc != OK:
+            raise PagedKVError(name, rc)
+
+    launch.__name__ = f"prepared_{name}"
+    return launch
 
 
-def prepare_batch(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, completed: torch.Tensor,
-                  token_ids: Optional[torch.Tensor], num_tokens: int, *,
-                  index_mapping: torch.Tensor, query_start_loc: torch.Tensor,
-                  seq_lens: torch.Tensor, positions: torch.Tensor,
-                  input_ids: Optional[torch.Tensor] = None,
-                  status: Optional[torch.Tensor] = None, stream=None) -> None:
+def prepare_batch(sched_rows, num_scheduled, completed, token_ids, num_tokens, *, stream=None,
+                  **outputs) -> None:
+    """Batch assembly and flattening (pkv_prepare_batch); see prepared_prepare_batch."""
+    prepared_prepare_batch(sched_rows, num_scheduled, completed, token_ids, num_tokens,
+                           **outputs)(stream)
+
+
+def prepared_prepare_batch(sched_rows: torch.Tensor, num_scheduled: torch.Tensor,
+                           completed: torch.Tensor, token_ids: Optional[torch.Tensor],
+                           num_tokens: int, *, index_mapping: torch.Tensor,
+                           query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
+                           positions: torch.Tensor, input_ids: Optional[torch.Tensor] = None,
+                           status: Optional[torch.Tensor] = None):
     """Batch assembly and flattening into caller-owned output tensors.
 
     sched_rows, num_scheduled: int32 [n]; completed: int32 [R]; token_ids: int32
@@ -149,19 +166,28 @@ def prepare_batch(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, complet
     if status is not None and (status.dtype != torch.int32 or not status.is_cuda
                                or status.numel() < 1):
         raise ValueError("status must be an int32 GPU tensor (bit pattern of a uint32)")
-    rc = _lib.pkv_prepare_batch(n, T, _ptr(sched_rows), _ptr(num_scheduled), _ptr(completed), R,
-                                _ptr(token_ids), stride, L, _ptr(index_mapping),
-                                _ptr(query_start_loc), _ptr(seq_lens), _ptr(positions),
-                                _ptr(input_ids), _ptr(status), _stream(stream))
-    _check("prepare_batch", rc)
+    args = (n, T, _ptr(sched_rows), _ptr(num_scheduled), _ptr(completed), R, _ptr(token_ids),
+            stride, L, _ptr(index_mapping), _ptr(query_start_loc), _ptr(seq_lens),
+            _ptr(positions), _ptr(input_ids), _ptr(status))
+    return _prepared("prepare_batch", _lib.pkv_prepare_batch, args,
+                     (sched_rows, num_scheduled, completed, token_ids, index_mapping,
+                      query_start_loc, seq_lens, positions, input_ids, status))
 
 
-def compute_slot_mapping(index_mapping: torch.Tensor, query_start_loc: torch.Tensor,
-                         seq_lens: Optional[torch.Tensor], positions: torch.Tensor,
-                         block_table: torch.Tensor, block_size: int, num_blocks: int, *,
-                         slot_mapping: torch.Tensor,
-                         input_block_tables: Optional[torch.Tensor] = None,
-                         status: Optional[torch.Tensor] = None, stream=None) -> None:
+def compute_slot_mapping(index_mapping, query_start_loc, seq_lens, positions, block_table,
+                         block_size, num_blocks, *, stream=None, **outputs) -> None:
+    """Write slots and visible pages of ONE KV-cache group (pkv_compute_slot_mapping);
+    see prepared_compute_slot_mapping."""
+    prepared_compute_slot_mapping(index_mapping, query_start_loc, seq_lens, positions,
+                                  block_table, block_size, num_blocks, **outputs)(stream)
+
+
+def prepared_compute_slot_mapping(index_mapping: torch.Tensor, query_start_loc: torch.Tensor,
+                                  seq_lens: Optional[torch.Tensor], positions: torch.Tensor,
+                                  block_table: torch.Tensor, block_size: int, num_blocks: int,
+                                  *, slot_mapping: torch.Tensor,
+                                  input_block_tables: Optional[torch.Tensor] = None,
+                                  status: Optional[torch.Tensor] = None):
     """Write slots (and optionally visible pages) of ONE KV-cache group.
 
     block_table: int32 [R, MB] contiguous; slot_mapping: int32 [T];
@@ -180,16 +206,22 @@ def compute_slot_mapping(index_mapping: torch.Tensor, query_start_loc: torch.Ten
     _idx("input_block_tables", input_block_tables, (n, MB), optional=True)
     if input_block_tables is not None:
         _idx("seq_lens", seq_lens, (n,))
-    rc = _lib.pkv_compute_slot_mapping(n, T, _ptr(index_mapping), _ptr(query_start_loc),
-                                       _ptr(seq_lens), _ptr(positions), _ptr(block_table), R, MB,
-                                       int(block_size), int(num_blocks), _ptr(slot_mapping),
-                                       _ptr(input_block_tables), _ptr(status), _stream(stream))
-    _check("compute_slot_mapping", rc)
+    args = (n, T, _ptr(index_mapping), _ptr(query_start_loc), _ptr(seq_lens), _ptr(positions),
+            _ptr(block_table), R, MB, int(block_size), int(num_blocks), _ptr(slot_mapping),
+            _ptr(input_block_tables), _ptr(status))
+    return _prepared("compute_slot_mapping", _lib.pkv_compute_slot_mapping, args,
+                     (index_mapping, query_start_loc, seq_lens, positions, block_table,
+                      slot_mapping, input_block_tables, status))
 
 
-def scatter_kv(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-               slot_mapping: torch.Tensor, *, status: Optional[torch.Tensor] = None,
-               stream=None) -> None:
+def scatter_kv(k, v, k_cache, v_cache, slot_mapping, *, status=None, stream=None) -> None:
+    """Write K/V rows at their slots (pkv_scatter_kv); see prepared_scatter_kv."""
+    prepared_scatter_kv(k, v, k_cache, v_cache, slot_mapping, status=status)(stream)
+
+
+def prepared_scatter_kv(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, slot_mapping: torch.Tensor, *,
+                        status: Optional[torch.Tensor] = None):
     """Write token t's K/V rows to slot slot_mapping[t] of ONE group's caches.
 
     k, v: [T, ...] GPU tensors whose per-token rows are contiguous (the token
@@ -200,10 +232,10 @@ def scatter_kv(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache:
     T = slot_mapping.shape[0]
     _idx("slot_mapping", slot_mapping, (T,))
     row_bytes, strides = _kv_layout("", k, v, k_cache, v_cache, T)
-    rc = _lib.pkv_scatter_kv(T, row_bytes, _ptr(k), strides[0], _ptr(v), strides[1],
-                             _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _ptr(slot_mapping),
-                             _ptr(status), _stream(stream))
-    _check("scatter_kv", rc)
+    args = (T, row_bytes, _ptr(k), strides[0], _ptr(v), strides[1], _ptr(k_cache), _ptr(v_cache),
+            k_cache.shape[0], _ptr(slot_mapping), _ptr(status))
+    return _prepared("scatter_kv", _lib.pkv_scatter_kv, args,
+                     (k, v, k_cache, v_cache, slot_mapping, status))
 
 
 def _kv_layout(name_k, k, v, k_cache, v_cache, T):
@@ -236,6 +268,23 @@ def step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, completed: torch
     groups: sequence of dicts with keys block_table, block_size, num_blocks,
     slot_mapping, input_block_tables (or None), k, v, k_cache, v_cache.
     """
+    prepared_step(sched_rows, num_scheduled, completed, token_ids, num_tokens, groups,
+                  index_mapping=index_mapping, query_start_loc=query_start_loc,
+                  seq_lens=seq_lens, positions=positions, input_ids=input_ids,
+                  status=status)(stream)
+
+
+def prepared_step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, completed: torch.Tensor,
+                  token_ids: Optional[torch.Tensor], num_tokens: int, groups, *,
+                  index_mapping: torch.Tensor, query_start_loc: torch.Tensor,
+                  seq_lens: torch.Tensor, positions: torch.Tensor,
+                  input_ids: Optional[torch.Tensor] = None,
+                  status: Optional[torch.Tensor] = None):
+    """Check and marshal the arguments of ``step`` once; return a function
+    ``launch(stream=None)`` that enqueues pkv_step with them.  For loops that
+    repeat a step on the same buffers (new contents, same tensors), this keeps
+    the host's per-step cost to one foreign call.  The tensors must stay alive
+    and unmoved while the returned function is used."""
     n = sched_rows.shape[0]
     T = int(num_tokens)
     _idx("sched_rows", sched_rows, (n,))
@@ -271,8 +320,9 @@ def step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, completed: torch
                        g["k_cache"].data_ptr(), g["v_cache"].data_ptr(), ks, vs,
                        g["k_cache"].shape[0], row_bytes, MB, int(g["block_size"]),
                        int(g["num_blocks"]), 0)
-    rc = _lib.pkv_step(n, T, _ptr(sched_rows), _ptr(num_scheduled), _ptr(completed), R,
-                       _ptr(token_ids), stride, L, _ptr(index_mapping), _ptr(query_start_loc),
-                       _ptr(seq_lens), _ptr(positions), _ptr(input_ids), len(groups), arr,
-                       _ptr(status), _stream(stream))
-    _check("step", rc)
+    args = (n, T, _ptr(sched_rows), _ptr(num_scheduled), _ptr(completed), R, _ptr(token_ids),
+            stride, L, _ptr(index_mapping), _ptr(query_start_loc), _ptr(seq_lens),
+            _ptr(positions), _ptr(input_ids), len(groups), arr, _ptr(status))
+    return _prepared("step", _lib.pkv_step, args,
+                     (sched_rows, num_scheduled, completed, token_ids, index_mapping,
+                      query_start_loc, seq_lens, positions, input_ids, status, list(groups), arr))

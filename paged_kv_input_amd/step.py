@@ -58,6 +58,8 @@ class DeviceStep:
         self.input_ids = torch.empty(self.T, **i32) if with_input_ids else None
         self.status = torch.zeros(1, **i32)
         self.groups: List[dict] = []
+        self._fused = None
+        self._prep = None
         for g in groups:
             bt = up(np.asarray(g.block_table, np.int32))
             k = up(np.ascontiguousarray(g.k).view(np.int16))
@@ -83,26 +85,32 @@ class DeviceStep:
                                     v_cache=vc, slot_mapping=torch.empty(self.T, **i32),
                                     input_block_tables=ibt))
 
-    # -- the three calls -------------------------------------------------------
+    # -- the three calls (arguments checked and marshalled once, then reused) -----
     def prepare(self, stream=None):
-        api.prepare_batch(self.sched_rows, self.num_scheduled, self.completed, self.token_ids,
-                          self.T, index_mapping=self.index_mapping,
-                          query_start_loc=self.query_start_loc, seq_lens=self.seq_lens,
-                          positions=self.positions, input_ids=self.input_ids,
-                          status=self.status, stream=stream)
+        if self._prep is None:
+            self._prep = api.prepared_prepare_batch(
+                self.sched_rows, self.num_scheduled, self.completed, self.token_ids, self.T,
+                index_mapping=self.index_mapping, query_start_loc=self.query_start_loc,
+                seq_lens=self.seq_lens, positions=self.positions, input_ids=self.input_ids,
+                status=self.status)
+        self._prep(stream)
 
     def slots(self, gi: int, stream=None):
         g = self.groups[gi]
-        api.compute_slot_mapping(self.index_mapping, self.query_start_loc, self.seq_lens,
-                                 self.positions, g["block_table"], g["block_size"],
-                                 g["num_blocks"], slot_mapping=g["slot_mapping"],
-                                 input_block_tables=g["input_block_tables"], status=self.status,
-                                 stream=stream)
+        if g.get("_slots") is None:
+            g["_slots"] = api.prepared_compute_slot_mapping(
+                self.index_mapping, self.query_start_loc, self.seq_lens, self.positions,
+                g["block_table"], g["block_size"], g["num_blocks"],
+                slot_mapping=g["slot_mapping"], input_block_tables=g["input_block_tables"],
+                status=self.status)
+        g["_slots"](stream)
 
     def scatter(self, gi: int, stream=None):
         g = self.groups[gi]
-        api.scatter_kv(g["k"], g["v"], g["k_cache"], g["v_cache"], g["slot_mapping"],
-                       status=self.status, stream=stream)
+        if g.get("_scatter") is None:
+            g["_scatter"] = api.prepared_scatter_kv(g["k"], g["v"], g["k_cache"], g["v_cache"],
+                                                    g["slot_mapping"], status=self.status)
+        g["_scatter"](stream)
 
     def run(self, stream=None):
         """One whole step: prepare, then every group's slots and scatter."""
@@ -113,15 +121,19 @@ class DeviceStep:
             self.scatter(gi, stream)
 
     def run_fused(self, stream=None):
-        """The same step through the single pkv_step entry point."""
-        api.step(self.sched_rows, self.num_scheduled, self.completed, self.token_ids, self.T,
-                 [dict(block_table=g["block_table"], block_size=g["block_size"],
-                       num_blocks=g["num_blocks"], slot_mapping=g["slot_mapping"],
-                       input_block_tables=g["input_block_tables"], k=g["k"], v=g["v"],
-                       k_cache=g["k_cache"], v_cache=g["v_cache"]) for g in self.groups],
-                 index_mapping=self.index_mapping, query_start_loc=self.query_start_loc,
-                 seq_lens=self.seq_lens, positions=self.positions, input_ids=self.input_ids,
-                 status=self.status, stream=stream)
+        """The same step through the single pkv_step entry point (arguments
+        checked and marshalled on the first call, then reused)."""
+        if self._fused is None:
+            self._fused = api.prepared_step(
+                self.sched_rows, self.num_scheduled, self.completed, self.token_ids, self.T,
+                [dict(block_table=g["block_table"], block_size=g["block_size"],
+                      num_blocks=g["num_blocks"], slot_mapping=g["slot_mapping"],
+                      input_block_tables=g["input_block_tables"], k=g["k"], v=g["v"],
+                      k_cache=g["k_cache"], v_cache=g["v_cache"]) for g in self.groups],
+                index_mapping=self.index_mapping, query_start_loc=self.query_start_loc,
+                seq_lens=self.seq_lens, positions=self.positions, input_ids=self.input_ids,
+                status=self.status)
+        self._fused(stream)
 
     def status_bits(self) -> int:
         return int(self.status.item()) & 0xFFFFFFFF
