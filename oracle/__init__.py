@@ -31,7 +31,7 @@ _lib = None
 OK = 0
 EINVAL = -1
 ST_BAD_ROW, ST_BAD_COUNT, ST_TOKEN_SUM, ST_POS_OOR = 0x01, 0x02, 0x04, 0x08
-ST_LB_OOR, ST_BLOCK_OOR, ST_SLOT_OOR = 0x10, 0x20, 0x40
+ST_LB_OOR, ST_BLOCK_OOR, ST_SLOT_OOR, ST_BAD_RANGE = 0x10, 0x20, 0x40, 0x80
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -56,6 +56,13 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
                                              _I32, _I32, _P, _P, _P]
     lib.orc_scatter_kv.restype = ctypes.c_int
     lib.orc_scatter_kv.argtypes = [_I32, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _P]
+    lib.orc_add_requests.restype = ctypes.c_int
+    lib.orc_add_requests.argtypes = [_I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P,
+                                     _I64, _I32, _P, _I32, _P, _P]
+    lib.orc_append_blocks.restype = ctypes.c_int
+    lib.orc_append_blocks.argtypes = [_I32, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P]
+    lib.orc_advance_state.restype = ctypes.c_int
+    lib.orc_advance_state.argtypes = [_I32, _P, _P, _P, _I32, _P, _P, _I64, _I32, _P]
     return lib
 
 
@@ -179,3 +186,70 @@ def run_chain(batch, *, caches=None, sentinel=0xFFFF, lib=None):
         sm["k_cache"], sm["v_cache"] = kc, vc
         groups.append(sm)
     return prep, groups
+
+
+# ---------------------------------------------------------------------------
+# persistent request state (updated in place)
+# ---------------------------------------------------------------------------
+
+def csr(lists):
+    """[list, ...] -> (start[m+1], flat, total) with int32 arrays (flat holds at
+    least one element so that its pointer is valid)."""
+    start = np.zeros(len(lists) + 1, np.int32)
+    start[1:] = np.cumsum([len(x) for x in lists]) if lists else []
+    total = int(start[-1])
+    flat = np.array([v for x in lists for v in x], np.int32) if total else np.zeros(1, np.int32)
+    return start, flat, total
+
+
+def add_requests(state, rows, num_computed, prompts, blocks, *, lib=None):
+    """add_request for each new request, on a state dict with int32 arrays
+    completed[R], token_ids[R, L], block_table[R, MB], row_blocks[R] (in place).
+    prompts / blocks: one list per request, or (start, flat, total) CSR triples
+    (which may hold bad ranges).  Returns (rc, status)."""
+    lib = lib or load()
+    rows, nc = _i32(rows), _i32(num_computed)
+    ps, pt, ptot = prompts if isinstance(prompts, tuple) else csr(prompts)
+    bs_, bl, btot = blocks if isinstance(blocks, tuple) else csr(blocks)
+    tok, bt = state["token_ids"], state["block_table"]
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_add_requests(rows.size, _ptr(rows), _ptr(nc), _ptr(_i32(ps)), _ptr(_i32(pt)),
+                              ptot, _ptr(_i32(bs_)), _ptr(_i32(bl)), btot,
+                              state["completed"].size, _ptr(state["completed"]),
+                              _ptr(tok), tok.strides[0] // 4, tok.shape[1], _ptr(bt), bt.shape[1],
+                              _ptr(state["row_blocks"]), _ptr(st))
+    return int(rc), int(st[0])
+
+
+def append_blocks(state, rows, blocks, *, lib=None):
+    """update_request: append each request's newly allocated blocks (in place)."""
+    lib = lib or load()
+    rows = _i32(rows)
+    bs_, bl, btot = blocks if isinstance(blocks, tuple) else csr(blocks)
+    bt = state["block_table"]
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_append_blocks(rows.size, _ptr(rows), _ptr(_i32(bs_)), _ptr(_i32(bl)), btot,
+                               bt.shape[0], _ptr(bt), bt.shape[1], _ptr(state["row_blocks"]),
+                               _ptr(st))
+    return int(rc), int(st[0])
+
+
+def advance_state(state, index_mapping, seq_lens, sampled=None, *, lib=None):
+    """After a step: completed[row] = seq_len, sampled tokens appended (in place)."""
+    lib = lib or load()
+    im, sl = _i32(index_mapping), _i32(seq_lens)
+    sm = None if sampled is None else _i32(sampled)
+    tok = state["token_ids"]
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_advance_state(im.size, _ptr(im), _ptr(sl), _ptr(sm), state["completed"].size,
+                               _ptr(state["completed"]), _ptr(tok), tok.strides[0] // 4,
+                               tok.shape[1], _ptr(st))
+    return int(rc), int(st[0])
+
+
+def empty_state(R, L, MB, token_fill=-1):
+    """A fresh state: nothing computed, no tokens, no blocks."""
+    return {"completed": np.zeros(R, np.int32),
+            "token_ids": np.full((R, L), token_fill, np.int32),
+            "block_table": np.full((R, MB), -1, np.int32),
+            "row_blocks": np.zeros(R, np.int32)}

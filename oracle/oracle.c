@@ -33,6 +33,10 @@
  *                               block size 1, invariants.
  *   orc_scatter_kv           -- NumPy fancy-index assignment, gather round trip,
  *                               sentinel count.
+ *   orc_add_requests,        -- the [KC] worked example's state rebuilt from
+ *   orc_append_blocks,          nothing, the [CF] prefix example's [P1][P2][B3]
+ *   orc_advance_state           table (reuse, then one appended block), brute-
+ *                               force state loops, a multi-step decode loop.
  * Readings of points the pages leave open are listed at each step (R1..R9).
  */
 #include <stdint.h>
@@ -51,6 +55,7 @@
 #define ORC_ST_LB_OOR     0x10u  /* logic_block >= block-table width              */
 #define ORC_ST_BLOCK_OOR  0x20u  /* physical_block_id < 0 or >= pool size         */
 #define ORC_ST_SLOT_OOR   0x40u  /* slot_id >= cache slots                        */
+#define ORC_ST_BAD_RANGE  0x80u  /* CSR offsets decreasing or outside the array   */
 
 /* One scheduled request while the batch is being assembled. */
 typedef struct {
@@ -358,6 +363,165 @@ int orc_scatter_kv(int32_t T, int64_t row_bytes,
                (size_t)row_bytes);
     }
 
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * Persistent request state ([KC] "Persistent Request Context Strategy" and
+ * "Design Logic Behind the Dual-Index System"): per request_state_index, the
+ * tokens already processed (completed), the request's token list (token_ids
+ * row) and its block table row.  R10: the state also keeps row_blocks[r], the
+ * number of logical blocks allocated to row r, so that new block ids can be
+ * appended after the existing ones.  Choosing and recycling rows (the free
+ * list) stays with the caller, as the scheduler's bookkeeping.
+ */
+
+/*
+ * add_request for m new requests: row rows[i] gets completed = num_computed[i]
+ * (tokens already covered, e.g. by reused prefix blocks), its prompt tokens
+ * prompt_tokens[prompt_start[i] .. prompt_start[i+1]) at positions 0.., and its
+ * block table blocks[block_start[i] .. block_start[i+1]) at logical blocks 0..,
+ * the rest of the row set to -1 (a recycled row keeps nothing of its previous
+ * request); row_blocks = the number of blocks given.
+ * R11 (data errors): a row outside [0, R) is flagged BAD_ROW and skipped; a
+ * request whose token or block range is not inside its flat array
+ * (start < 0, end < start, end > the array's length) is flagged BAD_RANGE and
+ * skipped; prompt tokens at positions >= L are flagged POS_OOR and dropped;
+ * block ids past MB are flagged LB_OOR and dropped (row_blocks is cut to MB);
+ * token-table entries past the prompt are left as they are.
+ */
+static int bad_range(const int32_t* start, int32_t i, int32_t total)
+{
+    return start[i] < 0 || start[i + 1] < start[i] || start[i + 1] > total;
+}
+
+int orc_add_requests(int32_t m, const int32_t* rows, const int32_t* num_computed,
+                     const int32_t* prompt_start, const int32_t* prompt_tokens,
+                     int32_t num_prompt_tokens, const int32_t* block_start,
+                     const int32_t* blocks, int32_t num_blocks_given, int32_t R,
+                     int32_t* completed, int32_t* token_ids, int64_t token_stride, int32_t L,
+                     int32_t* block_table, int32_t MB, int32_t* row_blocks, uint32_t* status)
+{
+    if (m < 0 || R < 0 || L < 0 || MB < 0 || token_stride < L || num_prompt_tokens < 0 ||
+        num_blocks_given < 0)
+        return ORC_EINVAL;
+    if (m > 0 && (rows == NULL || num_computed == NULL || prompt_start == NULL ||
+                  block_start == NULL))
+        return ORC_EINVAL;
+    uint32_t st = 0;
+    for (int32_t i = 0; i < m; ++i) {
+        int32_t r = rows[i];
+        if (r < 0 || r >= R) {
+            st |= ORC_ST_BAD_ROW;
+            continue;
+        }
+        if (bad_range(prompt_start, i, num_prompt_tokens) ||
+            bad_range(block_start, i, num_blocks_given)) {
+            st |= ORC_ST_BAD_RANGE;
+            continue;
+        }
+        completed[r] = num_computed[i];
+        for (int64_t j = 0; j < (int64_t)prompt_start[i + 1] - prompt_start[i]; ++j) {
+            if (j >= L) {
+                st |= ORC_ST_POS_OOR;
+                break;
+            }
+            token_ids[(int64_t)r * token_stride + j] = prompt_tokens[prompt_start[i] + j];
+        }
+        int64_t given = (int64_t)block_start[i + 1] - block_start[i];
+        if (given > MB) {
+            st |= ORC_ST_LB_OOR;
+            given = MB;
+        }
+        for (int64_t j = 0; j < MB; ++j)
+            block_table[(int64_t)r * MB + j] = j < given ? blocks[block_start[i] + j] : -1;
+        row_blocks[r] = (int32_t)given;
+    }
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * update_request for m requests already registered: the newly allocated block
+ * ids blocks[block_start[i] .. block_start[i+1]) are appended to row rows[i]'s
+ * block table after its row_blocks[r] existing entries; row_blocks grows by as
+ * many.  R11: a bad row is flagged and skipped, a bad block range likewise
+ * (BAD_RANGE); entries that would land at or past MB (or a row_blocks outside
+ * [0, MB]) are flagged LB_OOR and dropped.  Rows must be distinct in one call.
+ */
+int orc_append_blocks(int32_t m, const int32_t* rows, const int32_t* block_start,
+                      const int32_t* blocks, int32_t num_blocks_given, int32_t R,
+                      int32_t* block_table, int32_t MB, int32_t* row_blocks, uint32_t* status)
+{
+    if (m < 0 || R < 0 || MB < 0 || num_blocks_given < 0)
+        return ORC_EINVAL;
+    if (m > 0 && (rows == NULL || block_start == NULL))
+        return ORC_EINVAL;
+    uint32_t st = 0;
+    for (int32_t i = 0; i < m; ++i) {
+        int32_t r = rows[i];
+        if (r < 0 || r >= R) {
+            st |= ORC_ST_BAD_ROW;
+            continue;
+        }
+        if (bad_range(block_start, i, num_blocks_given)) {
+            st |= ORC_ST_BAD_RANGE;
+            continue;
+        }
+        int64_t have = row_blocks[r];
+        for (int64_t j = 0; j < (int64_t)block_start[i + 1] - block_start[i]; ++j) {
+            if (have >= MB || have < 0) {
+                st |= ORC_ST_LB_OOR;
+                break;
+            }
+            block_table[(int64_t)r * MB + have] = blocks[block_start[i] + j];
+            ++have;
+        }
+        row_blocks[r] = (int32_t)have;
+    }
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * After a step: each scheduled request's tokens are now computed, so
+ * completed[row] becomes its seq_len (history plus this step's tokens; [CF]
+ * "为什么还有 num_in_flight_tokens": the computed count advances by the tokens
+ * scheduled), and a request that produced a new token (sampled[b] >= 0; NULL:
+ * none did) gets it appended to its token list at position seq_len, the next
+ * position to compute.  R11: a bad row is flagged and skipped; a token at a
+ * position outside [0, L) is flagged POS_OOR and dropped; sampled[b] < 0 means
+ * no token (a prefill chunk that is not the prompt's last).
+ */
+int orc_advance_state(int32_t n, const int32_t* index_mapping, const int32_t* seq_lens,
+                      const int32_t* sampled, int32_t R, int32_t* completed, int32_t* token_ids,
+                      int64_t token_stride, int32_t L, uint32_t* status)
+{
+    if (n < 0 || R < 0 || L < 0 || token_stride < L)
+        return ORC_EINVAL;
+    if (n > 0 && (index_mapping == NULL || seq_lens == NULL))
+        return ORC_EINVAL;
+    uint32_t st = 0;
+    for (int32_t b = 0; b < n; ++b) {
+        int32_t r = index_mapping[b];
+        if (r < 0 || r >= R) {
+            st |= ORC_ST_BAD_ROW;
+            continue;
+        }
+        completed[r] = seq_lens[b];
+        if (sampled != NULL && sampled[b] >= 0) {
+            int32_t p = seq_lens[b];
+            if (p < 0 || p >= L) {
+                st |= ORC_ST_POS_OOR;
+                continue;
+            }
+            token_ids[(int64_t)r * token_stride + p] = sampled[b];
+        }
+    }
     if (status != NULL)
         *status |= st;
     return ORC_OK;

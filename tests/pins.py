@@ -305,3 +305,207 @@ def pin_strided_kv(lib):
 ALL_PINS = [pin_pages_example, pin_prefix_example, pin_budget_tie_example, pin_bruteforce,
             pin_library_routines, pin_closed_forms, pin_invariants, pin_error_semantics,
             pin_strided_kv]
+
+
+# ---------------------------------------------------------------------------
+# persistent request state: add_request, update_request, the after-step advance
+# ---------------------------------------------------------------------------
+
+def pin_state_pages_example(lib):
+    """Rebuild the kongchang.com example's state from nothing with add_request
+    (rows 7 and 6, 31 and 16 tokens done, blocks [37, 12] and [81, 44]); the
+    chain on it then gives the printed values."""
+    g = _golden("pages_example.json")
+    ref = workloads.pages_example()
+    R, L, MB = ref.R, ref.L, ref.groups[0].max_blocks
+    st = oracle.empty_state(R, L, MB)
+    rows = [7, 6]
+    prompts = [ref.token_ids[7, :32].tolist(), ref.token_ids[6, :24].tolist()]
+    rc, status = oracle.add_requests(st, rows, [31, 16], prompts, [[37, 12], [81, 44]], lib=lib)
+    assert rc == 0 and status == 0
+    _eq(st["completed"], ref.completed, "completed")
+    _eq(st["block_table"], ref.groups[0].block_table, "block_table")
+    _eq(st["row_blocks"][[7, 6]], [2, 2], "row_blocks")
+    _eq(st["token_ids"][7, :32], ref.token_ids[7, :32], "tokens of B")
+    _eq(st["token_ids"][6, :24], ref.token_ids[6, :24], "tokens of A")
+    prep = oracle.prepare_batch(ref.sched_rows, ref.num_scheduled, st["completed"],
+                                st["token_ids"], lib=lib)
+    sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                     prep["seq_lens"], prep["positions"], st["block_table"], 16,
+                                     ref.groups[0].num_blocks, lib=lib)
+    _eq(prep["query_start_loc"], g["printed"]["query_start_loc"], "query_start_loc")
+    _eq(sm["slot_mapping"], g["derived"]["slot_mapping"], "slot_mapping")
+    # after the step both requests have computed their scheduled tokens
+    rc, status = oracle.advance_state(st, prep["index_mapping"], prep["seq_lens"], lib=lib)
+    _eq(st["completed"][[7, 6]], g["derived"]["seq_lens"], "completed after the step")
+
+
+def pin_state_prefix_example(lib):
+    """The caffein.top example: B reuses cached P1, P2 (8 tokens computed),
+    then B3 is newly allocated and appended: the table reads [P1][P2][B3]."""
+    g = _golden("prefix_reuse_example.json")
+    inst = g["inputs"]["instantiate"]
+    st = oracle.empty_state(4, 12, 3)
+    prompt = (np.arange(10) + 12).tolist()                # identity code of row 1
+    rc, status = oracle.add_requests(st, [1], [8], [prompt], [[inst["P1"], inst["P2"]]], lib=lib)
+    assert rc == 0 and status == 0
+    _eq(st["block_table"][1], [inst["P1"], inst["P2"], -1], "after reuse")
+    _eq(st["row_blocks"][1], 2, "row_blocks after reuse")
+    rc, status = oracle.append_blocks(st, [1], [[inst["B3"]]], lib=lib)
+    assert rc == 0 and status == 0
+    _eq(st["block_table"][1], [inst["P1"], inst["P2"], inst["B3"]], "[P1][P2][B3]")
+    _eq(st["row_blocks"][1], 3, "row_blocks after append")
+    prep = oracle.prepare_batch([1], [2], st["completed"], st["token_ids"], lib=lib)
+    sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                     prep["seq_lens"], prep["positions"], st["block_table"], 4, 16,
+                                     lib=lib)
+    e = g["expected"]
+    _eq(prep["positions"], e["positions"], "positions")
+    _eq(sm["slot_mapping"], [4 * inst["B3"], 4 * inst["B3"] + 1], "slots")
+
+
+class StateModel:
+    """Pure-Python model of the state: per row a token list, a block list and a
+    computed count (lists instead of arrays, no -1 padding)."""
+
+    def __init__(self, R, L, MB):
+        self.R, self.L, self.MB = R, L, MB
+        self.tokens = {r: {} for r in range(R)}
+        self.blocks = {r: [] for r in range(R)}
+        self.done = {r: 0 for r in range(R)}
+
+    def add(self, r, done, prompt, blocks):
+        self.done[r] = done
+        for p, t in enumerate(prompt[:self.L]):
+            self.tokens[r][p] = t
+        self.blocks[r] = list(blocks[:self.MB])
+
+    def append(self, r, blocks):
+        self.blocks[r] = (self.blocks[r] + list(blocks))[:self.MB]
+
+    def advance(self, r, seq_len, sampled):
+        self.done[r] = seq_len
+        if sampled is not None and sampled >= 0 and 0 <= seq_len < self.L:
+            self.tokens[r][seq_len] = sampled
+
+    def check(self, st, token_fill=-1):
+        for r in range(self.R):
+            assert st["completed"][r] == self.done[r], (r, "completed")
+            row = [-1] * self.MB
+            row[:len(self.blocks[r])] = self.blocks[r]
+            assert st["block_table"][r].tolist() == row, (r, "block_table")
+            assert st["row_blocks"][r] == len(self.blocks[r]), (r, "row_blocks")
+            want = [self.tokens[r].get(p, token_fill) for p in range(self.L)]
+            assert st["token_ids"][r].tolist() == want, (r, "token_ids")
+
+
+def pin_state_bruteforce(lib, seeds=range(60)):
+    """Random sequences of add / append / advance against the Python model."""
+    for seed in seeds:
+        rng = np.random.default_rng(500 + seed)
+        R, L, MB = 6, 12, 4
+        st = oracle.empty_state(R, L, MB)
+        model = StateModel(R, L, MB)
+        for _ in range(8):
+            op = rng.integers(3)
+            rows = rng.choice(R, int(rng.integers(1, 4)), replace=False).tolist()
+            if op == 0:
+                done = rng.integers(0, 8, len(rows)).tolist()
+                prompts = [rng.integers(0, 1000, int(rng.integers(0, 14))).tolist() for _ in rows]
+                blocks = [rng.integers(0, 50, int(rng.integers(0, 6))).tolist() for _ in rows]
+                oracle.add_requests(st, rows, done, prompts, blocks, lib=lib)
+                for r, d, p, b in zip(rows, done, prompts, blocks):
+                    model.add(r, d, p, b)
+            elif op == 1:
+                blocks = [rng.integers(0, 50, int(rng.integers(0, 3))).tolist() for _ in rows]
+                oracle.append_blocks(st, rows, blocks, lib=lib)
+                for r, b in zip(rows, blocks):
+                    model.append(r, b)
+            else:
+                seq = rng.integers(0, 14, len(rows)).tolist()
+                sampled = rng.integers(-1, 1000, len(rows)).tolist()
+                oracle.advance_state(st, rows, seq, sampled, lib=lib)
+                for r, q, s in zip(rows, seq, sampled):
+                    model.advance(r, q, s)
+            model.check(st)
+
+
+def pin_state_multistep(lib, steps=24):
+    """A decode loop closed on the state: each step appends a block to rows
+    whose next token starts a new one, runs the chain, and advances the state
+    with a sampled token; positions then walk on by one per step."""
+    rng = np.random.default_rng(77)
+    R, L, MB, bs, NB = 10, 64, 16, 4, 200
+    st = oracle.empty_state(R, L, MB)
+    model = StateModel(R, L, MB)
+    pool = rng.permutation(NB).tolist()
+    rows = rng.choice(R, 6, replace=False).tolist()
+    prompts = [rng.integers(0, 1000, int(rng.integers(1, 9))).tolist() for _ in rows]
+    blocks = [[pool.pop() for _ in range(-(-len(p) // bs))] for p in prompts]
+    oracle.add_requests(st, rows, [0] * len(rows), prompts, blocks, lib=lib)
+    for r, p, b in zip(rows, prompts, blocks):
+        model.add(r, 0, p, b)
+    counts = [len(p) for p in prompts]                    # first step: the whole prompt
+    seen = set()
+    for step in range(steps):
+        need = []
+        for r, c in zip(rows, counts):
+            have = int(st["row_blocks"][r])
+            want = -(-(int(st["completed"][r]) + c) // bs)
+            need.append([pool.pop() for _ in range(max(0, want - have))])
+        oracle.append_blocks(st, rows, need, lib=lib)
+        for r, b in zip(rows, need):
+            model.append(r, b)
+        prep = oracle.prepare_batch(rows, counts, st["completed"], st["token_ids"], lib=lib)
+        assert prep["status"] == 0
+        sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                         prep["seq_lens"], prep["positions"], st["block_table"],
+                                         bs, NB, lib=lib)
+        assert sm["status"] == 0 and (sm["slot_mapping"] >= 0).all()
+        for s in sm["slot_mapping"].tolist():
+            assert s not in seen, "a slot is written twice across steps"
+            seen.add(s)
+        # every scheduled position holds a known token (prompt or sampled)
+        for b_, r in enumerate(prep["index_mapping"].tolist()):
+            for t in range(prep["query_start_loc"][b_], prep["query_start_loc"][b_ + 1]):
+                assert prep["input_ids"][t] == model.tokens[r][prep["positions"][t]]
+        sampled = rng.integers(0, 1000, len(rows)).tolist()
+        oracle.advance_state(st, prep["index_mapping"], prep["seq_lens"], sampled, lib=lib)
+        for r, q, s_ in zip(prep["index_mapping"].tolist(), prep["seq_lens"].tolist(), sampled):
+            model.advance(r, q, s_)
+        model.check(st)
+        counts = [1] * len(rows)
+
+
+def pin_state_errors(lib):
+    st = oracle.empty_state(3, 4, 2)
+    rc, status = oracle.add_requests(st, [5, 1], [0, 2], [[1], [9, 8, 7, 6, 5, 4]],
+                                     [[1], [3, 4, 5]], lib=lib)
+    assert rc == 0 and status == (oracle.ST_BAD_ROW | oracle.ST_POS_OOR | oracle.ST_LB_OOR), status
+    _eq(st["token_ids"][1], [9, 8, 7, 6], "prompt cut at L")
+    _eq(st["block_table"][1], [3, 4], "blocks cut at MB")
+    _eq(st["row_blocks"][1], 2, "row_blocks cut at MB")
+    rc, status = oracle.append_blocks(st, [1, -1], [[7], [8]], lib=lib)
+    assert status == (oracle.ST_LB_OOR | oracle.ST_BAD_ROW), status
+    _eq(st["block_table"][1], [3, 4], "full row unchanged")
+    # CSR ranges outside the flat array: the request is skipped and flagged
+    st2 = oracle.empty_state(3, 4, 2)
+    rc, status = oracle.add_requests(
+        st2, [0, 1], [1, 1], (np.array([0, 3, 9], np.int32), np.array([4, 5, 6, 7], np.int32), 4),
+        (np.array([0, 1, 2], np.int32), np.array([8, 9], np.int32), 2), lib=lib)
+    assert rc == 0 and status == oracle.ST_BAD_RANGE, status
+    _eq(st2["completed"], [1, 0, 0], "second request skipped")
+    _eq(st2["token_ids"][0, :3], [4, 5, 6], "first request's prompt")
+    rc, status = oracle.append_blocks(st2, [0, 2], (np.array([0, 1, 0], np.int32),
+                                                    np.array([7], np.int32), 1), lib=lib)
+    assert status == oracle.ST_BAD_RANGE, status
+    _eq(st2["block_table"][0], [8, 7], "first append kept")
+    rc, status = oracle.advance_state(st, [1, 2, 7], [4, 1, 0], [5, -1, 3], lib=lib)
+    assert status == (oracle.ST_POS_OOR | oracle.ST_BAD_ROW), status
+    _eq(st["completed"], [0, 4, 1], "completed")
+    _eq(st["token_ids"][2], [-1, -1, -1, -1], "no token for sampled -1")
+
+
+STATE_PINS = [pin_state_pages_example, pin_state_prefix_example, pin_state_bruteforce,
+              pin_state_multistep, pin_state_errors]
+ALL_PINS += STATE_PINS

@@ -71,6 +71,24 @@ MUTANTS = {
     "scatter_ignores_stride": (
         "memcpy(kdst + slot_id * row_bytes, ksrc + (int64_t)flat_token_index * k_stride,",
         "memcpy(kdst + slot_id * row_bytes, ksrc + (int64_t)flat_token_index * row_bytes,"),
+    "add_keeps_old_blocks": (
+        "block_table[(int64_t)r * MB + j] = j < given ? blocks[block_start[i] + j] : -1;",
+        "if (j < given) block_table[(int64_t)r * MB + j] = blocks[block_start[i] + j];"),
+    "add_ignores_computed": (
+        "        completed[r] = num_computed[i];\n",
+        "        completed[r] = 0;\n"),
+    "append_overwrites_last": (
+        "            block_table[(int64_t)r * MB + have] = blocks[block_start[i] + j];",
+        "            block_table[(int64_t)r * MB + (have > 0 ? have - 1 : 0)] = blocks[block_start[i] + j];"),
+    "append_forgets_count": (
+        "        row_blocks[r] = (int32_t)have;",
+        "        (void)have;"),
+    "advance_adds_instead_of_sets": (
+        "        completed[r] = seq_lens[b];",
+        "        completed[r] += seq_lens[b];"),
+    "advance_token_one_early": (
+        "            int32_t p = seq_lens[b];",
+        "            int32_t p = seq_lens[b] - 1;"),
     "bad_row_not_flagged": (
         "            st |= ORC_ST_BAD_ROW;\n            seq_lens[b] = -1;",
         "            seq_lens[b] = -1;"),
