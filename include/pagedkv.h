@@ -59,6 +59,7 @@ extern "C" {
 #define PKV_ST_LB_OOR     0x10u /* logical block >= block-table width MB               */
 #define PKV_ST_BLOCK_OOR  0x20u /* physical block id < 0 or >= num_blocks              */
 #define PKV_ST_SLOT_OOR   0x40u /* slot id >= num_slots of the cache                   */
+#define PKV_ST_BAD_RANGE  0x80u /* CSR offsets decreasing or outside their array       */
 
 /* Largest batch (scheduled requests per step) one call accepts: the batch is
  * ordered inside one workgroup's LDS. */
@@ -213,6 +214,58 @@ int pkv_step(int32_t n, int32_t T,
              int32_t* positions, int32_t* input_ids,
              int32_t num_groups, const pkv_group* groups,
              uint32_t* status, void* stream);
+
+/*
+ * Persistent request state ("Persistent Request Context Strategy" and "Design
+ * Logic Behind the Dual-Index System" of the article above).  Per state row
+ * (request_state_index) the caller keeps, in device memory:
+ *   completed[R]            tokens already processed
+ *   token_ids[R * token_stride]  the request's token list, positions < L
+ *   block_table[R * MB]     logical block -> physical block, -1 = none
+ *   row_blocks[R]           logical blocks allocated to the row (entries
+ *                           0 .. row_blocks-1 of its block-table row)
+ * Choosing and recycling rows is the caller's (scheduler-side) bookkeeping.
+ * Ragged per-request lists come as CSR: list i is flat[start[i] .. start[i+1]),
+ * start has m+1 entries and the flat array `total` entries.  Rows must be
+ * distinct within one call.  Data errors (flagged in *status, never an
+ * out-of-bounds access): a row outside [0, R) is skipped (BAD_ROW); a range
+ * with start[i] < 0, start[i+1] < start[i] or start[i+1] > total skips its
+ * request (BAD_RANGE); tokens at positions >= L are dropped (POS_OOR); block
+ * ids past MB are dropped (LB_OOR).
+ */
+
+/* add_request: row rows[i] gets completed = num_computed[i], its prompt
+ * tokens at positions 0.. (entries past the prompt are left as they are), its
+ * blocks at logical blocks 0.. with the rest of the row set to -1, and
+ * row_blocks = the number of blocks given.  Host errors: EINVAL for negative
+ * sizes, token_stride < L, or a NULL pointer with m > 0. */
+int pkv_add_requests(int32_t m, const int32_t* rows, const int32_t* num_computed,
+                     const int32_t* prompt_start, const int32_t* prompt_tokens,
+                     int32_t num_prompt_tokens, const int32_t* block_start,
+                     const int32_t* blocks, int32_t num_blocks_given, int32_t R,
+                     int32_t* completed, int32_t* token_ids, int64_t token_stride, int32_t L,
+                     int32_t* block_table, int32_t MB, int32_t* row_blocks,
+                     uint32_t* status, void* stream);
+
+/* update_request: the new block ids of request i are appended to row
+ * rows[i]'s block table after its row_blocks existing entries, and row_blocks
+ * grows by as many.  Host errors: EINVAL for negative sizes or a NULL pointer
+ * with m > 0. */
+int pkv_append_blocks(int32_t m, const int32_t* rows, const int32_t* block_start,
+                      const int32_t* blocks, int32_t num_blocks_given, int32_t R,
+                      int32_t* block_table, int32_t MB, int32_t* row_blocks,
+                      uint32_t* status, void* stream);
+
+/* After a step (index_mapping and seq_lens as produced by pkv_prepare_batch):
+ * completed[index_mapping[b]] = seq_lens[b], and when sampled is not NULL and
+ * sampled[b] >= 0 that token is written at position seq_lens[b] of the row's
+ * token list (sampled[b] < 0: no new token, e.g. a prompt chunk that is not
+ * the last).  Host errors: EINVAL for negative sizes, token_stride < L, or a
+ * NULL pointer with n > 0. */
+int pkv_advance_state(int32_t n, const int32_t* index_mapping, const int32_t* seq_lens,
+                      const int32_t* sampled, int32_t R, int32_t* completed,
+                      int32_t* token_ids, int64_t token_stride, int32_t L,
+                      uint32_t* status, void* stream);
 
 /* Static text for a return code (never NULL). */
 const char* pkv_error_string(int code);

@@ -22,7 +22,7 @@ library_path = os.environ.get("PAGEDKV_LIB", os.path.join(_HERE, "libpagedkv.so"
 OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
 ST_BITS = {
     "BAD_ROW": 0x01, "BAD_COUNT": 0x02, "TOKEN_SUM": 0x04, "POS_OOR": 0x08,
-    "LB_OOR": 0x10, "BLOCK_OOR": 0x20, "SLOT_OOR": 0x40,
+    "LB_OOR": 0x10, "BLOCK_OOR": 0x20, "SLOT_OOR": 0x40, "BAD_RANGE": 0x80,
 }
 MAX_BATCH = 4096
 
@@ -71,6 +71,13 @@ def load_library(path: str = library_path) -> ctypes.CDLL:
     lib.pkv_step.restype = ctypes.c_int
     lib.pkv_step.argtypes = [_I32, _I32, _P, _P, _P, _I32, _P, _I64, _I32, _P, _P, _P, _P, _P,
                              _I32, ctypes.POINTER(Group), _P, _P]
+    lib.pkv_add_requests.restype = ctypes.c_int
+    lib.pkv_add_requests.argtypes = [_I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P,
+                                     _I64, _I32, _P, _I32, _P, _P, _P]
+    lib.pkv_append_blocks.restype = ctypes.c_int
+    lib.pkv_append_blocks.argtypes = [_I32, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _P]
+    lib.pkv_advance_state.restype = ctypes.c_int
+    lib.pkv_advance_state.argtypes = [_I32, _P, _P, _P, _I32, _P, _P, _I64, _I32, _P, _P]
     lib.pkv_error_string.restype = ctypes.c_char_p
     lib.pkv_error_string.argtypes = [ctypes.c_int]
     lib.pkv_abi_version.restype = ctypes.c_int
@@ -326,3 +333,119 @@ def prepared_step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, complet
     return _prepared("step", _lib.pkv_step, args,
                      (sched_rows, num_scheduled, completed, token_ids, index_mapping,
                       query_start_loc, seq_lens, positions, input_ids, status, list(groups), arr))
+
+
+# -- persistent request state -------------------------------------------------
+def _token_table(token_ids: torch.Tensor, R: int):
+    if token_ids.dtype != torch.int32 or not token_ids.is_cuda or token_ids.dim() != 2 \
+            or token_ids.stride(1) != 1 or token_ids.shape[0] != R:
+        raise ValueError("token_ids must be an int32 [R, L] GPU tensor with unit column stride")
+    return token_ids.shape[1], token_ids.stride(0)
+
+
+def _block_table(block_table: torch.Tensor, R: int):
+    _idx("block_table", block_table)
+    if block_table.dim() != 2 or block_table.shape[0] != R:
+        raise ValueError("block_table must be [R, MB]")
+    return block_table.shape[1]
+
+
+def _status(status):
+    if status is not None and (status.dtype != torch.int32 or not status.is_cuda
+                               or status.numel() < 1):
+        raise ValueError("status must be an int32 GPU tensor (bit pattern of a uint32)")
+    return status
+
+
+def add_requests(rows, num_computed, prompt_start, prompt_tokens, block_start, blocks, *,
+                 stream=None, **state) -> None:
+    """add_request for m new requests (pkv_add_requests); see prepared_add_requests."""
+    prepared_add_requests(rows, num_computed, prompt_start, prompt_tokens, block_start, blocks,
+                          **state)(stream)
+
+
+def prepared_add_requests(rows: torch.Tensor, num_computed: torch.Tensor,
+                          prompt_start: torch.Tensor, prompt_tokens: torch.Tensor,
+                          block_start: torch.Tensor, blocks: torch.Tensor, *,
+                          completed: torch.Tensor, token_ids: torch.Tensor,
+                          block_table: torch.Tensor, row_blocks: torch.Tensor,
+                          status: Optional[torch.Tensor] = None):
+    """Register m requests in the persistent state.
+
+    rows, num_computed: int32 [m]; prompts and block ids as CSR lists:
+    prompt_start [m+1] into prompt_tokens (flat int32), block_start [m+1] into
+    blocks (flat int32).  State (updated in place): completed [R], token_ids
+    [R, L], block_table [R, MB], row_blocks [R].
+    """
+    m = rows.shape[0]
+    _idx("rows", rows, (m,))
+    _idx("num_computed", num_computed, (m,))
+    _idx("prompt_start", prompt_start, (m + 1,))
+    _idx("prompt_tokens", prompt_tokens)
+    _idx("block_start", block_start, (m + 1,))
+    _idx("blocks", blocks)
+    _idx("completed", completed)
+    R = completed.shape[0]
+    _idx("row_blocks", row_blocks, (R,))
+    L, stride = _token_table(token_ids, R)
+    MB = _block_table(block_table, R)
+    args = (m, _ptr(rows), _ptr(num_computed), _ptr(prompt_start), _ptr(prompt_tokens),
+            prompt_tokens.numel(), _ptr(block_start), _ptr(blocks), blocks.numel(), R,
+            _ptr(completed), _ptr(token_ids), stride, L, _ptr(block_table), MB, _ptr(row_blocks),
+            _ptr(_status(status)))
+    return _prepared("add_requests", _lib.pkv_add_requests, args,
+                     (rows, num_computed, prompt_start, prompt_tokens, block_start, blocks,
+                      completed, token_ids, block_table, row_blocks, status))
+
+
+def append_blocks(rows, block_start, blocks, *, stream=None, **state) -> None:
+    """update_request: append new block ids (pkv_append_blocks); see prepared_append_blocks."""
+    prepared_append_blocks(rows, block_start, blocks, **state)(stream)
+
+
+def prepared_append_blocks(rows: torch.Tensor, block_start: torch.Tensor, blocks: torch.Tensor,
+                           *, block_table: torch.Tensor, row_blocks: torch.Tensor,
+                           status: Optional[torch.Tensor] = None):
+    """Append each request's newly allocated block ids (CSR: block_start [m+1]
+    into blocks) after the row_blocks[row] entries its block-table row holds."""
+    m = rows.shape[0]
+    _idx("rows", rows, (m,))
+    _idx("block_start", block_start, (m + 1,))
+    _idx("blocks", blocks)
+    _idx("row_blocks", row_blocks)
+    R = row_blocks.shape[0]
+    MB = _block_table(block_table, R)
+    args = (m, _ptr(rows), _ptr(block_start), _ptr(blocks), blocks.numel(), R, _ptr(block_table),
+            MB, _ptr(row_blocks), _ptr(_status(status)))
+    return _prepared("append_blocks", _lib.pkv_append_blocks, args,
+                     (rows, block_start, blocks, block_table, row_blocks, status))
+
+
+def advance_state(index_mapping, seq_lens, sampled=None, *, stream=None, **state) -> None:
+    """After a step (pkv_advance_state); see prepared_advance_state."""
+    prepared_advance_state(index_mapping, seq_lens, sampled, **state)(stream)
+
+
+def prepared_advance_state(index_mapping: torch.Tensor, seq_lens: torch.Tensor,
+                           sampled: Optional[torch.Tensor] = None, *, completed: torch.Tensor,
+                           token_ids: Optional[torch.Tensor] = None,
+                           status: Optional[torch.Tensor] = None):
+    """completed[index_mapping[b]] = seq_lens[b]; sampled[b] >= 0 is appended
+    to the row's token list at position seq_lens[b].  index_mapping, seq_lens,
+    sampled: int32 [n] (the batch order of prepare_batch); token_ids [R, L] is
+    needed with sampled."""
+    n = index_mapping.shape[0]
+    _idx("index_mapping", index_mapping, (n,))
+    _idx("seq_lens", seq_lens, (n,))
+    _idx("sampled", sampled, (n,), optional=True)
+    _idx("completed", completed)
+    R = completed.shape[0]
+    L, stride = 0, 0
+    if token_ids is not None:
+        L, stride = _token_table(token_ids, R)
+    elif sampled is not None:
+        raise ValueError("sampled needs token_ids")
+    args = (n, _ptr(index_mapping), _ptr(seq_lens), _ptr(sampled), R, _ptr(completed),
+            _ptr(token_ids), stride, L, _ptr(_status(status)))
+    return _prepared("advance_state", _lib.pkv_advance_state, args,
+                     (index_mapping, seq_lens, sampled, completed, token_ids, status))

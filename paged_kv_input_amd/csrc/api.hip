@@ -183,6 +183,61 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
     return from_hip(e);
 }
 
+int pkv_add_requests(int32_t m, const int32_t* rows, const int32_t* num_computed,
+                     const int32_t* prompt_start, const int32_t* prompt_tokens,
+                     int32_t num_prompt_tokens, const int32_t* block_start, const int32_t* blocks,
+                     int32_t num_blocks_given, int32_t R, int32_t* completed, int32_t* token_ids,
+                     int64_t token_stride, int32_t L, int32_t* block_table, int32_t MB,
+                     int32_t* row_blocks, uint32_t* status, void* stream)
+{
+    if (m < 0 || R < 0 || L < 0 || MB < 0 || token_stride < L || num_prompt_tokens < 0 ||
+        num_blocks_given < 0)
+        return PKV_EINVAL;
+    if (m > 0 && (rows == nullptr || num_computed == nullptr || prompt_start == nullptr ||
+                  block_start == nullptr || (num_prompt_tokens > 0 && prompt_tokens == nullptr) ||
+                  (num_blocks_given > 0 && blocks == nullptr) ||
+                  (R > 0 && (completed == nullptr || row_blocks == nullptr ||
+                             (L > 0 && token_ids == nullptr) ||
+                             (MB > 0 && block_table == nullptr)))))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_add_requests(m, rows, num_computed, prompt_start, prompt_tokens,
+                                             num_prompt_tokens, block_start, blocks,
+                                             num_blocks_given, R, completed, token_ids,
+                                             token_stride, L, block_table, MB, row_blocks, status,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int pkv_append_blocks(int32_t m, const int32_t* rows, const int32_t* block_start,
+                      const int32_t* blocks, int32_t num_blocks_given, int32_t R,
+                      int32_t* block_table, int32_t MB, int32_t* row_blocks, uint32_t* status,
+                      void* stream)
+{
+    if (m < 0 || R < 0 || MB < 0 || num_blocks_given < 0)
+        return PKV_EINVAL;
+    if (m > 0 && (rows == nullptr || block_start == nullptr ||
+                  (num_blocks_given > 0 && blocks == nullptr) ||
+                  (R > 0 && (row_blocks == nullptr || (MB > 0 && block_table == nullptr)))))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_append_blocks(m, rows, block_start, blocks, num_blocks_given, R,
+                                              block_table, MB, row_blocks, status,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int pkv_advance_state(int32_t n, const int32_t* index_mapping, const int32_t* seq_lens,
+                      const int32_t* sampled, int32_t R, int32_t* completed, int32_t* token_ids,
+                      int64_t token_stride, int32_t L, uint32_t* status, void* stream)
+{
+    if (n < 0 || R < 0 || L < 0 || token_stride < L)
+        return PKV_EINVAL;
+    if (n > 0 && (index_mapping == nullptr || seq_lens == nullptr ||
+                  (R > 0 && completed == nullptr) ||
+                  (sampled != nullptr && R > 0 && L > 0 && token_ids == nullptr)))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_advance_state(n, index_mapping, seq_lens, sampled, R, completed,
+                                              token_ids, token_stride, L, status,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 const char* pkv_error_string(int code)
 {
     switch (code) {

@@ -497,6 +497,24 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
 // Work-items of the grid launch_step would launch.
 int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
 
+hipError_t launch_add_requests(int32_t m, const int32_t* rows, const int32_t* num_computed,
+                               const int32_t* prompt_start, const int32_t* prompt_tokens,
+                               int32_t num_prompt_tokens, const int32_t* block_start,
+                               const int32_t* blocks, int32_t num_blocks_given, int32_t R,
+                               int32_t* completed, int32_t* token_ids, int64_t token_stride,
+                               int32_t L, int32_t* block_table, int32_t MB, int32_t* row_blocks,
+                               uint32_t* status, hipStream_t stream);
+
+hipError_t launch_append_blocks(int32_t m, const int32_t* rows, const int32_t* block_start,
+                                const int32_t* blocks, int32_t num_blocks_given, int32_t R,
+                                int32_t* block_table, int32_t MB, int32_t* row_blocks,
+                                uint32_t* status, hipStream_t stream);
+
+hipError_t launch_advance_state(int32_t n, const int32_t* index_mapping, const int32_t* seq_lens,
+                                const int32_t* sampled, int32_t R, int32_t* completed,
+                                int32_t* token_ids, int64_t token_stride, int32_t L,
+                                uint32_t* status, hipStream_t stream);
+
 hipError_t launch_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride,
                           const void* v, int64_t v_stride, void* k_cache, void* v_cache,
                           int64_t num_slots, const int32_t* slot_mapping, uint32_t* status,

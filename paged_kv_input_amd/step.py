@@ -19,7 +19,7 @@ from . import api
 class GroupSpec:
     """Host description of one KV-cache group for a step."""
 
-    block_table: np.ndarray     # int32 [R, MB]
+    block_table: np.ndarray     # int32 [R, MB] (or a device tensor, used in place)
     block_size: int
     num_blocks: int
     k: np.ndarray               # [T, H, D] payload words (any dtype, copied as bits)
@@ -35,21 +35,33 @@ class DeviceStep:
                  with_block_tables: bool = True, num_tokens: Optional[int] = None,
                  caches: Optional[Sequence] = None):
         dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
 
         def up(a, dtype=None):
+            if isinstance(a, torch.Tensor):      # already on the device (e.g. DeviceState's)
+                if a.device != dev or (dtype is not None and a.dtype != dtype):
+                    raise ValueError("device tensors must be on the step's device")
+                return a
             t = torch.from_numpy(np.ascontiguousarray(a))
             if dtype is not None:
                 t = t.to(dtype)
             return t.to(dev)
 
+        def as_i32(a):
+            return up(a, torch.int32) if isinstance(a, torch.Tensor) else up(np.asarray(a, np.int32))
+
         self.device = dev
-        self.sched_rows = up(np.asarray(sched_rows, np.int32))
-        self.num_scheduled = up(np.asarray(num_scheduled, np.int32))
-        self.completed = up(np.asarray(completed, np.int32))
-        self.token_ids = up(np.asarray(token_ids, np.int32)) if with_input_ids else None
+        self.sched_rows = as_i32(sched_rows)
+        self.num_scheduled = as_i32(num_scheduled)
+        self.completed = as_i32(completed)
+        self.token_ids = as_i32(token_ids) if with_input_ids else None
         self.n = int(self.sched_rows.shape[0])
-        self.T = int(np.maximum(np.asarray(num_scheduled, np.int64), 0).sum()) \
-            if num_tokens is None else int(num_tokens)
+        if num_tokens is None:
+            if isinstance(num_scheduled, torch.Tensor):
+                raise ValueError("num_tokens is required when num_scheduled is a device tensor")
+            num_tokens = int(np.maximum(np.asarray(num_scheduled, np.int64), 0).sum())
+        self.T = int(num_tokens)
         i32 = dict(dtype=torch.int32, device=dev)
         self.index_mapping = torch.empty(self.n, **i32)
         self.query_start_loc = torch.empty(self.n + 1, **i32)
@@ -61,7 +73,7 @@ class DeviceStep:
         self._fused = None
         self._prep = None
         for g in groups:
-            bt = up(np.asarray(g.block_table, np.int32))
+            bt = as_i32(g.block_table)
             k = up(np.ascontiguousarray(g.k).view(np.int16))
             v = up(np.ascontiguousarray(g.v).view(np.int16))
             row_shape = tuple(k.shape[1:])

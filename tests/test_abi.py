@@ -33,7 +33,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert names == ["pkv_abi_version", "pkv_compute_slot_mapping", "pkv_error_string",
+    assert names == ["pkv_abi_version", "pkv_add_requests", "pkv_advance_state",
+                     "pkv_append_blocks", "pkv_compute_slot_mapping", "pkv_error_string",
                      "pkv_prepare_batch", "pkv_scatter_kv", "pkv_step"]
     for name in names:
         assert hasattr(lib, name), name
@@ -117,6 +118,46 @@ def test_step_host_argument_errors(lib):
     args[0] = 4097
     arr[0].row_bytes = 16
     assert st(*args, 1, arr, None, None) == -3           # beyond PKV_MAX_BATCH
+
+
+def test_state_host_argument_errors(lib):
+    """The state updates reject what the oracle rejects, before any HIP call."""
+    N = None
+    fake = ctypes.c_void_p(0x1000)
+    add = lib.pkv_add_requests
+    ok = [1, fake, fake, fake, fake, 4, fake, fake, 2, 8, fake, fake, 16, 16, fake, 4, fake, N, N]
+
+    def with_(args, **kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return a
+
+    assert add(*with_(ok, a0=-1)) == -1                 # m < 0
+    assert add(*with_(ok, a5=-1)) == -1                 # num_prompt_tokens < 0
+    assert add(*with_(ok, a8=-1)) == -1                 # num_blocks_given < 0
+    assert add(*with_(ok, a12=8)) == -1                 # token_stride < L
+    assert add(*with_(ok, a15=-1)) == -1                # MB < 0
+    assert add(*with_(ok, a1=N)) == -1                  # rows NULL
+    assert add(*with_(ok, a4=N)) == -1                  # prompt tokens NULL, some given
+    assert add(*with_(ok, a7=N)) == -1                  # blocks NULL, some given
+    assert add(*with_(ok, a14=N)) == -1                 # block table NULL
+    assert add(*with_(ok, a0=0, a1=N, a2=N, a3=N, a6=N)) == 0   # m = 0: nothing to do
+    app = lib.pkv_append_blocks
+    ok = [1, fake, fake, fake, 2, 8, fake, 4, fake, N, N]
+    assert app(*with_(ok, a0=-1)) == -1
+    assert app(*with_(ok, a4=-1)) == -1
+    assert app(*with_(ok, a7=-1)) == -1
+    assert app(*with_(ok, a2=N)) == -1
+    assert app(*with_(ok, a8=N)) == -1
+    assert app(*with_(ok, a0=0, a1=N, a2=N)) == 0
+    adv = lib.pkv_advance_state
+    ok = [1, fake, fake, fake, 8, fake, fake, 16, 16, N, N]
+    assert adv(*with_(ok, a0=-1)) == -1
+    assert adv(*with_(ok, a7=8)) == -1                  # token_stride < L
+    assert adv(*with_(ok, a1=N)) == -1
+    assert adv(*with_(ok, a6=N)) == -1                  # sampled without a token table
+    assert adv(*with_(ok, a0=0, a1=N, a2=N)) == 0
 
 
 def test_binding_rejects_cpu_tensors():
