@@ -30,6 +30,7 @@ _lib = None
 # Contract values, restated (not shared) from the library's public header.
 OK = 0
 EINVAL = -1
+ENOROWS = -5
 ST_BAD_ROW, ST_BAD_COUNT, ST_TOKEN_SUM, ST_POS_OOR = 0x01, 0x02, 0x04, 0x08
 ST_LB_OOR, ST_BLOCK_OOR, ST_SLOT_OOR, ST_BAD_RANGE = 0x10, 0x20, 0x40, 0x80
 
@@ -63,6 +64,11 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_append_blocks.argtypes = [_I32, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P]
     lib.orc_advance_state.restype = ctypes.c_int
     lib.orc_advance_state.argtypes = [_I32, _P, _P, _P, _I32, _P, _P, _I64, _I32, _P]
+    for name in ("orc_pool_acquire", "orc_pool_release"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [_I32, _P, _P, _P, _I32, _P]
+    lib.orc_pool_reset.restype = ctypes.c_int
+    lib.orc_pool_reset.argtypes = [_I32, _P, _P, _P]
     return lib
 
 
@@ -253,3 +259,33 @@ def empty_state(R, L, MB, token_fill=-1):
             "token_ids": np.full((R, L), token_fill, np.int32),
             "block_table": np.full((R, MB), -1, np.int32),
             "row_blocks": np.zeros(R, np.int32)}
+
+
+class RowPool:
+    """The oracle's row pool on NumPy arrays (see orc_pool_* in oracle.c)."""
+
+    def __init__(self, R, *, lib=None):
+        self.lib = lib or load()
+        self.R = int(R)
+        self.free_rows = np.zeros(max(self.R, 1), np.int32)
+        self.in_use = np.zeros(max(self.R, 1), np.uint8)
+        self.num_free = np.zeros(1, np.int32)
+        rc = self.lib.orc_pool_reset(self.R, _ptr(self.free_rows), _ptr(self.num_free),
+                                     _ptr(self.in_use))
+        assert rc == OK
+
+    def acquire(self, m):
+        """(rc, rows handed out)"""
+        out = np.full(max(int(m), 1), -7, np.int32)
+        rc = self.lib.orc_pool_acquire(self.R, _ptr(self.free_rows), _ptr(self.num_free),
+                                       _ptr(self.in_use), int(m), _ptr(out))
+        return int(rc), (out[:m].tolist() if rc == OK else [])
+
+    def release(self, rows):
+        r = _i32(rows) if len(rows) else np.zeros(1, np.int32)
+        return int(self.lib.orc_pool_release(self.R, _ptr(self.free_rows), _ptr(self.num_free),
+                                             _ptr(self.in_use), len(rows), _ptr(r)))
+
+    @property
+    def free(self):
+        return int(self.num_free[0])

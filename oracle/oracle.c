@@ -37,6 +37,9 @@
  *   orc_append_blocks,          nothing, the [CF] prefix example's [P1][P2][B3]
  *   orc_advance_state           table (reuse, then one appended block), brute-
  *                               force state loops, a multi-step decode loop.
+ *   orc_pool_*               -- a Python list used as a stack, run on random
+ *                               acquire/release sequences; invariants (no row
+ *                               out twice, free + in use = R).
  * Readings of points the pages leave open are listed at each step (R1..R9).
  */
 #include <stdint.h>
@@ -44,8 +47,9 @@
 #include <string.h>
 
 /* Return codes (host-detectable argument errors). */
-#define ORC_OK      0
-#define ORC_EINVAL (-1)
+#define ORC_OK       0
+#define ORC_EINVAL  (-1)
+#define ORC_ENOROWS (-5)  /* row pool: fewer free rows than asked for */
 
 /* Status bits (data errors found while computing; OR-ed into *status). */
 #define ORC_ST_BAD_ROW    0x01u  /* request_state_index outside [0, R)            */
@@ -374,8 +378,8 @@ int orc_scatter_kv(int32_t T, int64_t row_bytes,
  * tokens already processed (completed), the request's token list (token_ids
  * row) and its block table row.  R10: the state also keeps row_blocks[r], the
  * number of logical blocks allocated to row r, so that new block ids can be
- * appended after the existing ones.  Choosing and recycling rows (the free
- * list) stays with the caller, as the scheduler's bookkeeping.
+ * appended after the existing ones.  Which row a request gets comes from the
+ * row pool at the end of this file.
  */
 
 /*
@@ -524,5 +528,66 @@ int orc_advance_state(int32_t n, const int32_t* index_mapping, const int32_t* se
     }
     if (status != NULL)
         *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * Row pool ([KC] "Design Logic Behind the Dual-Index System": a new request is
+ * handed a request_state_index and a completed request gives its index back to
+ * be handed out again, so rows are pooled instead of allocated and freed).
+ * State, caller-owned: free_rows[R] (a stack, valid below *num_free) and
+ * in_use[R] (1 while a row is handed out).
+ * R12: the stack starts with every row, arranged so that rows 0, 1, 2, ... come
+ *      out first; acquire pops from the top, release pushes the rows in the
+ *      order given, so the row released last is handed out next.
+ * R13: asking for more rows than are free hands out none (ORC_ENOROWS);
+ *      releasing a row outside [0, R), one not handed out, or one listed twice
+ *      in the call releases none (ORC_EINVAL).
+ */
+int orc_pool_reset(int32_t R, int32_t* free_rows, int32_t* num_free, uint8_t* in_use)
+{
+    if (R < 0 || num_free == NULL || (R > 0 && (free_rows == NULL || in_use == NULL)))
+        return ORC_EINVAL;
+    for (int32_t i = 0; i < R; ++i) {
+        free_rows[i] = R - 1 - i;        /* row 0 on top */
+        in_use[i] = 0;
+    }
+    *num_free = R;
+    return ORC_OK;
+}
+
+int orc_pool_acquire(int32_t R, int32_t* free_rows, int32_t* num_free, uint8_t* in_use,
+                     int32_t m, int32_t* out)
+{
+    if (R < 0 || m < 0 || num_free == NULL || (m > 0 && out == NULL))
+        return ORC_EINVAL;
+    if (m > *num_free)
+        return ORC_ENOROWS;
+    for (int32_t i = 0; i < m; ++i) {
+        int32_t r = free_rows[*num_free - 1];
+        *num_free -= 1;
+        in_use[r] = 1;
+        out[i] = r;
+    }
+    return ORC_OK;
+}
+
+int orc_pool_release(int32_t R, int32_t* free_rows, int32_t* num_free, uint8_t* in_use,
+                     int32_t m, const int32_t* rows)
+{
+    if (R < 0 || m < 0 || num_free == NULL || (m > 0 && rows == NULL))
+        return ORC_EINVAL;
+    for (int32_t i = 0; i < m; ++i) {
+        if (rows[i] < 0 || rows[i] >= R || !in_use[rows[i]])
+            return ORC_EINVAL;
+        for (int32_t j = 0; j < i; ++j)
+            if (rows[j] == rows[i])
+                return ORC_EINVAL;
+    }
+    for (int32_t i = 0; i < m; ++i) {
+        in_use[rows[i]] = 0;
+        free_rows[*num_free] = rows[i];
+        *num_free += 1;
+    }
     return ORC_OK;
 }

@@ -506,6 +506,62 @@ def pin_state_errors(lib):
     _eq(st["token_ids"][2], [-1, -1, -1, -1], "no token for sampled -1")
 
 
+def pin_pool_model(lib, seeds=range(40)):
+    """The row pool against a Python list used as a stack (rows 0, 1, ... on
+    top at the start; acquire pops, release pushes in order), with its
+    all-or-nothing failures, on random sequences; plus the invariants: no row
+    is handed out twice, and free plus handed-out rows make up every row."""
+    for seed in seeds:
+        rng = np.random.default_rng(700 + seed)
+        R = int(rng.integers(0, 12))
+        pool = oracle.RowPool(R, lib=lib)
+        stack = list(range(R - 1, -1, -1))
+        out = set()
+        for _ in range(30):
+            if rng.random() < 0.5:
+                m = int(rng.integers(0, R + 3))
+                rc, rows = pool.acquire(m)
+                if m > len(stack):
+                    assert rc == oracle.ENOROWS and rows == [], (seed, m)
+                else:
+                    want = [stack.pop() for _ in range(m)]
+                    assert rc == 0 and rows == want, (seed, rows, want)
+                    assert not (set(rows) & out), "row handed out twice"
+                    out |= set(rows)
+            else:
+                cand = sorted(out) * 2 + list(range(R)) + [-1, R, R + 5]
+                k = int(rng.integers(0, 4))
+                rows = [int(x) for x in rng.choice(cand, k)] if k else []
+                ok = len(set(rows)) == len(rows) and all(r in out for r in rows)
+                rc = pool.release(rows)
+                if ok:
+                    assert rc == 0, (seed, rows)
+                    stack.extend(rows)
+                    out -= set(rows)
+                else:
+                    assert rc == oracle.EINVAL, (seed, rows)
+            assert pool.free == len(stack) and pool.free + len(out) == R
+            assert pool.free_rows[:pool.free].tolist() == stack
+            assert sorted(np.flatnonzero(pool.in_use[:R]).tolist()) == sorted(out)
+
+
+def pin_pool_recycles_into_state(lib):
+    """A completed request's row goes back to the pool and the next request
+    gets it; add_request then leaves nothing of the old request's blocks."""
+    pool = oracle.RowPool(4, lib=lib)
+    st = oracle.empty_state(4, 8, 3)
+    rc, (a, b) = pool.acquire(2)
+    assert (a, b) == (0, 1)
+    oracle.add_requests(st, [a, b], [0, 0], [[1, 2, 3], [4]], [[5, 6, 7], [8]], lib=lib)
+    assert pool.release([a]) == 0
+    rc, (c,) = pool.acquire(1)
+    assert c == a
+    oracle.add_requests(st, [c], [0], [[9]], [[2]], lib=lib)
+    _eq(st["block_table"][c], [2, -1, -1], "recycled row's blocks")
+    _eq(st["row_blocks"][c], 1, "recycled row's block count")
+
+
 STATE_PINS = [pin_state_pages_example, pin_state_prefix_example, pin_state_bruteforce,
-              pin_state_multistep, pin_state_errors]
+              pin_state_multistep, pin_state_errors, pin_pool_model,
+              pin_pool_recycles_into_state]
 ALL_PINS += STATE_PINS

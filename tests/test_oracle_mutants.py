@@ -89,6 +89,15 @@ MUTANTS = {
     "advance_token_one_early": (
         "            int32_t p = seq_lens[b];",
         "            int32_t p = seq_lens[b] - 1;"),
+    "pool_fifo": (
+        "        int32_t r = free_rows[*num_free - 1];",
+        "        int32_t r = free_rows[R - *num_free];"),
+    "pool_no_duplicate_check": (
+        "            if (rows[j] == rows[i])\n                return ORC_EINVAL;",
+        "            (void)rows[j];"),
+    "pool_release_not_in_use": (
+        "        if (rows[i] < 0 || rows[i] >= R || !in_use[rows[i]])",
+        "        if (rows[i] < 0 || rows[i] >= R)"),
     "bad_row_not_flagged": (
         "            st |= ORC_ST_BAD_ROW;\n            seq_lens[b] = -1;",
         "            seq_lens[b] = -1;"),
