@@ -151,6 +151,82 @@ def cpu_baseline(batch, budget_s):
                        f"{el:.1f} s on one host thread (plain C oracle, gcc -O2)")
 
 
+def state_calls(batch, step, steps, warmup, stream):
+    """The persistent-state updates on this batch's shape, each timed back to
+    back like the step: registering the batch's requests (add_requests: each
+    prompt is the history plus this step's tokens, its blocks are the
+    allocated prefix of group 0's block-table row), appending one new block
+    per request (append_blocks; the table is widened so that every timed call
+    has room) and the after-step advance (advance_state on the step's own
+    index_mapping and seq_lens, one sampled token per request).  All three
+    move well under 1 MB here, so they are bound by launch and memory
+    latency; bytes count each required read or write once."""
+    import numpy as np
+    import torch
+
+    from paged_kv_input_amd import api
+    from paged_kv_input_amd.state import DeviceState, pack_csr
+
+    g = batch.groups[0]
+    rows = batch.sched_rows.astype(np.int64)
+    plen = np.minimum(batch.completed[rows].astype(np.int64)
+                      + np.maximum(batch.num_scheduled, 0), batch.L)
+    nblk = np.minimum(-(-plen // g.block_size), g.max_blocks)
+    MB = g.max_blocks + warmup + steps
+    ds = DeviceState(batch.R, batch.L + 1, MB)     # one spare position for the sampled token
+    dev = ds.device
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    ps, pt, _ = pack_csr([batch.token_ids[r, :p] for r, p in zip(rows, plen)])
+    bs_, bl, _ = pack_csr([g.block_table[r, :k] for r, k in zip(rows, nblk)])
+    ptot, btot = int(plen.sum()), int(nblk.sum())
+    rows_d = up(rows)
+    add = api.prepared_add_requests(
+        rows_d, up(batch.completed[rows]), up(ps), up(pt)[:ptot], up(bs_), up(bl)[:btot],
+        completed=ds.completed,
+        token_ids=ds.token_ids, block_table=ds.block_table, row_blocks=ds.row_blocks,
+        status=ds.status)
+    one = pack_csr([[int(b)] for b in np.arange(batch.n) % max(g.num_blocks, 1)])
+    app = api.prepared_append_blocks(rows_d, up(one[0]), up(one[1]),
+                                     block_table=ds.block_table, row_blocks=ds.row_blocks,
+                                     status=ds.status)
+    sampled = up(np.arange(batch.n) % 128256)
+    adv = api.prepared_advance_state(step.index_mapping, step.seq_lens, sampled,
+                                     completed=ds.completed, token_ids=ds.token_ids,
+                                     status=ds.status)
+    add(stream)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn(stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    n = batch.n
+    out = {}
+    for name, fn, nbytes in (
+            ("add_requests", add,
+             int((8 * plen + 4 * nblk).sum()) + 4 * MB * n + 24 * n + 8),
+            ("append_blocks", app, 24 * n + 4),
+            ("advance_state", adv, 20 * n)):
+        ms = timed(fn)
+        out[name] = {"ms": ms, "algorithmic_bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "bound": "latency"}
+    if ds.status_bits() != 0:
+        raise RuntimeError(f"state status bits set: {ds.status_bits():#x}")
+    out["note"] = (f"{n} requests; add_requests registers {ptot} prompt tokens and {btot} "
+                   f"blocks into a {MB}-wide table; append_blocks adds 1 block per request")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +332,7 @@ def main():
     for s in steps:
         if s.status_bits() != 0:
             raise RuntimeError(f"device status bits set: {s.status_bits():#x}")
+    state = state_calls(batch, steps[0], args.steps, args.warmup, stream)
 
     ab = algorithmic_bytes(batch)
     cb = call_bytes(batch)
@@ -313,6 +390,7 @@ def main():
             "per_call_note": "events between the calls; prepare and slot mapping move under "
                              "1 MB here, so their time is launch and memory latency",
         },
+        "state_calls": state,
         "cold_single_step": {
             "ms_median": statistics.median(cold),
             "note": "1 GiB rewrite before each step; HIP events around the single launch",

@@ -50,6 +50,8 @@ extern "C" {
 #define PKV_EALIGN       (-2)  /* K/V row, stride or pointer not a multiple of 16 bytes          */
 #define PKV_EUNSUPPORTED (-3)  /* beyond a documented limit (e.g. n > PKV_MAX_BATCH)             */
 #define PKV_EHIP         (-4)  /* the HIP runtime refused the launch                              */
+#define PKV_ENOROWS      (-5)  /* row pool: fewer free rows than asked for                       */
+#define PKV_ENOMEM       (-6)  /* row pool: host memory could not be allocated                   */
 
 /* Device status bits, OR-ed into *status. */
 #define PKV_ST_BAD_ROW    0x01u /* request_state_index outside [0, R)                 */
@@ -266,6 +268,29 @@ int pkv_advance_state(int32_t n, const int32_t* index_mapping, const int32_t* se
                       const int32_t* sampled, int32_t R, int32_t* completed,
                       int32_t* token_ids, int64_t token_stride, int32_t L,
                       uint32_t* status, void* stream);
+
+/*
+ * Row pool (host side): request_state_index rows handed to new requests and
+ * taken back from completed ones, so rows are reused instead of allocated
+ * ("Design Logic Behind the Dual-Index System" of the article above).  The
+ * host decides the row because the schedule names requests by it.  Free rows
+ * form a stack: rows 0, 1, 2, ... come out first and the row released last is
+ * handed out next.  `rows` are host arrays.  A pool is not thread-safe; it is
+ * created and destroyed by the caller (the only calls here that allocate,
+ * host memory only).
+ *   create:  R rows, all free.  EINVAL (R < 0, out NULL), ENOMEM.
+ *   acquire: m rows into rows[0..m).  ENOROWS (fewer than m free): none
+ *            handed out.  EINVAL (pool NULL, m < 0, rows NULL with m > 0).
+ *   release: rows[0..m) back to the pool, pushed in order.  EINVAL when a row
+ *            is outside [0, R), not handed out, or listed twice: none released.
+ *   num_free: free rows, -1 for a NULL pool.
+ */
+typedef struct pkv_row_pool pkv_row_pool;
+int pkv_row_pool_create(int32_t R, pkv_row_pool** out);
+void pkv_row_pool_destroy(pkv_row_pool* pool);
+int pkv_row_pool_acquire(pkv_row_pool* pool, int32_t m, int32_t* rows);
+int pkv_row_pool_release(pkv_row_pool* pool, int32_t m, const int32_t* rows);
+int32_t pkv_row_pool_num_free(const pkv_row_pool* pool);
 
 /* Static text for a return code (never NULL). */
 const char* pkv_error_string(int code);

@@ -7,7 +7,7 @@ same call names: ``prepare_batch``, ``compute_slot_mapping`` (one call per
 KV-cache group), ``scatter_kv`` (one call per group and layer) and ``step``
 (all of them for a step's first layer, in one launch), plus the persistent
 request-state updates ``add_requests``, ``append_blocks`` and
-``advance_state``.  It takes
+``advance_state`` and the host-side ``RowPool`` that hands out state rows.  It takes
 torch tensors for device memory and uses torch's current HIP stream; every
 step of the path runs in the library's kernels.  Importing an entry point loads
 the library and raises if it is missing -- there is no CPU fallback.
@@ -18,7 +18,7 @@ _API = ("prepare_batch", "compute_slot_mapping", "scatter_kv", "step", "add_requ
         "append_blocks", "advance_state", "prepared_prepare_batch",
         "prepared_compute_slot_mapping", "prepared_scatter_kv", "prepared_step",
         "prepared_add_requests", "prepared_append_blocks", "prepared_advance_state",
-        "PagedKVError",
+        "RowPool", "PagedKVError",
         "library_path", "abi_version", "error_string", "load_library", "ST_BITS", "MAX_BATCH",
         "STEP_MAX_BATCH", "STEP_MAX_GROUPS")
 

@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.environ.get("PAGEDKV_LIB", os.path.join(_HERE, "libpagedkv.so"))
 
-OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP, ENOROWS, ENOMEM = 0, -1, -2, -3, -4, -5, -6
 ST_BITS = {
     "BAD_ROW": 0x01, "BAD_COUNT": 0x02, "TOKEN_SUM": 0x04, "POS_OOR": 0x08,
     "LB_OOR": 0x10, "BLOCK_OOR": 0x20, "SLOT_OOR": 0x40, "BAD_RANGE": 0x80,
@@ -78,6 +78,16 @@ def load_library(path: str = library_path) -> ctypes.CDLL:
     lib.pkv_append_blocks.argtypes = [_I32, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _P]
     lib.pkv_advance_state.restype = ctypes.c_int
     lib.pkv_advance_state.argtypes = [_I32, _P, _P, _P, _I32, _P, _P, _I64, _I32, _P, _P]
+    lib.pkv_row_pool_create.restype = ctypes.c_int
+    lib.pkv_row_pool_create.argtypes = [_I32, ctypes.POINTER(_P)]
+    lib.pkv_row_pool_destroy.restype = None
+    lib.pkv_row_pool_destroy.argtypes = [_P]
+    lib.pkv_row_pool_acquire.restype = ctypes.c_int
+    lib.pkv_row_pool_acquire.argtypes = [_P, _I32, _P]
+    lib.pkv_row_pool_release.restype = ctypes.c_int
+    lib.pkv_row_pool_release.argtypes = [_P, _I32, _P]
+    lib.pkv_row_pool_num_free.restype = _I32
+    lib.pkv_row_pool_num_free.argtypes = [_P]
     lib.pkv_error_string.restype = ctypes.c_char_p
     lib.pkv_error_string.argtypes = [ctypes.c_int]
     lib.pkv_abi_version.restype = ctypes.c_int
@@ -449,3 +459,40 @@ def prepared_advance_state(index_mapping: torch.Tensor, seq_lens: torch.Tensor,
             _ptr(token_ids), stride, L, _ptr(_status(status)))
     return _prepared("advance_state", _lib.pkv_advance_state, args,
                      (index_mapping, seq_lens, sampled, completed, token_ids, status))
+
+
+class RowPool:
+    """Host-side pool of request_state_index rows (pkv_row_pool_*): ``acquire(m)``
+    hands out m free rows (the most recently released first), ``release(rows)``
+    takes rows back.  Both raise PagedKVError and change nothing on failure."""
+
+    def __init__(self, R: int):
+        h = _P()
+        rc = _lib.pkv_row_pool_create(int(R), ctypes.byref(h))
+        if rc != OK:
+            raise PagedKVError("row_pool_create", rc)
+        self._h = h
+        self.R = int(R)
+
+    def acquire(self, m: int):
+        out = (_I32 * max(int(m), 1))()
+        rc = _lib.pkv_row_pool_acquire(self._h, int(m), out)
+        if rc != OK:
+            raise PagedKVError("row_pool_acquire", rc)
+        return list(out[:int(m)])
+
+    def release(self, rows) -> None:
+        rows = [int(r) for r in rows]
+        arr = (_I32 * max(len(rows), 1))(*rows)
+        rc = _lib.pkv_row_pool_release(self._h, len(rows), arr)
+        if rc != OK:
+            raise PagedKVError("row_pool_release", rc)
+
+    @property
+    def num_free(self) -> int:
+        return int(_lib.pkv_row_pool_num_free(self._h))
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h is not None and _lib is not None:
+            _lib.pkv_row_pool_destroy(h)

@@ -246,6 +246,8 @@ const char* pkv_error_string(int code)
     case PKV_EALIGN: return "K/V rows, strides and pointers must be 16-byte aligned";
     case PKV_EUNSUPPORTED: return "beyond a documented limit of the library";
     case PKV_EHIP: return "HIP launch failed";
+    case PKV_ENOROWS: return "row pool: fewer free rows than asked for";
+    case PKV_ENOMEM: return "row pool: out of host memory";
     default: return "unknown pagedkv error code";
     }
 }

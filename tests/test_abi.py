@@ -35,7 +35,9 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["pkv_abi_version", "pkv_add_requests", "pkv_advance_state",
                      "pkv_append_blocks", "pkv_compute_slot_mapping", "pkv_error_string",
-                     "pkv_prepare_batch", "pkv_scatter_kv", "pkv_step"]
+                     "pkv_prepare_batch", "pkv_row_pool_acquire", "pkv_row_pool_create",
+                     "pkv_row_pool_destroy", "pkv_row_pool_num_free", "pkv_row_pool_release",
+                     "pkv_scatter_kv", "pkv_step"]
     for name in names:
         assert hasattr(lib, name), name
     so = os.path.join(ROOT, "paged_kv_input_amd", "libpagedkv.so")
@@ -58,9 +60,10 @@ def test_constants_match_binding(lib):
     for name, bit in api.ST_BITS.items():
         assert m["PKV_ST_" + name] == bit
         assert getattr(oracle, "ST_" + name) == bit
-    for code in ("OK", "EINVAL", "EALIGN", "EUNSUPPORTED", "EHIP"):
+    for code in ("OK", "EINVAL", "EALIGN", "EUNSUPPORTED", "EHIP", "ENOROWS", "ENOMEM"):
         assert m["PKV_" + code] == getattr(api, code)
-    for code in (0, -1, -2, -3, -4, 99):
+    assert m["PKV_ENOROWS"] == oracle.ENOROWS
+    for code in (0, -1, -2, -3, -4, -5, -6, 99):
         assert api.error_string(code)
 
 

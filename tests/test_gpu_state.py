@@ -3,9 +3,10 @@
 add_requests, append_blocks and advance_state run through the C ABI on a
 DeviceState; the oracle runs the same calls on host arrays.  After every call
 all four state arrays and the status word must agree bit for bit.  The last
-test closes a decode loop on the device: state updates and pkv_step alternate
+tests close a decode loop on the device: state updates and pkv_step alternate
 with no host copy of the state in between, and every step's outputs, the
-caches and the state match the oracle's loop.
+caches and the state match the oracle's loop; in the serving loop requests
+arrive and finish, and rows and blocks are recycled through the row pool.
 """
 import numpy as np
 import pytest
@@ -239,3 +240,90 @@ def test_device_decode_loop(mode):
     assert_equal("k_cache", caches[0][0].cpu().numpy().view(np.uint16), kc_o)
     assert_equal("v_cache", caches[0][1].cpu().numpy().view(np.uint16), vc_o)
     assert all(int(st["completed"][r]) > plen[i] for i, r in enumerate(rows))
+
+
+def test_device_serving_loop_with_row_pool():
+    """Requests arrive and finish: rows come from the library's RowPool (and
+    match the oracle's pool), finished rows and their blocks are recycled to
+    later requests, and the device state, step outputs and caches stay
+    bit-exact with the oracle's loop throughout."""
+    import torch
+    from paged_kv_input_amd import RowPool
+    from paged_kv_input_amd.step import DeviceStep, GroupSpec
+
+    rng = np.random.default_rng(5151)
+    R, L, MB, bs, NB, H, D = 24, 512, 32, 16, 600, 1, 64
+    chunk, steps = 64, 40
+    ds, st = new_state(R, L, MB)
+    pool, pool_o = RowPool(R), oracle.RowPool(R)
+    free_blocks = rng.permutation(NB).tolist()
+    active = {}                          # row -> [prompt_len, total_len, blocks]
+    kc_o = np.full((NB * bs, H, D), 0xFFFF, np.uint16)
+    vc_o = np.full((NB * bs, H, D), 0xFFFF, np.uint16)
+    caches, used_rows, recycled = None, set(), 0
+    for s in range(steps):
+        arrive = int(rng.integers(0, 4)) if len(active) < 16 else 0
+        if arrive:
+            rows = pool.acquire(arrive)
+            rc, rows_o = pool_o.acquire(arrive)
+            assert rc == 0 and rows == rows_o
+            plens = rng.integers(1, 150, arrive).tolist()
+            prompts = [rng.integers(0, 1 << 20, p).tolist() for p in plens]
+            blocks = [[free_blocks.pop() for _ in range(-(-min(p, chunk) // bs))] for p in plens]
+            ds.add_requests(rows, [0] * arrive, prompts, blocks)
+            oracle.add_requests(st, rows, [0] * arrive, prompts, blocks)
+            for r, p, b in zip(rows, plens, blocks):
+                recycled += r in used_rows
+                used_rows.add(r)
+                active[r] = [p, p + int(rng.integers(1, 40)), list(b)]
+        rows = list(active)
+        if not rows:
+            continue
+        counts = [min(active[r][0] - int(st["completed"][r]), chunk)
+                  if st["completed"][r] < active[r][0] else 1 for r in rows]
+        need = []
+        for r, c in zip(rows, counts):
+            want_blocks = -(-(int(st["completed"][r]) + c) // bs)
+            nb = [free_blocks.pop() for _ in range(max(0, want_blocks - int(st["row_blocks"][r])))]
+            active[r][2] += nb
+            need.append(nb)
+        ds.append_blocks(rows, need)
+        oracle.append_blocks(st, rows, need)
+        T = int(sum(counts))
+        say(f"[case] serving loop step={s} n={len(rows)} T={T} free_rows={pool.num_free}")
+        k = rng.integers(-30000, 30000, (T, H, D)).astype(np.int16)
+        v = rng.integers(-30000, 30000, (T, H, D)).astype(np.int16)
+        step = DeviceStep(rows, counts, ds.completed, ds.token_ids,
+                          [GroupSpec(ds.block_table, bs, NB, k, v)],
+                          cache_fill=SENTINEL16 if caches is None else None,
+                          ibt_fill=oracle.IBT_UNWRITTEN, caches=caches)
+        caches = [(step.groups[0]["k_cache"], step.groups[0]["v_cache"])]
+        step.run_fused()
+        prep = oracle.prepare_batch(rows, counts, st["completed"], st["token_ids"])
+        sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                         prep["seq_lens"], prep["positions"], st["block_table"],
+                                         bs, NB)
+        oracle.scatter_kv(k.view(np.uint16), v.view(np.uint16), kc_o, vc_o, sm["slot_mapping"])
+        assert prep["status"] == sm["status"] == step.status_bits() == 0
+        for key in ("index_mapping", "seq_lens", "positions", "input_ids"):
+            assert_equal(f"step {s} {key}", step.host(key), prep[key])
+        assert_equal(f"step {s} slot_mapping", step.host("slot_mapping", 0), sm["slot_mapping"])
+        sampled = rng.integers(0, 1 << 20, len(rows)).astype(np.int32)
+        for b_, r in enumerate(prep["index_mapping"].tolist()):
+            if prep["seq_lens"][b_] < active[r][0]:
+                sampled[b_] = -1
+        ds.advance(step.index_mapping, step.seq_lens, sampled)
+        oracle.advance_state(st, prep["index_mapping"], prep["seq_lens"], sampled)
+        assert take_status(ds) == 0
+        compare_state(ds, st, f"step {s}")
+        done = [r for r in rows if st["completed"][r] >= active[r][1]]
+        if done:
+            pool.release(done)
+            assert pool_o.release(done) == 0
+            for r in done:
+                free_blocks.extend(active.pop(r)[2])
+        assert pool.num_free == pool_o.free == R - len(active)
+    torch.cuda.synchronize()
+    assert_equal("k_cache", caches[0][0].cpu().numpy().view(np.uint16), kc_o)
+    assert_equal("v_cache", caches[0][1].cpu().numpy().view(np.uint16), vc_o)
+    assert recycled > 0, "no row was recycled: the loop is too short"
