@@ -64,6 +64,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_append_blocks.argtypes = [_I32, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P]
     lib.orc_advance_state.restype = ctypes.c_int
     lib.orc_advance_state.argtypes = [_I32, _P, _P, _P, _I32, _P, _P, _I64, _I32, _P]
+    lib.orc_gather_kv.restype = ctypes.c_int
+    lib.orc_gather_kv.argtypes = [_I32, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P, _I64,
+                                  _P, _I64, _P, _P]
     for name in ("orc_pool_acquire", "orc_pool_release"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = [_I32, _P, _P, _P, _I32, _P]
@@ -168,6 +171,34 @@ def scatter_kv(k, v, k_cache, v_cache, slot_mapping, *, lib=None):
                             _ptr(v), v.strides[0] if T else row_bytes,
                             _ptr(k_cache), _ptr(v_cache), num_slots, _ptr(sm), _ptr(st))
     return int(rc), int(st[0])
+
+
+def gather_kv(seq_lens, input_block_tables, block_size, num_blocks, k_cache, v_cache,
+              out_tokens=None, *, out_fill=0xFFFF, lib=None):
+    """Oracle of the paged K/V read: the rows of every position < seq_len,
+    request after request.  ``k_cache``/``v_cache`` are C-contiguous
+    [num_blocks * block_size, ...] arrays.  Returns a dict with ``k``, ``v``
+    ([out_tokens, ...], filled with ``out_fill`` where nothing is read),
+    ``kv_start`` [n+1], ``status`` and ``rc``."""
+    lib = lib or load()
+    sl, ibt = _i32(seq_lens), _i32(input_block_tables)
+    n = sl.shape[0]
+    MB = ibt.shape[1] if ibt.ndim == 2 else 0
+    if out_tokens is None:
+        out_tokens = int(np.maximum(sl.astype(np.int64), 0).sum())
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    assert k_cache.shape[0] >= num_blocks * block_size
+    row_shape = k_cache.shape[1:]
+    row_bytes = int(np.prod(row_shape)) * k_cache.itemsize
+    out = {"k": np.full((out_tokens, *row_shape), out_fill, k_cache.dtype),
+           "v": np.full((out_tokens, *row_shape), out_fill, v_cache.dtype),
+           "kv_start": np.full(n + 1, -7, np.int32)}
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_gather_kv(n, _ptr(sl), _ptr(ibt) if MB else None, MB, block_size, num_blocks,
+                           row_bytes, _ptr(k_cache), _ptr(v_cache), out_tokens, _ptr(out["k"]),
+                           row_bytes, _ptr(out["v"]), row_bytes, _ptr(out["kv_start"]), _ptr(st))
+    out["status"], out["rc"] = int(st[0]), int(rc)
+    return out
 
 
 def run_chain(batch, *, caches=None, sentinel=0xFFFF, lib=None):

@@ -37,6 +37,10 @@
  *   orc_append_blocks,          nothing, the [CF] prefix example's [P1][P2][B3]
  *   orc_advance_state           table (reuse, then one appended block), brute-
  *                               force state loops, a multi-step decode loop.
+ *   orc_gather_kv            -- the [KC] example read back (slot 207 holds B's
+ *                               new token), the inverse of the scatter,
+ *                               addresses enumerated block by block, the
+ *                               contiguous-table closed form, block size 1.
  *   orc_pool_*               -- a Python list used as a stack, run on random
  *                               acquire/release sequences; invariants (no row
  *                               out twice, free + in use = R).
@@ -367,6 +371,88 @@ int orc_scatter_kv(int32_t T, int64_t row_bytes,
                (size_t)row_bytes);
     }
 
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * Paged K/V read ([KC] "Complete Input Preparation for the Attention Module":
+ * seq_lens gives each request's KV range, history plus new tokens, and
+ * input_block_tables its visible pages, read by indirect addressing).  For
+ * every batch row b and position p < seq_lens[b] the address chain of
+ * "Multi-Layer Coordinate Conversion Pipeline" is run again -- logic_block =
+ * p / block_size, offset = p % block_size, physical_block_id from the visible
+ * pages, slot_id = physical_block_id * block_size + offset -- and the K and V
+ * rows at that slot are read.
+ * R14 (output): the pages' attention reads the pages in place; here the rows
+ *     are copied into one contiguous varlen array, request after request in
+ *     batch order: row kv_start[b] + p, where kv_start is the running sum of
+ *     the seq_lens (kv_start[0] = 0, n+1 entries, int64 sum kept in int32,
+ *     saturating at INT32_MAX).  This is the layout of a non-paged varlen
+ *     attention input and the exact inverse of the scatter.
+ * R15 (data errors): a negative seq_len counts as 0 (BAD_COUNT); a position
+ *     whose logical block is >= MB is not read (LB_OOR); a visible page
+ *     outside [0, num_blocks) is not read (BLOCK_OOR); rows at or past
+ *     out_tokens are not written (TOKEN_SUM).  Rows not read keep their
+ *     previous contents.  The cache holds num_blocks * block_size slots.
+ */
+int orc_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
+                  int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
+                  const void* k_cache, const void* v_cache, int64_t out_tokens, void* k_out,
+                  int64_t k_out_stride, void* v_out, int64_t v_out_stride, int32_t* kv_start,
+                  uint32_t* status)
+{
+    if (n < 0 || MB < 0 || block_size <= 0 || num_blocks < 0 || row_bytes <= 0 ||
+        out_tokens < 0 || k_out_stride < row_bytes || v_out_stride < row_bytes)
+        return ORC_EINVAL;
+    if (n > 0 && (seq_lens == NULL || (MB > 0 && input_block_tables == NULL)))
+        return ORC_EINVAL;
+    if (out_tokens > 0 && (k_out == NULL || v_out == NULL))
+        return ORC_EINVAL;
+    if (num_blocks > 0 && (k_cache == NULL || v_cache == NULL))
+        return ORC_EINVAL;
+
+    uint32_t st = 0;
+    const unsigned char* kc = (const unsigned char*)k_cache;
+    const unsigned char* vc = (const unsigned char*)v_cache;
+    unsigned char* ko = (unsigned char*)k_out;
+    unsigned char* vo = (unsigned char*)v_out;
+    int64_t start = 0;
+    for (int32_t batch_index = 0; batch_index < n; ++batch_index) {
+        if (kv_start != NULL)
+            kv_start[batch_index] = start > INT32_MAX ? INT32_MAX : (int32_t)start;
+        int64_t seq_len = seq_lens[batch_index];
+        if (seq_len < 0) {
+            st |= ORC_ST_BAD_COUNT;
+            seq_len = 0;
+        }
+        for (int64_t position = 0; position < seq_len; ++position) {
+            int64_t out_row = start + position;
+            if (out_row >= out_tokens) {
+                st |= ORC_ST_TOKEN_SUM;
+                break;
+            }
+            int64_t logic_block = position / block_size;
+            int64_t offset = position % block_size;
+            if (logic_block >= MB) {
+                st |= ORC_ST_LB_OOR;
+                continue;
+            }
+            int32_t physical_block_id =
+                input_block_tables[(int64_t)batch_index * MB + logic_block];
+            if (physical_block_id < 0 || physical_block_id >= num_blocks) {
+                st |= ORC_ST_BLOCK_OOR;
+                continue;
+            }
+            int64_t slot_id = (int64_t)physical_block_id * block_size + offset;
+            memcpy(ko + out_row * k_out_stride, kc + slot_id * row_bytes, (size_t)row_bytes);
+            memcpy(vo + out_row * v_out_stride, vc + slot_id * row_bytes, (size_t)row_bytes);
+        }
+        start += seq_len;
+    }
+    if (kv_start != NULL)
+        kv_start[n] = start > INT32_MAX ? INT32_MAX : (int32_t)start;
     if (status != NULL)
         *status |= st;
     return ORC_OK;

@@ -73,3 +73,19 @@ def chain(rows, counts, completed, token_ids, groups):
         out_groups.append({"slot_mapping": slots, "input_block_tables": ibt})
     return {"index_mapping": index_mapping, "query_start_loc": qsl, "seq_lens": seq_lens,
             "positions": positions, "input_ids": input_ids, "groups": out_groups}
+
+
+def gather_slots(seq_lens, visible_pages, bs):
+    """Slot read for every output row of the paged K/V read, by enumerating each
+    request's address space page by page (no division or remainder): request
+    b's rows follow the earlier requests' rows, and its position p sits at the
+    p-th address of its space.  -1 where no page exists."""
+    out = []
+    for b, sl in enumerate(seq_lens):
+        space = []
+        for blk in visible_pages[b]:
+            for o in range(bs):
+                space.append(-1 if blk < 0 else int(blk) * bs + o)
+        for p in range(max(int(sl), 0)):
+            out.append(space[p] if p < len(space) else -1)
+    return out

@@ -15,6 +15,7 @@ import numpy as np
 import oracle
 import workloads
 from bruteforce import chain as brute_chain
+from bruteforce import gather_slots as brute_gather_slots
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -305,6 +306,129 @@ def pin_strided_kv(lib):
 ALL_PINS = [pin_pages_example, pin_prefix_example, pin_budget_tie_example, pin_bruteforce,
             pin_library_routines, pin_closed_forms, pin_invariants, pin_error_semantics,
             pin_strided_kv]
+
+
+# ---------------------------------------------------------------------------
+# paged K/V read (the gather through visible pages)
+# ---------------------------------------------------------------------------
+
+def pin_gather_pages_example(lib):
+    """Reading back the kongchang.com example after its step: B's history runs
+    0..31 over blocks 37 and 12, so its row 31 is slot 207, the token just
+    written; A's rows 16..23 are slots 704..711.  kv_start = [0, 32, 56]."""
+    g = _golden("pages_example.json")
+    b = workloads.pages_example()
+    prep, groups = oracle.run_chain(b, lib=lib)
+    gr = groups[0]
+    out = oracle.gather_kv(prep["seq_lens"], gr["input_block_tables"], 16, b.groups[0].num_blocks,
+                           gr["k_cache"], gr["v_cache"], lib=lib)
+    assert out["rc"] == 0 and out["status"] == 0
+    sl = g["derived"]["seq_lens"]
+    _eq(out["kv_start"], [0, sl[0], sl[0] + sl[1]], "kv_start")
+    k, v = b.groups[0].k, b.groups[0].v
+    _eq(out["k"][31], k[0], "B's row 31")
+    _eq(out["v"][31], v[0], "B's row 31 (V)")
+    _eq(out["k"][32 + 16:32 + 24], k[1:9], "A's rows 16..23")
+    _eq(out["v"][32 + 16:32 + 24], v[1:9], "A's rows 16..23 (V)")
+    # everything else is history the step did not write: still the sentinel
+    assert int(np.any(out["k"] != 0xFFFF, axis=(1, 2)).sum()) == 9
+
+
+def pin_gather_inverse_of_scatter(lib, names=("seeded_16req", "seeded_16req_decode50")):
+    """Invariant: after a step, reading request b's positions completed ..
+    seq_len-1 gives back exactly the K/V rows of its tokens this step."""
+    for name in names:
+        b = workloads.make(name)
+        prep, groups = oracle.run_chain(b, lib=lib)
+        for g, gr in zip(b.groups, groups):
+            out = oracle.gather_kv(prep["seq_lens"], gr["input_block_tables"], g.block_size,
+                                   g.num_blocks, gr["k_cache"], gr["v_cache"], lib=lib)
+            assert out["rc"] == 0 and out["status"] == 0
+            qsl, ks = prep["query_start_loc"], out["kv_start"]
+            for bi in range(b.n):
+                cnt = int(qsl[bi + 1] - qsl[bi])
+                end = int(ks[bi + 1])
+                _eq(out["k"][end - cnt:end], g.k[qsl[bi]:qsl[bi + 1]], f"{name} K of request {bi}")
+                _eq(out["v"][end - cnt:end], g.v[qsl[bi]:qsl[bi + 1]], f"{name} V of request {bi}")
+
+
+def pin_gather_bruteforce(lib, seeds=range(150)):
+    """Random caches and visible pages (bad pages included): every output row
+    equals the cache row at the slot found by enumerating the request's
+    address space, by NumPy fancy indexing; unreadable rows keep the fill."""
+    for seed in seeds:
+        rng = np.random.default_rng(1300 + seed)
+        n = int(rng.integers(0, 7))
+        bs = int(rng.choice([1, 2, 3, 4, 16]))
+        MB = int(rng.integers(1, 6))
+        NB = int(rng.integers(1, 12))
+        sl = rng.integers(0, MB * bs + 1, n).astype(np.int32)
+        ibt = rng.integers(0, NB, (n, MB)).astype(np.int32)
+        if n and seed % 4 == 3:
+            ibt[rng.integers(n), rng.integers(MB)] = int(rng.choice([-1, NB, NB + 3]))
+        kc = rng.integers(0, 1 << 16, (NB * bs, 2, 3)).astype(np.uint16)
+        vc = rng.integers(0, 1 << 16, (NB * bs, 2, 3)).astype(np.uint16)
+        out = oracle.gather_kv(sl, ibt, bs, NB, kc, vc, lib=lib)
+        slots = np.asarray(brute_gather_slots(sl.tolist(), ibt.tolist(), bs), np.int64)
+        slots[(slots < 0) | (slots >= NB * bs)] = -1
+        good = slots >= 0
+        assert out["rc"] == 0
+        _eq(out["k"][good], kc[slots[good]], f"seed {seed} K")
+        _eq(out["v"][good], vc[slots[good]], f"seed {seed} V")
+        assert np.all(out["k"][~good] == 0xFFFF), f"seed {seed} unread rows"
+        want = oracle.ST_BLOCK_OOR if (~good).any() else 0
+        assert out["status"] == want, (seed, out["status"])
+        _eq(out["kv_start"], np.concatenate([[0], np.cumsum(sl)]), f"seed {seed} kv_start")
+
+
+def pin_gather_closed_forms(lib):
+    """Contiguous pages (page i of request b is block b*MB + i): each request's
+    rows are one contiguous slice of the cache.  Block size 1: row p is the
+    cache row named by page p."""
+    rng = np.random.default_rng(91)
+    n, MB, bs = 5, 4, 8
+    kc = rng.integers(0, 1 << 16, (n * MB * bs, 4)).astype(np.uint16)
+    sl = np.array([0, 1, 8, 9, 32], np.int32)
+    ibt = (np.arange(n)[:, None] * MB + np.arange(MB)[None, :]).astype(np.int32)
+    out = oracle.gather_kv(sl, ibt, bs, n * MB, kc, kc, lib=lib)
+    ks = out["kv_start"]
+    for b_ in range(n):
+        base = b_ * MB * bs
+        _eq(out["k"][ks[b_]:ks[b_ + 1]], kc[base:base + sl[b_]], f"contiguous request {b_}")
+    ibt1 = rng.permutation(40)[:24].reshape(3, 8).astype(np.int32)
+    kc1 = rng.integers(0, 1 << 16, (40, 2)).astype(np.uint16)
+    sl1 = np.array([8, 3, 5], np.int32)
+    out = oracle.gather_kv(sl1, ibt1, 1, 40, kc1, kc1, lib=lib)
+    want = np.concatenate([kc1[ibt1[i, :sl1[i]]] for i in range(3)])
+    _eq(out["k"], want, "block size 1")
+
+
+def pin_gather_errors(lib):
+    """R15: negative seq_len (0 rows, BAD_COUNT), a position past MB pages
+    (LB_OOR), a bad page (BLOCK_OOR), an output too small (TOKEN_SUM)."""
+    kc = np.arange(40, dtype=np.uint16).reshape(20, 2)
+    ibt = np.array([[0, 1], [2, 9], [3, 4]], np.int32)      # block 9 is outside 5 blocks
+    out = oracle.gather_kv([-3, 9, 5], ibt, 4, 5, kc, kc, out_tokens=14, lib=lib)
+    assert out["rc"] == 0
+    assert out["status"] == (oracle.ST_BAD_COUNT | oracle.ST_BLOCK_OOR | oracle.ST_LB_OOR), \
+        hex(out["status"])
+    _eq(out["kv_start"], [0, 0, 9, 14], "kv_start")
+    _eq(out["k"][0:4], kc[8:12], "request 1, page 0 (block 2)")
+    assert np.all(out["k"][4:9] == 0xFFFF), "bad page and past-MB rows unread"
+    _eq(out["k"][9:13], kc[12:16], "request 2, page 0 (block 3)")
+    _eq(out["k"][13], kc[16], "request 2, page 1, first slot")
+    out = oracle.gather_kv([-3, 9, 5], ibt, 4, 5, kc, kc, out_tokens=13, lib=lib)
+    assert out["status"] & oracle.ST_TOKEN_SUM
+    _eq(out["kv_start"], [0, 0, 9, 14], "kv_start past the output")
+    _eq(out["k"][9:13], kc[12:16], "rows before the cut")
+    out = oracle.gather_kv([4, 4], ibt[:2], 4, 5, kc, kc, out_tokens=6, lib=lib)
+    assert out["status"] == oracle.ST_TOKEN_SUM
+    _eq(out["k"][4:6], kc[8:10], "cut at out_tokens")
+
+
+GATHER_PINS = [pin_gather_pages_example, pin_gather_inverse_of_scatter, pin_gather_bruteforce,
+               pin_gather_closed_forms, pin_gather_errors]
+ALL_PINS += GATHER_PINS
 
 
 # ---------------------------------------------------------------------------
