@@ -227,6 +227,57 @@ def state_calls(batch, step, steps, warmup, stream):
     return out
 
 
+def gather_calls(batch, steps_dev, steps, warmup, stream):
+    """The paged K/V read on this batch's shape: after the step, every group's
+    KV range of every request (history plus new tokens) read through its
+    visible pages into a contiguous varlen array; rotating over the same
+    seeded batches as the step, timed back to back.  Bytes (averaged over the
+    rotation): each K/V row read once and written once, 4 B per visible page
+    read, the seq_lens read and kv_start written."""
+    import numpy as np
+    import torch
+
+    from paged_kv_input_amd import api
+
+    seqs = [np.maximum(st.seq_lens.cpu().numpy().astype(np.int64), 0) for st in steps_dev]
+    rows = [int(q.sum()) for q in seqs]
+    outs = []
+    for g in steps_dev[0].groups:
+        kc = g["k_cache"]
+        outs.append(tuple(torch.empty((max(rows), *kc.shape[1:]), dtype=kc.dtype,
+                                      device=kc.device) for _ in range(2)))
+    launches = [[api.prepared_gather_kv(st.seq_lens, g["input_block_tables"], g["block_size"],
+                                        g["num_blocks"], g["k_cache"], g["v_cache"],
+                                        k_out=o[0][:r], v_out=o[1][:r], status=st.status)
+                 for g, o in zip(st.groups, outs)]
+                for st, r in zip(steps_dev, rows)]
+    per_batch = [sum(4 * r * bg.row_bytes + 4 * int((-(-q // bg.block_size)).sum())
+                     + 8 * batch.n + 4 for bg in batch.groups) for q, r in zip(seqs, rows)]
+    nbytes = statistics.fmean(per_batch)          # the timed loop cycles through them evenly
+
+    def run(i):
+        for fn in launches[i % len(launches)]:
+            fn(stream)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        run(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    for st in steps_dev:
+        if st.status_bits() != 0:
+            raise RuntimeError(f"gather status bits set: {st.status_bits():#x}")
+    return {"ms": ms, "kv_rows": statistics.fmean(rows), "algorithmic_bytes": nbytes,
+            "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bound": "hbm",
+            "launches_per_step": len(batch.groups)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,6 +384,7 @@ def main():
         if s.status_bits() != 0:
             raise RuntimeError(f"device status bits set: {s.status_bits():#x}")
     state = state_calls(batch, steps[0], args.steps, args.warmup, stream)
+    gather = gather_calls(batch, steps, args.steps, args.warmup, stream)
 
     ab = algorithmic_bytes(batch)
     cb = call_bytes(batch)
@@ -391,6 +443,7 @@ def main():
                              "1 MB here, so their time is launch and memory latency",
         },
         "state_calls": state,
+        "gather_kv": gather,
         "cold_single_step": {
             "ms_median": statistics.median(cold),
             "note": "1 GiB rewrite before each step; HIP events around the single launch",

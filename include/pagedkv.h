@@ -15,7 +15,15 @@
  *                               KV-cache group, plus the group's visible pages
  *                               (input_block_tables);
  *   pkv_scatter_kv           -- the write of each new token's K/V at its slot,
- *                               one call per KV-cache group and layer.
+ *                               one call per KV-cache group and layer;
+ *   pkv_step                 -- all three for a step's first layer, one launch;
+ *   pkv_gather_kv            -- the read side: each request's KV range through
+ *                               its visible pages ("Complete Input Preparation
+ *                               for the Attention Module");
+ *   pkv_add_requests, pkv_append_blocks, pkv_advance_state, pkv_row_pool_*
+ *                            -- the persistent request state the path reads
+ *                               ("Persistent Request Context Strategy", "Design
+ *                               Logic Behind the Dual-Index System").
  *
  * Conventions shared by every call
  *   - Pointers named as device pointers must point to device memory (HBM) that
@@ -218,6 +226,44 @@ int pkv_step(int32_t n, int32_t T,
              uint32_t* status, void* stream);
 
 /*
+ * pkv_gather_kv -- read every request's KV range through its visible pages
+ * into one contiguous varlen array, for ONE group and ONE layer.  Attention
+ * reads positions 0 .. seq_len-1 of each request (history plus new tokens)
+ * through input_block_tables by indirect addressing ("Complete Input
+ * Preparation for the Attention Module"); this call runs that address chain
+ * ("Multi-Layer Coordinate Conversion Pipeline") and copies the rows out.  It
+ * is the exact inverse of pkv_scatter_kv.
+ *
+ * Inputs (device):
+ *   seq_lens[n]             as produced by pkv_prepare_batch
+ *   input_block_tables[n * MB]  visible pages, as produced by
+ *                           pkv_compute_slot_mapping (entries past
+ *                           ceil(seq_len / block_size) are never read)
+ *   k_cache, v_cache        [num_blocks * block_size][row_bytes] each
+ * Outputs (device):
+ *   kv_start[n+1]           (may be NULL) running sum of the seq_lens,
+ *                           kv_start[0] = 0, saturated at INT32_MAX
+ *   k_out, v_out            row kv_start[b] + p = the K / V row of position p
+ *                           of batch row b, i.e. of slot
+ *                           input_block_tables[b][p / block_size] * block_size
+ *                           + p % block_size; out_tokens rows, byte strides
+ *                           k_out_stride / v_out_stride (rows contiguous)
+ * Data errors (the row is not written; it keeps its contents): seq_len < 0
+ *   counts as 0 (BAD_COUNT); a logical block >= MB (LB_OOR); a page outside
+ *   [0, num_blocks) (BLOCK_OOR); rows at or past out_tokens (TOKEN_SUM).
+ * Host errors: EINVAL for negative sizes, block_size <= 0, row_bytes <= 0,
+ *   strides < row_bytes, num_blocks * block_size > 2^31, or a NULL pointer
+ *   that data is needed from; EALIGN unless row_bytes, the strides and every
+ *   K/V pointer are multiples of 16 bytes; EUNSUPPORTED for n > PKV_MAX_BATCH,
+ *   out_tokens > INT32_MAX or rows of 2^23 or more 16-byte chunks.
+ */
+int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
+                  int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
+                  const void* k_cache, const void* v_cache, int64_t out_tokens, void* k_out,
+                  int64_t k_out_stride, void* v_out, int64_t v_out_stride, int32_t* kv_start,
+                  uint32_t* status, void* stream);
+
+/*
  * Persistent request state ("Persistent Request Context Strategy" and "Design
  * Logic Behind the Dual-Index System" of the article above).  Per state row
  * (request_state_index) the caller keeps, in device memory:
@@ -239,8 +285,11 @@ int pkv_step(int32_t n, int32_t T,
 /* add_request: row rows[i] gets completed = num_computed[i], its prompt
  * tokens at positions 0.. (entries past the prompt are left as they are), its
  * blocks at logical blocks 0.. with the rest of the row set to -1, and
- * row_blocks = the number of blocks given.  Host errors: EINVAL for negative
- * sizes, token_stride < L, or a NULL pointer with m > 0. */
+ * row_blocks = the number of blocks given.  Each KV-cache group has its own
+ * block_table and row_blocks: register the requests in a further group by
+ * calling again with that group's table and empty prompt lists (completed is
+ * set to the same values again, the token table is left alone).  Host errors:
+ * EINVAL for negative sizes, token_stride < L, or a NULL pointer with m > 0. */
 int pkv_add_requests(int32_t m, const int32_t* rows, const int32_t* num_computed,
                      const int32_t* prompt_start, const int32_t* prompt_tokens,
                      int32_t num_prompt_tokens, const int32_t* block_start,

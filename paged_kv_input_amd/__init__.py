@@ -5,7 +5,8 @@ The work runs in hand-written HIP kernels behind a C ABI (``libpagedkv.so``,
 declared in ``include/pagedkv.h``).  This package is a thin binding with the
 same call names: ``prepare_batch``, ``compute_slot_mapping`` (one call per
 KV-cache group), ``scatter_kv`` (one call per group and layer) and ``step``
-(all of them for a step's first layer, in one launch), plus the persistent
+(all of them for a step's first layer, in one launch), the read side
+``gather_kv`` (each request's KV range through its visible pages), the persistent
 request-state updates ``add_requests``, ``append_blocks`` and
 ``advance_state`` and the host-side ``RowPool`` that hands out state rows.  It takes
 torch tensors for device memory and uses torch's current HIP stream; every
@@ -14,7 +15,8 @@ the library and raises if it is missing -- there is no CPU fallback.
 """
 from __future__ import annotations
 
-_API = ("prepare_batch", "compute_slot_mapping", "scatter_kv", "step", "add_requests",
+_API = ("prepare_batch", "compute_slot_mapping", "scatter_kv", "step", "gather_kv",
+        "prepared_gather_kv", "add_requests",
         "append_blocks", "advance_state", "prepared_prepare_batch",
         "prepared_compute_slot_mapping", "prepared_scatter_kv", "prepared_step",
         "prepared_add_requests", "prepared_append_blocks", "prepared_advance_state",

@@ -71,6 +71,9 @@ def load_library(path: str = library_path) -> ctypes.CDLL:
     lib.pkv_step.restype = ctypes.c_int
     lib.pkv_step.argtypes = [_I32, _I32, _P, _P, _P, _I32, _P, _I64, _I32, _P, _P, _P, _P, _P,
                              _I32, ctypes.POINTER(Group), _P, _P]
+    lib.pkv_gather_kv.restype = ctypes.c_int
+    lib.pkv_gather_kv.argtypes = [_I32, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P, _I64,
+                                  _P, _I64, _P, _P, _P]
     lib.pkv_add_requests.restype = ctypes.c_int
     lib.pkv_add_requests.argtypes = [_I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P,
                                      _I64, _I32, _P, _I32, _P, _P, _P]
@@ -253,6 +256,46 @@ def prepared_scatter_kv(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
             k_cache.shape[0], _ptr(slot_mapping), _ptr(status))
     return _prepared("scatter_kv", _lib.pkv_scatter_kv, args,
                      (k, v, k_cache, v_cache, slot_mapping, status))
+
+
+def gather_kv(seq_lens, input_block_tables, block_size, num_blocks, k_cache, v_cache, *,
+              stream=None, **outputs) -> None:
+    """Read each request's KV range through its visible pages (pkv_gather_kv);
+    see prepared_gather_kv."""
+    prepared_gather_kv(seq_lens, input_block_tables, block_size, num_blocks, k_cache, v_cache,
+                       **outputs)(stream)
+
+
+def prepared_gather_kv(seq_lens: torch.Tensor, input_block_tables: torch.Tensor,
+                       block_size: int, num_blocks: int, k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, *, k_out: torch.Tensor, v_out: torch.Tensor,
+                       kv_start: Optional[torch.Tensor] = None,
+                       status: Optional[torch.Tensor] = None):
+    """Copy positions 0 .. seq_len-1 of every batch row, read through its
+    visible pages, to rows kv_start[b] + p of k_out / v_out (ONE group, ONE layer).
+
+    seq_lens: int32 [n]; input_block_tables: int32 [n, MB]; k_cache, v_cache:
+    contiguous [num_slots, ...] with num_slots >= num_blocks * block_size;
+    k_out, v_out: [out_tokens, ...] with rows of the cache's size (contiguous
+    rows, the token stride may be larger); kv_start: int32 [n+1] or None.
+    """
+    n = seq_lens.shape[0]
+    _idx("seq_lens", seq_lens, (n,))
+    _idx("input_block_tables", input_block_tables)
+    if input_block_tables.dim() != 2 or input_block_tables.shape[0] != n:
+        raise ValueError("input_block_tables must be [n, MB]")
+    MB = input_block_tables.shape[1]
+    _idx("kv_start", kv_start, (n + 1,), optional=True)
+    out_tokens = k_out.shape[0]
+    row_bytes, (ks, vs) = _kv_layout("", k_out, v_out, k_cache, v_cache, out_tokens)
+    if k_cache.shape[0] < int(num_blocks) * int(block_size):
+        raise ValueError("the caches hold fewer than num_blocks * block_size slots")
+    args = (n, _ptr(seq_lens), _ptr(input_block_tables), MB, int(block_size), int(num_blocks),
+            row_bytes, _ptr(k_cache), _ptr(v_cache), out_tokens, _ptr(k_out), ks, _ptr(v_out), vs,
+            _ptr(kv_start), _ptr(_status(status)))
+    return _prepared("gather_kv", _lib.pkv_gather_kv, args,
+                     (seq_lens, input_block_tables, k_cache, v_cache, k_out, v_out, kv_start,
+                      status))
 
 
 def _kv_layout(name_k, k, v, k_cache, v_cache, T):

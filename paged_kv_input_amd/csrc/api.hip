@@ -183,6 +183,34 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
     return from_hip(e);
 }
 
+int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
+                  int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
+                  const void* k_cache, const void* v_cache, int64_t out_tokens, void* k_out,
+                  int64_t k_out_stride, void* v_out, int64_t v_out_stride, int32_t* kv_start,
+                  uint32_t* status, void* stream)
+{
+    if (n < 0 || MB < 0 || block_size <= 0 || num_blocks < 0 || row_bytes <= 0 ||
+        out_tokens < 0 || k_out_stride < row_bytes || v_out_stride < row_bytes)
+        return PKV_EINVAL;
+    if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX + 1)
+        return PKV_EINVAL;
+    if (n > 0 && (seq_lens == nullptr || (MB > 0 && input_block_tables == nullptr)))
+        return PKV_EINVAL;
+    if (out_tokens > 0 && (k_out == nullptr || v_out == nullptr))
+        return PKV_EINVAL;
+    if (num_blocks > 0 && (k_cache == nullptr || v_cache == nullptr))
+        return PKV_EINVAL;
+    if ((row_bytes & 15) != 0 || (k_out_stride & 15) != 0 || (v_out_stride & 15) != 0 ||
+        !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_out) || !aligned16(v_out))
+        return PKV_EALIGN;
+    if (n > PKV_MAX_BATCH || out_tokens > INT32_MAX || row_bytes / 16 >= (int64_t)1 << 23)
+        return PKV_EUNSUPPORTED;
+    return from_hip(pkv::launch_gather(n, seq_lens, input_block_tables, MB, block_size, num_blocks,
+                                       row_bytes, k_cache, v_cache, (int32_t)out_tokens, k_out,
+                                       k_out_stride, v_out, v_out_stride, kv_start, status,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int pkv_add_requests(int32_t m, const int32_t* rows, const int32_t* num_computed,
                      const int32_t* prompt_start, const int32_t* prompt_tokens,
                      int32_t num_prompt_tokens, const int32_t* block_start, const int32_t* blocks,

@@ -1,0 +1,312 @@
+// gather.hip -- the paged K/V read: every position below seq_len, through the
+// visible pages, into one contiguous varlen array.
+//
+// Attention reads each request's KV range (seq_lens: history plus the new
+// tokens) through its visible pages (input_block_tables) by indirect
+// addressing ("Complete Input Preparation for the Attention Module" of "Deep
+// Dive into vLLM's Scheduling Mechanism: The Complete CPU-to-GPU Mapping
+// Pipeline", kongchang.com/en).  For position p of batch row b the address
+// chain of its "Multi-Layer Coordinate Conversion Pipeline" runs again: logical
+// block p / block_size, offset p % block_size, the physical block from the
+// visible pages, slot = block * block_size + offset.  The K and V rows at that
+// slot go to row kv_start[b] + p of the outputs, kv_start being the running sum
+// of the seq_lens.  It is the exact inverse of the scatter.
+//
+// Design (gfx950): a persistent grid, 256 threads per workgroup.  Every
+// workgroup first forms the running sum of the seq_lens in LDS (at most
+// PKV_MAX_BATCH values, 16 per thread, wave scans combined across the four
+// wavefronts).  Then, as in the fused step kernel, three copy wavefronts and
+// one index wavefront split the work: the index wavefront resolves the rows of
+// the next 256-row tile (owner by binary search in LDS, page lookup) while the
+// copy wavefronts move the current tile.  Here the loads depend on the slots
+// and the stores do not: the copy wavefronts read whole 16-byte chunks of the
+// cache rows at the tile's slots (consecutive positions of a page are
+// consecutive slots, so a page is one contiguous span) and write the output
+// rows in order.  The index wavefront's page loads never queue behind the
+// payload, since a wavefront's memory counter only covers its own accesses.
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#ifndef PKV_GATHER_UNROLL
+#define PKV_GATHER_UNROLL 6
+#endif
+#ifndef PKV_GATHER_WGS
+#define PKV_GATHER_WGS 2048                // persistent workgroups, at most
+#endif
+
+constexpr int kCopyWaves = 3;
+constexpr int kCopyThreads = kCopyWaves * kWave;
+constexpr int kThreads = kCopyThreads + kWave;
+constexpr int kUnroll = PKV_GATHER_UNROLL;
+constexpr int kChunks = kCopyThreads * kUnroll;     // 16-byte chunks per round
+constexpr int kTile = 256;                          // output rows per tile
+constexpr int kRowsPerLane = kTile / kWave;
+constexpr int kScanPer = PKV_MAX_BATCH / kThreads;  // seq_lens per thread in the scan
+
+struct GatherArgs {
+    const int32_t* seq_lens;
+    const int32_t* pages;            // input_block_tables [n, MB]
+    const u32x4* k_cache;
+    const u32x4* v_cache;
+    u32x4* k_out;
+    u32x4* v_out;
+    int32_t* kv_start;
+    uint32_t* status;
+    int64_t k_out_stride16;
+    int64_t v_out_stride16;
+    int32_t n;
+    int32_t MB;
+    int32_t block_size;
+    int32_t bs_shift;                // log2(block_size), or -1
+    int32_t num_blocks;
+    int32_t chunks_per_row;
+    int32_t row_shift;               // log2(chunks_per_row), or -1
+    int32_t rounds;                  // ceil(kTile * chunks_per_row / kChunks)
+    int32_t out_tokens;
+};
+
+__device__ inline u32x4 nt_load(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ inline void nt_store(u32x4 x, u32x4* p) { __builtin_nontemporal_store(x, p); }
+
+__device__ inline bool is_index_wave()
+{
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)) == kCopyWaves;
+}
+
+// Running sum of the seq_lens into s_start[0..n] (clamped to out_tokens: rows
+// at or past it are never written), by every thread of the workgroup.
+// Workgroup 0 also writes kv_start (saturated at INT32_MAX) and the flags of
+// the batch as a whole.
+__device__ inline void start_offsets(const GatherArgs& a, int32_t* s_start, int64_t* s_wave,
+                                     uint32_t& flags)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int i0 = tid * kScanPer;
+    int64_t v[kScanPer];
+    // Unconditional loads from clamped in-bounds addresses (n > 0 is uniform).
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+        const int i = i0 + k;
+        v[k] = a.n > 0 ? a.seq_lens[i < a.n ? i : a.n - 1] : 0;
+        if (i >= a.n)
+            v[k] = 0;
+    }
+    int64_t total = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+        if (v[k] < 0) {
+            flags |= PKV_ST_BAD_COUNT;
+            v[k] = 0;
+        }
+        total += v[k];
+    }
+    const int64_t incl = wave_inclusive_scan(total);
+    if (lane == kWave - 1)
+        s_wave[wave] = incl;
+    __syncthreads();
+    int64_t before = incl - total;
+    for (int w = 0; w < wave; ++w)
+        before += s_wave[w];
+    const bool first = blockIdx.x == 0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+        const int i = i0 + k;
+        if (i <= a.n) {            // i == n: the grand total
+            s_start[i] = (int32_t)(before < a.out_tokens ? before : a.out_tokens);
+            if (first && a.kv_start != nullptr)
+                a.kv_start[i] = (int32_t)(before < INT32_MAX ? before : INT32_MAX);
+        }
+        before += v[k];
+    }
+    if (i0 + kScanPer == PKV_MAX_BATCH && a.n == PKV_MAX_BATCH) {   // last thread, full batch
+        s_start[a.n] = (int32_t)(before < a.out_tokens ? before : a.out_tokens);
+        if (first && a.kv_start != nullptr)
+            a.kv_start[a.n] = (int32_t)(before < INT32_MAX ? before : INT32_MAX);
+    }
+    if (first && before > a.out_tokens && tid == kThreads - 1)
+        flags |= PKV_ST_TOKEN_SUM;
+    if (!first)
+        flags &= ~(uint32_t)PKV_ST_BAD_COUNT;    // batch-wide flags: workgroup 0 only
+}
+
+// Index wavefront: the source slot of each row of a tile, -1 where no page
+// can be read (flagged).  All of a lane's page loads are issued together.
+__device__ inline void tile_slots(const GatherArgs& a, const int32_t* s_start, int64_t u0,
+                                  int len, int32_t* s_slot, uint32_t& flags)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    int64_t src[kRowsPerLane];
+    int32_t off[kRowsPerLane];
+#pragma unroll
+    for (int k = 0; k < kRowsPerLane; ++k) {
+        const int j = k * kWave + lane;
+        src[k] = -1;
+        off[k] = 0;
+        if (j >= len)
+            continue;
+        const int64_t u = u0 + j;
+        const int b = owner_of(s_start, a.n, u);      // in [0, n): u < s_start[n]
+        const int32_t p = (int32_t)(u - s_start[b]);
+        const int32_t lb = a.bs_shift >= 0 ? (p >> a.bs_shift) : p / a.block_size;
+        off[k] = p - lb * a.block_size;
+        if (lb >= a.MB)
+            flags |= PKV_ST_LB_OOR;
+        else
+            src[k] = (int64_t)b * a.MB + lb;
+    }
+    const bool have_pages = a.MB > 0;                 // uniform
+    int32_t blk[kRowsPerLane];
+#pragma unroll
+    for (int k = 0; k < kRowsPerLane; ++k) {
+        blk[k] = have_pages ? a.pages[src[k] >= 0 ? src[k] : 0] : -1;
+        if (src[k] < 0)
+            blk[k] = -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerLane; ++k) {
+        const int j = k * kWave + lane;
+        if (j >= len)
+            continue;
+        int32_t slot = -1;
+        if (src[k] >= 0) {
+            if (blk[k] < 0 || blk[k] >= a.num_blocks)
+                flags |= PKV_ST_BLOCK_OOR;
+            else
+                slot = blk[k] * a.block_size + off[k];
+        }
+        s_slot[j] = slot;
+    }
+}
+
+template <bool kPow2Row>
+__device__ inline void copy_tile(const GatherArgs& a, const int32_t* s_slot, int64_t u0, int len)
+{
+    const int tid = threadIdx.x;
+    const bool have_cache = a.num_blocks > 0;         // uniform
+    u32x4* kb = a.k_out + u0 * a.k_out_stride16;
+    u32x4* vb = a.v_out + u0 * a.v_out_stride16;
+    for (int r = 0; r < a.rounds; ++r) {
+        u32x4 kv[kUnroll];
+        u32x4 vv[kUnroll];
+        int32_t slot[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int idx = r * kChunks + u * kCopyThreads + tid;
+            int tok = kPow2Row ? (idx >> a.row_shift) : idx / a.chunks_per_row;
+            const int c = idx - tok * a.chunks_per_row;
+            slot[u] = tok < len ? s_slot[tok] : -1;
+            const int64_t s = (int64_t)(slot[u] >= 0 ? slot[u] : 0) * a.chunks_per_row + c;
+            if (have_cache) {
+                kv[u] = nt_load(a.k_cache + s);
+                vv[u] = nt_load(a.v_cache + s);
+            } else {
+                kv[u] = u32x4{0, 0, 0, 0};
+                vv[u] = kv[u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            __asm__ volatile("" : "+v"(kv[u]), "+v"(vv[u]));
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (slot[u] < 0)
+                continue;
+            const int idx = r * kChunks + u * kCopyThreads + tid;
+            const int tok = kPow2Row ? (idx >> a.row_shift) : idx / a.chunks_per_row;
+            const int c = idx - tok * a.chunks_per_row;
+            nt_store(kv[u], kb + (int64_t)tok * a.k_out_stride16 + c);
+            nt_store(vv[u], vb + (int64_t)tok * a.v_out_stride16 + c);
+        }
+    }
+}
+
+template <bool kPow2Row>
+__global__ __launch_bounds__(kThreads) void k_gather(const GatherArgs a)
+{
+    __shared__ int32_t s_start[PKV_MAX_BATCH + 1];
+    __shared__ int64_t s_wave[kThreads / kWave];
+    __shared__ int32_t s_slot[2 * kTile];
+
+    uint32_t flags = 0;
+    start_offsets(a, s_start, s_wave, flags);
+    __syncthreads();
+    const int64_t rows = s_start[a.n];                   // rows to write (uniform)
+    const int64_t tiles = (rows + kTile - 1) / kTile;
+    const int64_t G = gridDim.x;
+    auto tile_len = [&](int64_t t) {
+        const int64_t u0 = t * kTile;
+        return (int)(rows - u0 < kTile ? rows - u0 : kTile);
+    };
+    // Barriers per role: one after the first tile's slots, then one per tile.
+    int buf = 0;
+    if (is_index_wave()) {
+        int64_t tile = blockIdx.x;
+        if (tile < tiles)
+            tile_slots(a, s_start, tile * kTile, tile_len(tile), s_slot, flags);
+        __syncthreads();
+        for (; tile < tiles; tile += G) {
+            const int64_t next = tile + G;
+            if (next < tiles)
+                tile_slots(a, s_start, next * kTile, tile_len(next), s_slot + (buf ^ 1) * kTile,
+                           flags);
+            __syncthreads();
+            buf ^= 1;
+        }
+    } else {
+        __syncthreads();
+        for (int64_t tile = blockIdx.x; tile < tiles; tile += G) {
+            copy_tile<kPow2Row>(a, s_slot + buf * kTile, tile * kTile, tile_len(tile));
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+    report_status(a.status, flags);
+}
+
+}  // namespace
+
+hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
+                         int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
+                         const void* k_cache, const void* v_cache, int32_t out_tokens,
+                         void* k_out, int64_t k_out_stride, void* v_out, int64_t v_out_stride,
+                         int32_t* kv_start, uint32_t* status, hipStream_t stream)
+{
+    if (n == 0 && kv_start == nullptr)
+        return hipSuccess;
+    GatherArgs a;
+    a.seq_lens = seq_lens;
+    a.pages = input_block_tables;
+    a.k_cache = static_cast<const u32x4*>(k_cache);
+    a.v_cache = static_cast<const u32x4*>(v_cache);
+    a.k_out = static_cast<u32x4*>(k_out);
+    a.v_out = static_cast<u32x4*>(v_out);
+    a.kv_start = kv_start;
+    a.status = status;
+    a.k_out_stride16 = k_out_stride / 16;
+    a.v_out_stride16 = v_out_stride / 16;
+    a.n = n;
+    a.MB = MB;
+    a.block_size = block_size;
+    a.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
+    a.num_blocks = num_blocks;
+    a.chunks_per_row = (int32_t)(row_bytes / 16);
+    a.row_shift = (a.chunks_per_row & (a.chunks_per_row - 1)) == 0
+                      ? __builtin_ctz((unsigned)a.chunks_per_row) : -1;
+    a.rounds = (int32_t)(((int64_t)kTile * a.chunks_per_row + kChunks - 1) / kChunks);
+    a.out_tokens = out_tokens;
+    const int64_t tiles = ((int64_t)out_tokens + kTile - 1) / kTile;
+    const int64_t grid = tiles < 1 ? 1 : (tiles < PKV_GATHER_WGS ? tiles : PKV_GATHER_WGS);
+    if (a.row_shift >= 0)
+        k_gather<true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(a);
+    else
+        k_gather<false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

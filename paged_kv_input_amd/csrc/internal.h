@@ -497,6 +497,12 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
 // Work-items of the grid launch_step would launch.
 int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
 
+hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
+                         int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
+                         const void* k_cache, const void* v_cache, int32_t out_tokens,
+                         void* k_out, int64_t k_out_stride, void* v_out, int64_t v_out_stride,
+                         int32_t* kv_start, uint32_t* status, hipStream_t stream);
+
 hipError_t launch_add_requests(int32_t m, const int32_t* rows, const int32_t* num_computed,
                                const int32_t* prompt_start, const int32_t* prompt_tokens,
                                int32_t num_prompt_tokens, const int32_t* block_start,

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["pkv_abi_version", "pkv_add_requests", "pkv_advance_state",
                      "pkv_append_blocks", "pkv_compute_slot_mapping", "pkv_error_string",
-                     "pkv_prepare_batch", "pkv_row_pool_acquire", "pkv_row_pool_create",
+                     "pkv_gather_kv", "pkv_prepare_batch", "pkv_row_pool_acquire", "pkv_row_pool_create",
                      "pkv_row_pool_destroy", "pkv_row_pool_num_free", "pkv_row_pool_release",
                      "pkv_scatter_kv", "pkv_step"]
     for name in names:
@@ -121,6 +121,36 @@ def test_step_host_argument_errors(lib):
     args[0] = 4097
     arr[0].row_bytes = 16
     assert st(*args, 1, arr, None, None) == -3           # beyond PKV_MAX_BATCH
+
+
+def test_gather_host_argument_errors(lib):
+    N = None
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    g = lib.pkv_gather_kv
+    ok = [2, fake, fake, 4, 16, 8, 256, fake, fake, 64, fake, 256, fake, 256, N, N, N]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return g(*a)
+
+    assert call(a0=-1) == -1                       # n < 0
+    assert call(a4=0) == -1                        # block_size <= 0
+    assert call(a6=0) == -1                        # row_bytes <= 0
+    assert call(a9=-1) == -1                       # out_tokens < 0
+    assert call(a11=128) == -1                     # k_out stride < row_bytes
+    assert call(a5=1 << 27, a4=32) == -1           # num_blocks * block_size > 2^31
+    assert call(a1=N) == -1                        # seq_lens NULL
+    assert call(a2=N) == -1                        # pages NULL with MB > 0
+    assert call(a10=N) == -1                       # k_out NULL
+    assert call(a7=N) == -1                        # cache NULL
+    assert call(a6=24, a11=32, a13=32) == -2       # row not a multiple of 16
+    assert call(a10=P(0x1008)) == -2               # misaligned output
+    assert call(a0=4097) == -3                     # beyond PKV_MAX_BATCH
+    assert call(a9=1 << 31) == -3                  # out_tokens > INT32_MAX
+    assert call(a0=0, a1=N, a2=N, a14=N) == 0      # nothing to do: nothing enqueued
 
 
 def test_state_host_argument_errors(lib):

@@ -327,3 +327,38 @@ def test_device_serving_loop_with_row_pool():
     assert_equal("k_cache", caches[0][0].cpu().numpy().view(np.uint16), kc_o)
     assert_equal("v_cache", caches[0][1].cpu().numpy().view(np.uint16), vc_o)
     assert recycled > 0, "no row was recycled: the loop is too short"
+
+
+def test_second_group_registration():
+    """A second KV-cache group: the same requests registered again with that
+    group's block table and empty prompts leaves the tokens alone."""
+    import torch
+
+    rng = np.random.default_rng(77)
+    R, L = 16, 200
+    ds, st = new_state(R, L, 12)
+    rows = rng.choice(R, 6, replace=False).tolist()
+    done = rng.integers(0, 100, 6).tolist()
+    prompts = [rng.integers(0, 1000, int(rng.integers(1, 200))).tolist() for _ in rows]
+    ds.add_requests(rows, done, prompts, [[1, 2]] * 6)
+    oracle.add_requests(st, rows, done, prompts, [[1, 2]] * 6)
+    # group 1: its own table (width 5) and block counts
+    bt1 = torch.full((R, 5), -1, dtype=torch.int32, device=ds.device)
+    rb1 = torch.zeros(R, dtype=torch.int32, device=ds.device)
+    st1 = {"completed": st["completed"], "token_ids": st["token_ids"],
+           "block_table": np.full((R, 5), -1, np.int32), "row_blocks": np.zeros(R, np.int32)}
+    blocks1 = [rng.integers(0, 50, int(rng.integers(0, 6))).tolist() for _ in rows]
+    from paged_kv_input_amd import api
+    from paged_kv_input_amd.state import pack_csr
+
+    ps, pt, _ = pack_csr([[] for _ in rows])
+    bs_, bl, bt = pack_csr(blocks1)
+    up = ds._up
+    api.add_requests(up(rows), up(done), up(ps), up(pt)[:0], up(bs_), up(bl)[:bt],
+                     completed=ds.completed, token_ids=ds.token_ids, block_table=bt1,
+                     row_blocks=rb1, status=ds.status)
+    rc, want = oracle.add_requests(st1, rows, done, [[] for _ in rows], blocks1)
+    assert rc == 0 and take_status(ds) == want
+    compare_state(ds, st, "group 0 after group 1's registration")
+    assert_equal("group 1 block_table", bt1.cpu().numpy(), st1["block_table"])
+    assert_equal("group 1 row_blocks", rb1.cpu().numpy(), st1["row_blocks"])
