@@ -17,8 +17,9 @@
 // PKV_MAX_BATCH values, 16 per thread, wave scans combined across the four
 // wavefronts).  Then, as in the fused step kernel, three copy wavefronts and
 // one index wavefront split the work: the index wavefront resolves the rows of
-// the next 256-row tile (owner by binary search in LDS, page lookup) while the
-// copy wavefronts move the current tile.  Here the loads depend on the slots
+// the next tile of at most 256 rows (owner by binary search in LDS, page
+// lookup) while the copy wavefronts move the current tile.  Tiles are
+// shortened for short reads, so that even those spread over the whole chip.  Here the loads depend on the slots
 // and the stores do not: the copy wavefronts read whole 16-byte chunks of the
 // cache rows at the tile's slots (consecutive positions of a page are
 // consecutive slots, so a page is one contiguous span) and write the output
@@ -35,7 +36,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define PKV_GATHER_UNROLL 6
 #endif
 #ifndef PKV_GATHER_WGS
-#define PKV_GATHER_WGS 2048                // persistent workgroups, at most
+#define PKV_GATHER_WGS 1024                // persistent workgroups, at most
+#endif
+#ifndef PKV_GATHER_TARGET_TILES
+#define PKV_GATHER_TARGET_TILES 2048       // tiles are shortened until there are this many
+#endif
+#ifndef PKV_GATHER_MIN_TILE
+#define PKV_GATHER_MIN_TILE 16
+#endif
+#ifndef PKV_GATHER_PIPE
+#define PKV_GATHER_PIPE 0                  // 1: next round's loads issued before this round's stores
 #endif
 
 constexpr int kCopyWaves = 3;
@@ -43,7 +53,7 @@ constexpr int kCopyThreads = kCopyWaves * kWave;
 constexpr int kThreads = kCopyThreads + kWave;
 constexpr int kUnroll = PKV_GATHER_UNROLL;
 constexpr int kChunks = kCopyThreads * kUnroll;     // 16-byte chunks per round
-constexpr int kTile = 256;                          // output rows per tile
+constexpr int kTile = 256;                          // output rows per tile, at most
 constexpr int kRowsPerLane = kTile / kWave;
 constexpr int kScanPer = PKV_MAX_BATCH / kThreads;  // seq_lens per thread in the scan
 
@@ -65,7 +75,7 @@ struct GatherArgs {
     int32_t num_blocks;
     int32_t chunks_per_row;
     int32_t row_shift;               // log2(chunks_per_row), or -1
-    int32_t rounds;                  // ceil(kTile * chunks_per_row / kChunks)
+    int32_t tile;                    // output rows per tile (a power of two <= kTile)
     int32_t out_tokens;
 };
 
@@ -184,46 +194,93 @@ __device__ inline void tile_slots(const GatherArgs& a, const int32_t* s_start, i
     }
 }
 
+// Chunk u of round r: its row within the tile, its 16-byte chunk within the
+// row, the source slot (-1: nothing to copy) and the cache chunk to load (the
+// first chunk of slot 0 when there is nothing to copy, so the load needs no
+// branch).
+template <bool kPow2Row>
+__device__ inline void chunk_at(const GatherArgs& a, const int32_t* s_slot, int len, int r, int u,
+                                int& tok, int& c, int32_t& slot, int64_t& src)
+{
+    const int idx = r * kChunks + u * kCopyThreads + (int)threadIdx.x;
+    tok = kPow2Row ? (idx >> a.row_shift) : idx / a.chunks_per_row;
+    c = idx - tok * a.chunks_per_row;
+    slot = tok < len ? s_slot[tok] : -1;
+    src = (int64_t)(slot >= 0 ? slot : 0) * a.chunks_per_row + c;
+}
+
+template <bool kPow2Row>
+__device__ inline void load_round(const GatherArgs& a, const int32_t* s_slot, int len, int r,
+                                  u32x4 (&kv)[kUnroll], u32x4 (&vv)[kUnroll])
+{
+    const bool have_cache = a.num_blocks > 0;         // uniform
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        int tok, c;
+        int32_t slot;
+        int64_t src;
+        chunk_at<kPow2Row>(a, s_slot, len, r, u, tok, c, slot, src);
+        if (have_cache) {
+            kv[u] = nt_load(a.k_cache + src);
+            vv[u] = nt_load(a.v_cache + src);
+        } else {
+            kv[u] = u32x4{0, 0, 0, 0};
+            vv[u] = kv[u];
+        }
+    }
+}
+
+template <bool kPow2Row>
+__device__ inline void store_round(const GatherArgs& a, const int32_t* s_slot, int len, int r,
+                                   u32x4* kb, u32x4* vb, u32x4 (&kv)[kUnroll],
+                                   u32x4 (&vv)[kUnroll])
+{
+    // Keep the payload in registers here, so the loads are not sunk into the
+    // store branches below.
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+        __asm__ volatile("" : "+v"(kv[u]), "+v"(vv[u]));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        int tok, c;
+        int32_t slot;
+        int64_t src;
+        chunk_at<kPow2Row>(a, s_slot, len, r, u, tok, c, slot, src);
+        if (slot < 0)
+            continue;
+        nt_store(kv[u], kb + (int64_t)tok * a.k_out_stride16 + c);
+        nt_store(vv[u], vb + (int64_t)tok * a.v_out_stride16 + c);
+    }
+}
+
 template <bool kPow2Row>
 __device__ inline void copy_tile(const GatherArgs& a, const int32_t* s_slot, int64_t u0, int len)
 {
-    const int tid = threadIdx.x;
-    const bool have_cache = a.num_blocks > 0;         // uniform
     u32x4* kb = a.k_out + u0 * a.k_out_stride16;
     u32x4* vb = a.v_out + u0 * a.v_out_stride16;
-    for (int r = 0; r < a.rounds; ++r) {
+    const int rounds = (int)(((int64_t)len * a.chunks_per_row + kChunks - 1) / kChunks);
+#if PKV_GATHER_PIPE
+    // Two rounds in flight: a round's stores go out behind the next round's
+    // loads, so waiting for those loads does not also wait for the stores.
+    u32x4 ka[kUnroll], va[kUnroll], kn[kUnroll], vn[kUnroll];
+    load_round<kPow2Row>(a, s_slot, len, 0, ka, va);
+    for (int r = 0; r < rounds; r += 2) {
+        if (r + 1 < rounds)
+            load_round<kPow2Row>(a, s_slot, len, r + 1, kn, vn);
+        store_round<kPow2Row>(a, s_slot, len, r, kb, vb, ka, va);
+        if (r + 2 < rounds)
+            load_round<kPow2Row>(a, s_slot, len, r + 2, ka, va);
+        if (r + 1 < rounds)
+            store_round<kPow2Row>(a, s_slot, len, r + 1, kb, vb, kn, vn);
+    }
+#else
+    for (int r = 0; r < rounds; ++r) {
         u32x4 kv[kUnroll];
         u32x4 vv[kUnroll];
-        int32_t slot[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int idx = r * kChunks + u * kCopyThreads + tid;
-            int tok = kPow2Row ? (idx >> a.row_shift) : idx / a.chunks_per_row;
-            const int c = idx - tok * a.chunks_per_row;
-            slot[u] = tok < len ? s_slot[tok] : -1;
-            const int64_t s = (int64_t)(slot[u] >= 0 ? slot[u] : 0) * a.chunks_per_row + c;
-            if (have_cache) {
-                kv[u] = nt_load(a.k_cache + s);
-                vv[u] = nt_load(a.v_cache + s);
-            } else {
-                kv[u] = u32x4{0, 0, 0, 0};
-                vv[u] = kv[u];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            __asm__ volatile("" : "+v"(kv[u]), "+v"(vv[u]));
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (slot[u] < 0)
-                continue;
-            const int idx = r * kChunks + u * kCopyThreads + tid;
-            const int tok = kPow2Row ? (idx >> a.row_shift) : idx / a.chunks_per_row;
-            const int c = idx - tok * a.chunks_per_row;
-            nt_store(kv[u], kb + (int64_t)tok * a.k_out_stride16 + c);
-            nt_store(vv[u], vb + (int64_t)tok * a.v_out_stride16 + c);
-        }
+        load_round<kPow2Row>(a, s_slot, len, r, kv, vv);
+        store_round<kPow2Row>(a, s_slot, len, r, kb, vb, kv, vv);
     }
+#endif
 }
 
 template <bool kPow2Row>
@@ -237,23 +294,23 @@ __global__ __launch_bounds__(kThreads) void k_gather(const GatherArgs a)
     start_offsets(a, s_start, s_wave, flags);
     __syncthreads();
     const int64_t rows = s_start[a.n];                   // rows to write (uniform)
-    const int64_t tiles = (rows + kTile - 1) / kTile;
+    const int64_t tiles = (rows + a.tile - 1) / a.tile;
     const int64_t G = gridDim.x;
     auto tile_len = [&](int64_t t) {
-        const int64_t u0 = t * kTile;
-        return (int)(rows - u0 < kTile ? rows - u0 : kTile);
+        const int64_t u0 = t * a.tile;
+        return (int)(rows - u0 < a.tile ? rows - u0 : a.tile);
     };
     // Barriers per role: one after the first tile's slots, then one per tile.
     int buf = 0;
     if (is_index_wave()) {
         int64_t tile = blockIdx.x;
         if (tile < tiles)
-            tile_slots(a, s_start, tile * kTile, tile_len(tile), s_slot, flags);
+            tile_slots(a, s_start, tile * a.tile, tile_len(tile), s_slot, flags);
         __syncthreads();
         for (; tile < tiles; tile += G) {
             const int64_t next = tile + G;
             if (next < tiles)
-                tile_slots(a, s_start, next * kTile, tile_len(next), s_slot + (buf ^ 1) * kTile,
+                tile_slots(a, s_start, next * a.tile, tile_len(next), s_slot + (buf ^ 1) * kTile,
                            flags);
             __syncthreads();
             buf ^= 1;
@@ -261,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void k_gather(const GatherArgs a)
     } else {
         __syncthreads();
         for (int64_t tile = blockIdx.x; tile < tiles; tile += G) {
-            copy_tile<kPow2Row>(a, s_slot + buf * kTile, tile * kTile, tile_len(tile));
+            copy_tile<kPow2Row>(a, s_slot + buf * kTile, tile * a.tile, tile_len(tile));
             __syncthreads();
             buf ^= 1;
         }
@@ -298,9 +355,15 @@ hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* inpu
     a.chunks_per_row = (int32_t)(row_bytes / 16);
     a.row_shift = (a.chunks_per_row & (a.chunks_per_row - 1)) == 0
                       ? __builtin_ctz((unsigned)a.chunks_per_row) : -1;
-    a.rounds = (int32_t)(((int64_t)kTile * a.chunks_per_row + kChunks - 1) / kChunks);
+    // Tiles as long as kTile rows, shortened (by halves, down to a minimum)
+    // while the output has fewer than PKV_GATHER_TARGET_TILES of them, so a
+    // short read still spreads over the whole chip.
+    a.tile = kTile;
+    while (a.tile > PKV_GATHER_MIN_TILE &&
+           ((int64_t)out_tokens + a.tile - 1) / a.tile < PKV_GATHER_TARGET_TILES)
+        a.tile >>= 1;
     a.out_tokens = out_tokens;
-    const int64_t tiles = ((int64_t)out_tokens + kTile - 1) / kTile;
+    const int64_t tiles = ((int64_t)out_tokens + a.tile - 1) / a.tile;
     const int64_t grid = tiles < 1 ? 1 : (tiles < PKV_GATHER_WGS ? tiles : PKV_GATHER_WGS);
     if (a.row_shift >= 0)
         k_gather<true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(a);
