@@ -111,7 +111,8 @@ def source_digest(paths):
 
 def kernel_sources(kernel):
     csrc = os.path.join(ROOT, "paged_kv_input_amd", "csrc")
-    files = {"step": ["step.hip", "internal.h"], "scatter_kv": ["scatter.hip", "internal.h"]}
+    files = {"step": ["step.hip", "internal.h"], "scatter_kv": ["scatter.hip", "internal.h"],
+             "gather_kv": ["gather.hip", "internal.h"]}
     return [os.path.join(csrc, f) for f in files[kernel]]
 
 
@@ -227,7 +228,7 @@ def state_calls(batch, step, steps, warmup, stream):
     return out
 
 
-def gather_calls(batch, steps_dev, steps, warmup, stream):
+def gather_calls(batch, steps_dev, steps, warmup, stream, workload):
     """The paged K/V read on this batch's shape: after the step, every group's
     KV range of every request (history plus new tokens) read through its
     visible pages into a contiguous varlen array; rotating over the same
@@ -275,7 +276,8 @@ def gather_calls(batch, steps_dev, steps, warmup, stream):
     return {"ms": ms, "kv_rows": statistics.fmean(rows), "algorithmic_bytes": nbytes,
             "gbs": nbytes / (ms * 1e-3) / 1e9,
             "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bound": "hbm",
-            "launches_per_step": len(batch.groups)}
+            "kernel": "pkv_gather_kv (k_gather)", "launches_per_step": len(batch.groups),
+            "traffic_per_launch": traffic_from_profile("gather_kv", workload)}
 
 
 def main():
@@ -384,7 +386,7 @@ def main():
         if s.status_bits() != 0:
             raise RuntimeError(f"device status bits set: {s.status_bits():#x}")
     state = state_calls(batch, steps[0], args.steps, args.warmup, stream)
-    gather = gather_calls(batch, steps, args.steps, args.warmup, stream)
+    gather = gather_calls(batch, steps, args.steps, args.warmup, stream, args.workload)
 
     ab = algorithmic_bytes(batch)
     cb = call_bytes(batch)

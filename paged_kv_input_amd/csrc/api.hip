@@ -3,7 +3,7 @@
 // (layouts, outputs, error behaviour) is stated in include/pagedkv.h.
 #include <stdint.h>
 
-#include "internal.h"
+#include "launchers.h"
 
 namespace {
 

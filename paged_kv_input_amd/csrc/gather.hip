@@ -26,6 +26,7 @@
 // rows in order.  The index wavefront's page loads never queue behind the
 // payload, since a wavefront's memory counter only covers its own accesses.
 #include "internal.h"
+#include "launchers.h"
 
 namespace pkv {
 namespace {

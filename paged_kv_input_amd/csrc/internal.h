@@ -1,5 +1,6 @@
-// internal.h -- device helpers and launcher declarations shared by the HIP
-// sources of libpagedkv (gfx950, wave64).  Not part of the public ABI.
+// internal.h -- device helpers shared by the HIP kernels of libpagedkv
+// (gfx950, wave64).  Not part of the public ABI; the host-side launchers are
+// declared in launchers.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -470,60 +471,5 @@ __device__ inline int64_t xcd_tile(int64_t blk, int64_t tiles)
     return blk;
 #endif
 }
-
-// Launchers (host side).  Arguments are already validated; each returns a
-// hipError_t from the launch.
-hipError_t launch_prepare(int32_t n, int32_t T, const int32_t* sched_rows,
-                          const int32_t* num_scheduled, const int32_t* completed, int32_t R,
-                          const int32_t* token_ids, int64_t token_stride, int32_t L,
-                          int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
-                          int32_t* positions, int32_t* input_ids, uint32_t* status,
-                          hipStream_t stream);
-
-hipError_t launch_slots(int32_t n, int32_t T, const int32_t* index_mapping,
-                        const int32_t* query_start_loc, const int32_t* seq_lens,
-                        const int32_t* positions, const int32_t* block_table, int32_t R,
-                        int32_t MB, int32_t block_size, int32_t num_blocks,
-                        int32_t* slot_mapping, int32_t* input_block_tables, uint32_t* status,
-                        hipStream_t stream);
-
-hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
-                       const int32_t* num_scheduled, const int32_t* completed, int32_t R,
-                       const int32_t* token_ids, int64_t token_stride, int32_t L,
-                       int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
-                       int32_t* positions, int32_t* input_ids, int32_t num_groups,
-                       const pkv_group* groups, uint32_t* status, hipStream_t stream);
-
-// Work-items of the grid launch_step would launch.
-int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
-
-hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
-                         int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
-                         const void* k_cache, const void* v_cache, int32_t out_tokens,
-                         void* k_out, int64_t k_out_stride, void* v_out, int64_t v_out_stride,
-                         int32_t* kv_start, uint32_t* status, hipStream_t stream);
-
-hipError_t launch_add_requests(int32_t m, const int32_t* rows, const int32_t* num_computed,
-                               const int32_t* prompt_start, const int32_t* prompt_tokens,
-                               int32_t num_prompt_tokens, const int32_t* block_start,
-                               const int32_t* blocks, int32_t num_blocks_given, int32_t R,
-                               int32_t* completed, int32_t* token_ids, int64_t token_stride,
-                               int32_t L, int32_t* block_table, int32_t MB, int32_t* row_blocks,
-                               uint32_t* status, hipStream_t stream);
-
-hipError_t launch_append_blocks(int32_t m, const int32_t* rows, const int32_t* block_start,
-                                const int32_t* blocks, int32_t num_blocks_given, int32_t R,
-                                int32_t* block_table, int32_t MB, int32_t* row_blocks,
-                                uint32_t* status, hipStream_t stream);
-
-hipError_t launch_advance_state(int32_t n, const int32_t* index_mapping, const int32_t* seq_lens,
-                                const int32_t* sampled, int32_t R, int32_t* completed,
-                                int32_t* token_ids, int64_t token_stride, int32_t L,
-                                uint32_t* status, hipStream_t stream);
-
-hipError_t launch_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride,
-                          const void* v, int64_t v_stride, void* k_cache, void* v_cache,
-                          int64_t num_slots, const int32_t* slot_mapping, uint32_t* status,
-                          hipStream_t stream);
 
 }  // namespace pkv

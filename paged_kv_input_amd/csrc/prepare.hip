@@ -17,6 +17,7 @@
 // that would otherwise need a second launch or a device-side counter.
 // Workgroup 0 alone writes the per-request outputs and the per-request flags.
 #include "internal.h"
+#include "launchers.h"
 
 namespace pkv {
 namespace {

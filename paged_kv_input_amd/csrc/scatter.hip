@@ -14,6 +14,7 @@
 // token is shared by its lanes.  Loads and stores are non-temporal: the
 // payload is touched once and the cache rows are not read back by this step.
 #include "internal.h"
+#include "launchers.h"
 
 namespace pkv {
 namespace {

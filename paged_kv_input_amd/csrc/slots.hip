@@ -16,6 +16,7 @@
 // handful of lines per wave).  Page workgroups copy the visible prefix of one
 // block-table row per wavefront.  Power-of-two block sizes use shift and mask.
 #include "internal.h"
+#include "launchers.h"
 
 namespace pkv {
 namespace {

@@ -18,6 +18,7 @@
 // other workgroup touches the row, so the count cannot race); advance_state
 // takes one lane per batch row.
 #include "internal.h"
+#include "launchers.h"
 
 namespace pkv {
 namespace {

@@ -24,6 +24,7 @@
 // positions and input ids; extra workgroups per group copy the visible
 // block-table prefixes (one wavefront per batch row).
 #include "internal.h"
+#include "launchers.h"
 
 namespace pkv {
 namespace {
