@@ -33,6 +33,8 @@ EINVAL = -1
 ENOROWS = -5
 ST_BAD_ROW, ST_BAD_COUNT, ST_TOKEN_SUM, ST_POS_OOR = 0x01, 0x02, 0x04, 0x08
 ST_LB_OOR, ST_BLOCK_OOR, ST_SLOT_OOR, ST_BAD_RANGE = 0x10, 0x20, 0x40, 0x80
+ST_TABLE_FULL = 0x100
+NO_BLOCK = 2**31 - 1          # prefix index: an entry without a block
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -67,6 +69,16 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_gather_kv.restype = ctypes.c_int
     lib.orc_gather_kv.argtypes = [_I32, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P, _I64,
                                   _P, _I64, _P, _P]
+    lib.orc_fnv1a64.restype = ctypes.c_uint64
+    lib.orc_fnv1a64.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+    lib.orc_hash_blocks.restype = ctypes.c_int
+    lib.orc_hash_blocks.argtypes = [_I32, _P, _I64, _P, _P, _I32, _I32, _P, _P, _P]
+    lib.orc_prefix_lookup.restype = ctypes.c_int
+    lib.orc_prefix_lookup.argtypes = [_I32, _P, _I32, _P, _I32, _P, _P, _I64, _P, _P, _P]
+    lib.orc_prefix_insert.restype = ctypes.c_int
+    lib.orc_prefix_insert.argtypes = [_I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I64, _P]
+    lib.orc_prefix_evict.restype = ctypes.c_int
+    lib.orc_prefix_evict.argtypes = [_I32, _P, _P, _P, _P, _I64]
     for name in ("orc_pool_acquire", "orc_pool_release"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = [_I32, _P, _P, _P, _I32, _P]
@@ -250,8 +262,10 @@ def add_requests(state, rows, num_computed, prompts, blocks, *, lib=None):
     bs_, bl, btot = blocks if isinstance(blocks, tuple) else csr(blocks)
     tok, bt = state["token_ids"], state["block_table"]
     st = np.zeros(1, np.uint32)
-    rc = lib.orc_add_requests(rows.size, _ptr(rows), _ptr(nc), _ptr(_i32(ps)), _ptr(_i32(pt)),
-                              ptot, _ptr(_i32(bs_)), _ptr(_i32(bl)), btot,
+    # every array passed by address is held in a local for the whole call
+    ps, pt, bs_, bl = _i32(ps), _i32(pt), _i32(bs_), _i32(bl)
+    rc = lib.orc_add_requests(rows.size, _ptr(rows), _ptr(nc), _ptr(ps), _ptr(pt),
+                              ptot, _ptr(bs_), _ptr(bl), btot,
                               state["completed"].size, _ptr(state["completed"]),
                               _ptr(tok), tok.strides[0] // 4, tok.shape[1], _ptr(bt), bt.shape[1],
                               _ptr(state["row_blocks"]), _ptr(st))
@@ -265,7 +279,8 @@ def append_blocks(state, rows, blocks, *, lib=None):
     bs_, bl, btot = blocks if isinstance(blocks, tuple) else csr(blocks)
     bt = state["block_table"]
     st = np.zeros(1, np.uint32)
-    rc = lib.orc_append_blocks(rows.size, _ptr(rows), _ptr(_i32(bs_)), _ptr(_i32(bl)), btot,
+    bs_, bl = _i32(bs_), _i32(bl)
+    rc = lib.orc_append_blocks(rows.size, _ptr(rows), _ptr(bs_), _ptr(bl), btot,
                                bt.shape[0], _ptr(bt), bt.shape[1], _ptr(state["row_blocks"]),
                                _ptr(st))
     return int(rc), int(st[0])
@@ -320,3 +335,93 @@ class RowPool:
     @property
     def free(self):
         return int(self.num_free[0])
+
+
+# ---------------------------------------------------------------------------
+# prefix-cache block hashes and the prefix index
+# ---------------------------------------------------------------------------
+
+def hash_blocks(token_lists=None, block_size=16, MB=None, *, views=None, lib=None):
+    """Hashes of every full block of each token list (see orc_hash_blocks).
+    token_lists: list of int sequences, or views=(tokens flat, total, starts
+    int64 [m], lengths int32 [m]).  Returns dict(hashes uint64 [m, MB] (0
+    where not written), num_full [m], status, rc)."""
+    lib = lib or load()
+    if views is None:
+        lens = [len(t) for t in token_lists]
+        starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64) if lens else \
+            np.zeros(0, np.int64)
+        flat = np.array([x for t in token_lists for x in t], np.int32)
+        total = int(flat.size)
+        lengths = np.asarray(lens, np.int32)
+        if MB is None:
+            MB = max([l // block_size for l in lens] + [0])
+    else:
+        flat, total, starts, lengths = views
+        flat = _i32(flat)
+        starts = np.ascontiguousarray(starts, np.int64)
+        lengths = _i32(lengths)
+    if flat.size == 0:
+        flat = np.zeros(1, np.int32)
+    m = lengths.size
+    out = np.zeros((m, MB), np.uint64)
+    nf = np.full(m, -7, np.int32)
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_hash_blocks(m, _ptr(flat), total, _ptr(starts), _ptr(lengths), block_size, MB,
+                             _ptr(out), _ptr(nf), _ptr(st))
+    return {"hashes": out, "num_full": nf, "status": int(st[0]), "rc": int(rc)}
+
+
+def fnv1a64(data: bytes, *, lib=None) -> int:
+    """The oracle's FNV-1a 64-bit hash of a byte string."""
+    lib = lib or load()
+    return int(lib.orc_fnv1a64(data, len(data)))
+
+
+class PrefixIndex:
+    """The oracle's prefix index: hash -> smallest registered block id, with
+    room for ``capacity`` distinct hashes (see orc_prefix_*)."""
+
+    def __init__(self, capacity, *, lib=None):
+        self.lib = lib or load()
+        self.capacity = int(capacity)
+        self.keys = np.zeros(max(self.capacity, 1), np.uint64)
+        self.vals = np.full(max(self.capacity, 1), NO_BLOCK, np.int32)
+
+    def lookup(self, hashes, lengths, block_size):
+        h = np.ascontiguousarray(hashes, np.uint64)
+        m, MB = h.shape
+        ln = _i32(lengths)
+        hit = np.full((m, MB), -7, np.int32)
+        nc = np.full(m, -7, np.int32)
+        st = np.zeros(1, np.uint32)
+        rc = self.lib.orc_prefix_lookup(m, _ptr(h), MB, _ptr(ln), block_size, _ptr(self.keys),
+                                        _ptr(self.vals), self.capacity, _ptr(hit), _ptr(nc),
+                                        _ptr(st))
+        return {"hit_blocks": hit, "num_computed": nc, "status": int(st[0]), "rc": int(rc)}
+
+    def insert(self, hashes, lo, hi, rows, block_table):
+        h = np.ascontiguousarray(hashes, np.uint64)
+        m, MB = h.shape
+        bt = _i32(block_table)
+        st = np.zeros(1, np.uint32)
+        lo, hi, rows = _i32(lo), _i32(hi), _i32(rows)        # held for the call
+        rc = self.lib.orc_prefix_insert(m, _ptr(h), MB, _ptr(lo), _ptr(hi),
+                                        _ptr(rows), _ptr(bt), bt.shape[0], _ptr(self.keys),
+                                        _ptr(self.vals), self.capacity, _ptr(st))
+        return int(rc), int(st[0])
+
+    def evict(self, hashes, blocks):
+        h = np.ascontiguousarray(hashes, np.uint64).reshape(-1)
+        bl = _i32(blocks).reshape(-1)
+        return int(self.lib.orc_prefix_evict(h.size, _ptr(h), _ptr(bl), _ptr(self.keys),
+                                             _ptr(self.vals), self.capacity))
+
+    def live(self):
+        """{hash: block} of the entries that hold a block."""
+        return {int(k): int(v) for k, v in zip(self.keys[:self.capacity], self.vals[:self.capacity])
+                if k != 0 and v != NO_BLOCK}
+
+    def known(self):
+        """Every hash that takes room (with or without a block)."""
+        return {int(k) for k in self.keys[:self.capacity] if k != 0}

@@ -41,6 +41,11 @@
  *                               new token), the inverse of the scatter,
  *                               addresses enumerated block by block, the
  *                               contiguous-table closed form, block size 1.
+ *   orc_hash_blocks          -- FNV-1a's published test vectors, the chain's
+ *                               closed form (a sum of powers), the [CF] shared
+ *                               system prompt (equal hashes for equal prefixes).
+ *   orc_prefix_*             -- the [CF] example (B hits P1, P2: 8 tokens),
+ *                               the hit cap, a Python dict model of the index.
  *   orc_pool_*               -- a Python list used as a stack, run on random
  *                               acquire/release sequences; invariants (no row
  *                               out twice, free + in use = R).
@@ -64,6 +69,7 @@
 #define ORC_ST_BLOCK_OOR  0x20u  /* physical_block_id < 0 or >= pool size         */
 #define ORC_ST_SLOT_OOR   0x40u  /* slot_id >= cache slots                        */
 #define ORC_ST_BAD_RANGE  0x80u  /* CSR offsets decreasing or outside the array   */
+#define ORC_ST_TABLE_FULL 0x100u /* prefix index: no free slot for a new key      */
 
 /* One scheduled request while the batch is being assembled. */
 typedef struct {
@@ -674,6 +680,231 @@ int orc_pool_release(int32_t R, int32_t* free_rows, int32_t* num_free, uint8_t* 
         in_use[rows[i]] = 0;
         free_rows[*num_free] = rows[i];
         *num_free += 1;
+    }
+    return ORC_OK;
+}
+
+/*
+ * Prefix-cache block hashes ([CF] "Prefix Cache：复用的是 KV，不是答案"): a
+ * request's full token blocks are hashed together with their prefix context
+ * -- the hash is an index key over token blocks, not over K/V -- and looked up
+ * in the block pool's hash index; hit blocks are reused as they are.
+ *
+ * R16 (the hash; the pages fix only what it covers): FNV-1a, 64-bit, as
+ *     published by Fowler, Noll and Vo: h = 14695981039346656037; for each
+ *     byte, h ^= byte, then h *= 1099511628211 (mod 2^64).  For full block i
+ *     (tokens i*bs .. i*bs+bs-1, each int32 as 4 little-endian bytes):
+ *       c_i = FNV-1a(the block's 4*bs bytes)             content
+ *       s_i = s_{i-1} * 1099511628211 + c_i (mod 2^64)   prefix context,
+ *             s_{-1} = 0
+ *       h_i = FNV-1a(the 8 little-endian bytes of s_i), 0 replaced by 1
+ *     so h_i depends on block i and every block before it.  Only full blocks
+ *     (floor(num_tokens / bs) of them, at most MB) are hashed.
+ * Token lists are ragged views into one flat array: list b is
+ * tokens[starts[b] .. starts[b] + lengths[b]) (a CSR array, or rows of the
+ * persistent token table with starts[b] = row * token_stride).
+ * R17 (data errors): a negative length is read as 0 (BAD_COUNT); a view
+ *     outside [0, total) hashes nothing (BAD_RANGE); blocks past MB are not
+ *     hashed (LB_OOR).
+ */
+uint64_t orc_fnv1a64(const unsigned char* bytes, size_t len)
+{
+    uint64_t h = 14695981039346656037ull;
+    for (size_t i = 0; i < len; ++i) {
+        h ^= bytes[i];
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
+static void le64(uint64_t x, unsigned char out[8])
+{
+    for (int i = 0; i < 8; ++i)
+        out[i] = (unsigned char)(x >> (8 * i));
+}
+
+int orc_hash_blocks(int32_t m, const int32_t* tokens, int64_t total, const int64_t* starts,
+                    const int32_t* lengths, int32_t block_size, int32_t MB, uint64_t* hashes,
+                    int32_t* num_full, uint32_t* status)
+{
+    if (m < 0 || total < 0 || block_size <= 0 || MB < 0)
+        return ORC_EINVAL;
+    if (m > 0 && (starts == NULL || lengths == NULL || (MB > 0 && hashes == NULL) ||
+                  (total > 0 && tokens == NULL)))
+        return ORC_EINVAL;
+    uint32_t st = 0;
+    unsigned char* buf = (unsigned char*)malloc((size_t)block_size * 4);
+    if (buf == NULL)
+        return ORC_EINVAL;
+    for (int32_t b = 0; b < m; ++b) {
+        int64_t len = lengths[b];
+        if (len < 0) {
+            st |= ORC_ST_BAD_COUNT;
+            len = 0;
+        }
+        int64_t full = 0;
+        if (starts[b] < 0 || starts[b] + len > total) {
+            st |= ORC_ST_BAD_RANGE;
+        } else {
+            full = len / block_size;
+            if (full > MB) {
+                st |= ORC_ST_LB_OOR;
+                full = MB;
+            }
+        }
+        uint64_t s = 0;
+        for (int64_t i = 0; i < full; ++i) {
+            for (int32_t j = 0; j < block_size; ++j) {
+                uint32_t t = (uint32_t)tokens[starts[b] + i * block_size + j];
+                for (int k = 0; k < 4; ++k)
+                    buf[4 * j + k] = (unsigned char)(t >> (8 * k));
+            }
+            uint64_t c = orc_fnv1a64(buf, (size_t)block_size * 4);
+            s = s * 1099511628211ull + c;
+            unsigned char sb[8];
+            le64(s, sb);
+            uint64_t h = orc_fnv1a64(sb, 8);
+            hashes[(int64_t)b * MB + i] = h == 0 ? 1 : h;
+        }
+        if (num_full != NULL)
+            num_full[b] = (int32_t)full;
+    }
+    free(buf);
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * The prefix index: hash -> physical block id.  R18: an entry holds the
+ * smallest block id registered for its hash (a deterministic choice among
+ * blocks with the same content and prefix); evicting (hash, block) empties the
+ * entry only if it still names that block.  The index has room for `capacity`
+ * distinct hashes; a hash that stays known after eviction still takes its
+ * room.  Here it is a plain list searched from the front (key 0 = unused);
+ * a new hash that finds no room is flagged TABLE_FULL and not added.
+ */
+#define ORC_NO_BLOCK INT32_MAX
+
+static int64_t find_key(const uint64_t* keys, int64_t capacity, uint64_t key)
+{
+    for (int64_t i = 0; i < capacity; ++i)
+        if (keys[i] == key)
+            return i;
+    return -1;
+}
+
+/*
+ * Lookup ([CF]: B's blocks are hashed and looked up; the hits P1, P2 are
+ * reused and only the rest is computed).  R19: the hit is the run of leading
+ * full blocks whose hashes are in the index with a block, at most
+ * floor((num_tokens - 1) / bs) blocks ([CF]: a hit never covers the last
+ * token, which is computed again for its logits).  Outputs: num_computed[b] =
+ * hit blocks * bs; hit_blocks[b*MB + i] = the block of hit i (entries past the
+ * hit are not written).
+ */
+int orc_prefix_lookup(int32_t m, const uint64_t* hashes, int32_t MB, const int32_t* lengths,
+                      int32_t block_size, const uint64_t* keys, const int32_t* vals,
+                      int64_t capacity, int32_t* hit_blocks, int32_t* num_computed,
+                      uint32_t* status)
+{
+    if (m < 0 || MB < 0 || block_size <= 0 || capacity < 0)
+        return ORC_EINVAL;
+    if (m > 0 && (lengths == NULL || num_computed == NULL || (MB > 0 && hashes == NULL)))
+        return ORC_EINVAL;
+    uint32_t st = 0;
+    for (int32_t b = 0; b < m; ++b) {
+        int64_t len = lengths[b];
+        if (len < 0) {
+            st |= ORC_ST_BAD_COUNT;
+            len = 0;
+        }
+        int64_t cap = len > 0 ? (len - 1) / block_size : 0;
+        if (cap > MB)
+            cap = MB;
+        int64_t hits = 0;
+        while (hits < cap) {
+            int64_t at = find_key(keys, capacity, hashes[(int64_t)b * MB + hits]);
+            if (at < 0 || vals[at] == ORC_NO_BLOCK)
+                break;
+            if (hit_blocks != NULL)
+                hit_blocks[(int64_t)b * MB + hits] = vals[at];
+            ++hits;
+        }
+        num_computed[b] = (int32_t)(hits * block_size);
+    }
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * Registration of full blocks ([CF]: after allocation the blocks whose
+ * contents are settled are written into the prefix cache).  For request b,
+ * blocks i in [lo[b], hi[b]) register hashes[b*MB + i] -> block_table[rows[b]
+ * * MB + i].  R20 (data errors): a bad row (BAD_ROW) or a range outside
+ * [0, MB] or reversed (BAD_RANGE) registers nothing; a block id < 0 or
+ * == INT32_MAX is skipped (BLOCK_OOR); a hash of 0 is ignored.
+ */
+int orc_prefix_insert(int32_t m, const uint64_t* hashes, int32_t MB, const int32_t* lo,
+                      const int32_t* hi, const int32_t* rows, const int32_t* block_table,
+                      int32_t R, uint64_t* keys, int32_t* vals, int64_t capacity,
+                      uint32_t* status)
+{
+    if (m < 0 || MB < 0 || R < 0 || capacity < 0)
+        return ORC_EINVAL;
+    if (m > 0 && (lo == NULL || hi == NULL || rows == NULL))
+        return ORC_EINVAL;
+    uint32_t st = 0;
+    for (int32_t b = 0; b < m; ++b) {
+        int32_t r = rows[b];
+        if (r < 0 || r >= R) {
+            st |= ORC_ST_BAD_ROW;
+            continue;
+        }
+        if (lo[b] < 0 || hi[b] < lo[b] || hi[b] > MB) {
+            st |= ORC_ST_BAD_RANGE;
+            continue;
+        }
+        for (int32_t i = lo[b]; i < hi[b]; ++i) {
+            int32_t block = block_table[(int64_t)r * MB + i];
+            if (block < 0 || block == ORC_NO_BLOCK) {
+                st |= ORC_ST_BLOCK_OOR;
+                continue;
+            }
+            uint64_t key = hashes[(int64_t)b * MB + i];
+            if (key == 0)
+                continue;                 /* never produced by the hash; marks unused entries */
+            int64_t at = find_key(keys, capacity, key);
+            if (at < 0) {
+                at = find_key(keys, capacity, 0);        /* the first unused entry */
+                if (at < 0) {
+                    st |= ORC_ST_TABLE_FULL;
+                    continue;
+                }
+                keys[at] = key;
+                vals[at] = ORC_NO_BLOCK;
+            }
+            if (block < vals[at])
+                vals[at] = block;
+        }
+    }
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/* Eviction (R18): entry (hashes[i] -> blocks[i]) loses its block when the
+ * block is freed for other contents; an entry naming another block stays. */
+int orc_prefix_evict(int32_t count, const uint64_t* hashes, const int32_t* blocks,
+                     uint64_t* keys, int32_t* vals, int64_t capacity)
+{
+    if (count < 0 || capacity < 0 || (count > 0 && (hashes == NULL || blocks == NULL)))
+        return ORC_EINVAL;
+    for (int32_t i = 0; i < count; ++i) {
+        int64_t at = find_key(keys, capacity, hashes[i]);
+        if (at >= 0 && vals[at] == blocks[i])
+            vals[at] = ORC_NO_BLOCK;
     }
     return ORC_OK;
 }

@@ -9,6 +9,7 @@ test_oracle_mutants.py checks that each planted mistake fails at least one.
 """
 import json
 import os
+import struct
 
 import numpy as np
 
@@ -689,3 +690,181 @@ STATE_PINS = [pin_state_pages_example, pin_state_prefix_example, pin_state_brute
               pin_state_multistep, pin_state_errors, pin_pool_model,
               pin_pool_recycles_into_state]
 ALL_PINS += STATE_PINS
+
+
+# ---------------------------------------------------------------------------
+# prefix-cache block hashes and the prefix index
+# ---------------------------------------------------------------------------
+
+# FNV-1a 64-bit test vectors published with the FNV specification (Fowler,
+# Noll, Vo; IETF draft-eastlake-fnv): the empty string, "a" and "foobar".
+FNV1A64_VECTORS = [(b"", 0xcbf29ce484222325), (b"a", 0xaf63dc4c8601ec8c),
+                   (b"foobar", 0x85944171f73967e8)]
+FNV_PRIME64 = 1099511628211
+
+
+def pin_fnv_vectors(lib):
+    for data, want in FNV1A64_VECTORS:
+        assert oracle.fnv1a64(data, lib=lib) == want, data
+
+
+def pin_hash_closed_form(lib, seeds=range(30)):
+    """The chain written as a sum: s_i = sum_j c_j * P^(i-j) (mod 2^64), with
+    c_j the FNV-1a of block j's little-endian bytes and h_i the FNV-1a of s_i's
+    8 little-endian bytes (0 -> 1); Python integers, not the oracle's loop."""
+    for seed in seeds:
+        rng = np.random.default_rng(1700 + seed)
+        bs = int(rng.choice([1, 2, 4, 16, 32]))
+        lists = [rng.integers(-2**31, 2**31, int(rng.integers(0, 7 * bs))).tolist()
+                 for _ in range(int(rng.integers(1, 5)))]
+        MB = 6
+        out = oracle.hash_blocks(lists, bs, MB, lib=lib)
+        assert out["rc"] == 0 and out["status"] == 0
+        for b, toks in enumerate(lists):
+            full = len(toks) // bs
+            assert out["num_full"][b] == full
+            c = [oracle.fnv1a64(struct.pack(f"<{bs}i", *toks[j * bs:(j + 1) * bs]), lib=lib)
+                 for j in range(full)]
+            for i in range(full):
+                s_i = sum(c[j] * pow(FNV_PRIME64, i - j, 2**64) for j in range(i + 1)) % 2**64
+                h = oracle.fnv1a64(struct.pack("<Q", s_i), lib=lib) or 1
+                assert int(out["hashes"][b, i]) == h, (seed, b, i)
+            assert np.all(out["hashes"][b, full:] == 0), "blocks past the full ones are not written"
+
+
+def pin_hash_prefix_context(lib):
+    """Equal prefixes give equal hashes; changing one token of block j changes
+    the hashes of blocks j, j+1, ... and no earlier one; a partial last block
+    is not hashed."""
+    rng = np.random.default_rng(5)
+    bs = 4
+    base = rng.integers(0, 1000, 6 * bs).tolist()
+    for j in range(6):
+        for t in range(bs):
+            other = list(base)
+            other[j * bs + t] += 1
+            out = oracle.hash_blocks([base, other, base[:-1]], bs, 6, lib=lib)
+            h = out["hashes"]
+            assert np.array_equal(h[0, :j], h[1, :j])
+            assert np.all(h[0, j:] != h[1, j:]), (j, t)
+            assert out["num_full"].tolist() == [6, 6, 5]
+            assert np.array_equal(h[2, :5], h[0, :5])
+
+
+def pin_prefix_cf_example(lib):
+    """caffein.top: block size 4, A and B share an 8-token system prompt.  A's
+    full blocks are registered (P1, P2, A's own third block); B (10 tokens)
+    hashes its two full blocks, hits P1 and P2, and has 8 tokens computed."""
+    g = _golden("prefix_reuse_example.json")
+    inst = g["inputs"]["instantiate"]
+    P1, P2 = inst["P1"], inst["P2"]
+    system = [101, 102, 103, 104, 105, 106, 107, 108]
+    a = system + [201, 202, 203, 204]
+    b = system + [301, 302]
+    ha = oracle.hash_blocks([a], 4, 3, lib=lib)["hashes"]
+    hb = oracle.hash_blocks([b], 4, 3, lib=lib)
+    assert hb["num_full"].tolist() == [2]
+    idx = oracle.PrefixIndex(16, lib=lib)
+    bt = np.array([[P1, P2, 40]], np.int32)
+    rc, st = idx.insert(ha, [0], [3], [0], bt)
+    assert rc == 0 and st == 0
+    look = idx.lookup(hb["hashes"], [len(b)], 4)
+    assert look["num_computed"].tolist() == [g["inputs"]["completed"]]      # 8 reused tokens
+    _eq(look["hit_blocks"][0, :2], [P1, P2], "B reuses P1, P2")
+    assert look["hit_blocks"][0, 2] == -7, "nothing written past the hit"
+
+
+def pin_prefix_hit_cap(lib):
+    """A hit never covers the last token: a prompt of exactly two cached full
+    blocks (8 tokens, block size 4) hits one block; with a ninth token, two."""
+    toks = list(range(9))
+    h = oracle.hash_blocks([toks], 4, 3, lib=lib)["hashes"]
+    idx = oracle.PrefixIndex(8, lib=lib)
+    idx.insert(h, [0], [2], [0], np.array([[7, 9, -1]], np.int32))
+    assert idx.lookup(h, [8], 4)["num_computed"].tolist() == [4]
+    assert idx.lookup(h, [9], 4)["num_computed"].tolist() == [8]
+    assert idx.lookup(h, [1], 4)["num_computed"].tolist() == [0]
+    assert idx.lookup(h, [0], 4)["num_computed"].tolist() == [0]
+
+
+class IndexModel:
+    """Python dict model of the prefix index."""
+
+    def __init__(self, capacity):
+        self.capacity = capacity
+        self.entries = {}                       # hash -> block or None
+
+    def insert(self, key, block):
+        if key == 0:
+            return 0
+        if key not in self.entries:
+            if len(self.entries) == self.capacity:
+                return oracle.ST_TABLE_FULL
+            self.entries[key] = None
+        cur = self.entries[key]
+        self.entries[key] = block if cur is None else min(cur, block)
+        return 0
+
+    def evict(self, key, block):
+        if self.entries.get(key, "absent") == block:
+            self.entries[key] = None
+
+    def lookup(self, hashes, length, bs):
+        cap = (length - 1) // bs if length > 0 else 0
+        out = []
+        for i in range(min(cap, len(hashes))):
+            blk = self.entries.get(int(hashes[i]))
+            if blk is None:
+                break
+            out.append(blk)
+        return out
+
+
+def pin_prefix_model(lib, seeds=range(40)):
+    """Random inserts, evictions and lookups against the dict model, with a
+    small hash alphabet (many repeats) and a capacity that fills up."""
+    for seed in seeds:
+        rng = np.random.default_rng(2300 + seed)
+        cap = int(rng.integers(1, 12))
+        MB = 5
+        alphabet = rng.integers(1, 2**63, 10).astype(np.uint64)
+        idx, model = oracle.PrefixIndex(cap, lib=lib), IndexModel(cap)
+        for _ in range(12):
+            m = int(rng.integers(1, 4))
+            hashes = alphabet[rng.integers(0, 10, (m, MB))]
+            op = int(rng.integers(3))
+            if op == 0:
+                R = 4
+                bt = rng.integers(-1, 30, (R, MB)).astype(np.int32)
+                rows = rng.choice(R, m, replace=False)
+                lo = rng.integers(0, MB + 1, m)
+                hi = np.minimum(lo + rng.integers(0, 4, m), MB)
+                rc, st = idx.insert(hashes, lo, hi, rows, bt)
+                want = 0
+                for b in range(m):
+                    for i in range(lo[b], hi[b]):
+                        blk = int(bt[rows[b], i])
+                        if blk < 0:
+                            want |= oracle.ST_BLOCK_OOR
+                            continue
+                        want |= model.insert(int(hashes[b, i]), blk)
+                assert rc == 0 and st == want, (seed, st, want)
+            elif op == 1:
+                blocks = rng.integers(0, 30, m * MB)
+                idx.evict(hashes.reshape(-1), blocks)
+                for k, blk in zip(hashes.reshape(-1).tolist(), blocks.tolist()):
+                    model.evict(int(k), int(blk))
+            else:
+                lens = rng.integers(0, MB * 4 + 3, m)
+                look = idx.lookup(hashes, lens, 4)
+                for b in range(m):
+                    want = model.lookup(hashes[b], int(lens[b]), 4)
+                    assert look["num_computed"][b] == 4 * len(want), (seed, b)
+                    _eq(look["hit_blocks"][b, :len(want)], want, f"seed {seed} hits")
+            assert idx.live() == {k: v for k, v in model.entries.items() if v is not None}
+            assert idx.known() == set(model.entries)
+
+
+PREFIX_PINS = [pin_fnv_vectors, pin_hash_closed_form, pin_hash_prefix_context,
+               pin_prefix_cf_example, pin_prefix_hit_cap, pin_prefix_model]
+ALL_PINS += PREFIX_PINS

@@ -104,6 +104,30 @@ MUTANTS = {
     "gather_one_row_short": (
         "        for (int64_t position = 0; position < seq_len; ++position) {",
         "        for (int64_t position = 0; position + 1 < seq_len; ++position) {"),
+    "hash_chain_drops_parent": (
+        "            s = s * 1099511628211ull + c;",
+        "            s = c;"),
+    "hash_tokens_big_endian": (
+        "                    buf[4 * j + k] = (unsigned char)(t >> (8 * k));",
+        "                    buf[4 * j + k] = (unsigned char)(t >> (8 * (3 - k)));"),
+    "hash_fnv1_order": (
+        "        h ^= bytes[i];\n        h *= 1099511628211ull;",
+        "        h *= 1099511628211ull;\n        h ^= bytes[i];"),
+    "hash_counts_partial_block": (
+        "            full = len / block_size;",
+        "            full = (len + block_size - 1) / block_size;\n            if (starts[b] + full * block_size > total) full = len / block_size;"),
+    "lookup_cap_off_by_one": (
+        "        int64_t cap = len > 0 ? (len - 1) / block_size : 0;",
+        "        int64_t cap = len / block_size;"),
+    "lookup_skips_misses": (
+        "            if (at < 0 || vals[at] == ORC_NO_BLOCK)\n                break;",
+        "            if (at < 0 || vals[at] == ORC_NO_BLOCK)\n                { ++hits; continue; }"),
+    "insert_keeps_last": (
+        "            if (block < vals[at])\n                vals[at] = block;",
+        "            vals[at] = block;"),
+    "evict_unconditional": (
+        "        if (at >= 0 && vals[at] == blocks[i])",
+        "        if (at >= 0)"),
     "pool_fifo": (
         "        int32_t r = free_rows[*num_free - 1];",
         "        int32_t r = free_rows[R - *num_free];"),
