@@ -20,6 +20,10 @@
  *   pkv_gather_kv            -- the read side: each request's KV range through
  *                               its visible pages ("Complete Input Preparation
  *                               for the Attention Module");
+ *   pkv_hash_blocks, pkv_prefix_* -- prefix-cache block hashes and the hash
+ *                               index of reusable blocks ("从源码读 vLLM
+ *                               Scheduler", caffein.top: "Prefix Cache",
+ *                               "allocate_slots()");
  *   pkv_add_requests, pkv_append_blocks, pkv_advance_state, pkv_row_pool_*
  *                            -- the persistent request state the path reads
  *                               ("Persistent Request Context Strategy", "Design
@@ -70,6 +74,7 @@ extern "C" {
 #define PKV_ST_BLOCK_OOR  0x20u /* physical block id < 0 or >= num_blocks              */
 #define PKV_ST_SLOT_OOR   0x40u /* slot id >= num_slots of the cache                   */
 #define PKV_ST_BAD_RANGE  0x80u /* CSR offsets decreasing or outside their array       */
+#define PKV_ST_TABLE_FULL 0x100u /* prefix index: no free slot for a new hash           */
 
 /* Largest batch (scheduled requests per step) one call accepts: the batch is
  * ordered inside one workgroup's LDS. */
@@ -262,6 +267,70 @@ int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block
                   const void* k_cache, const void* v_cache, int64_t out_tokens, void* k_out,
                   int64_t k_out_stride, void* v_out, int64_t v_out_stride, int32_t* kv_start,
                   uint32_t* status, void* stream);
+
+/*
+ * Prefix-cache block hashes ("从源码读 vLLM Scheduler：一轮调度如何分配请求与
+ * KV Cache", caffein.top, "Prefix Cache": a request's full token blocks are
+ * hashed with their prefix context and looked up in the block pool's hash
+ * index; hit blocks are reused, and blocks whose contents are settled are
+ * registered, "allocate_slots()").  The pages fix what the hash covers, not the
+ * function; here, for full block i of a token list (tokens i*bs .. i*bs+bs-1,
+ * int32 as 4 little-endian bytes):
+ *   c_i = FNV-1a 64 of the block's bytes     (Fowler/Noll/Vo: basis
+ *         14695981039346656037, per byte h ^= byte, h *= 1099511628211)
+ *   s_i = s_{i-1} * 1099511628211 + c_i (mod 2^64), s_{-1} = 0
+ *   h_i = FNV-1a 64 of s_i's 8 little-endian bytes; 0 becomes 1
+ * so h_i depends on block i and every block before it.
+ *
+ * pkv_hash_blocks: token list b is tokens[starts[b] .. starts[b]+lengths[b])
+ *   of a flat device array of `total` int32 (a CSR array, or the persistent
+ *   token table with starts[b] = row * token_stride).  hashes[b*MB + i] = h_i
+ *   for its floor(lengths[b] / block_size) full blocks (at most MB); entries
+ *   past them are not written.  num_full[b] (may be NULL) = that count.
+ *   Data errors: length < 0 counts as 0 (BAD_COUNT); a list outside
+ *   [0, total) hashes nothing (BAD_RANGE); blocks past MB are not hashed
+ *   (LB_OOR).  Host errors: EINVAL for m < 0, total < 0, block_size <= 0,
+ *   MB < 0 or a NULL pointer that data is needed from.
+ *
+ * The index: keys[capacity] (uint64, 0 = unused) and vals[capacity] (int32
+ * block id, INT32_MAX = none), device memory the caller owns; capacity is a
+ * power of two.  An entry maps a hash to the smallest block registered for
+ * it.  pkv_prefix_clear empties it.
+ *
+ * pkv_prefix_lookup: for request b (lengths[b] tokens, hashes from
+ *   pkv_hash_blocks) the hit is the run of leading full blocks whose hashes
+ *   have a block, at most floor((lengths[b]-1) / block_size) blocks (the last
+ *   token is always computed again, for its logits).  num_computed[b] = hit
+ *   blocks * block_size; hit_blocks[b*MB + i] (may be NULL) = the block of hit
+ *   i, entries past the hit not written.  Data errors: length < 0 counts as 0
+ *   (BAD_COUNT).
+ * pkv_prefix_insert: registers hashes[b*MB + i] -> block_table[rows[b]*MB + i]
+ *   for i in [lo[b], hi[b]).  Data errors: a bad row (BAD_ROW) or a range
+ *   outside [0, MB] (BAD_RANGE) registers nothing; a block < 0 or INT32_MAX is
+ *   skipped (BLOCK_OOR); a new hash finding no free slot is not registered
+ *   (TABLE_FULL); a hash of 0 is ignored.  Order-independent: concurrent
+ *   registrations of one hash keep the smallest block.
+ * pkv_prefix_evict: entry hashes[i] loses its block if that is blocks[i] (the
+ *   block was freed for other contents); an entry naming another block stays.
+ *   Evicted hashes keep their slot until the next clear.
+ * Host errors of the index calls: EINVAL for negative sizes, a capacity that
+ *   is not a power of two (0 is allowed: nothing is ever found or stored), or
+ *   a NULL pointer that data is needed from.
+ */
+int pkv_hash_blocks(int32_t m, const int32_t* tokens, int64_t total, const int64_t* starts,
+                    const int32_t* lengths, int32_t block_size, int32_t MB, uint64_t* hashes,
+                    int32_t* num_full, uint32_t* status, void* stream);
+int pkv_prefix_clear(uint64_t* keys, int32_t* vals, int64_t capacity, void* stream);
+int pkv_prefix_lookup(int32_t m, const uint64_t* hashes, int32_t MB, const int32_t* lengths,
+                      int32_t block_size, const uint64_t* keys, const int32_t* vals,
+                      int64_t capacity, int32_t* hit_blocks, int32_t* num_computed,
+                      uint32_t* status, void* stream);
+int pkv_prefix_insert(int32_t m, const uint64_t* hashes, int32_t MB, const int32_t* lo,
+                      const int32_t* hi, const int32_t* rows, const int32_t* block_table,
+                      int32_t R, uint64_t* keys, int32_t* vals, int64_t capacity,
+                      uint32_t* status, void* stream);
+int pkv_prefix_evict(int32_t count, const uint64_t* hashes, const int32_t* blocks,
+                     uint64_t* keys, int32_t* vals, int64_t capacity, void* stream);
 
 /*
  * Persistent request state ("Persistent Request Context Strategy" and "Design

@@ -23,7 +23,9 @@ OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP, ENOROWS, ENOMEM = 0, -1, -2, -3, -4, -5,
 ST_BITS = {
     "BAD_ROW": 0x01, "BAD_COUNT": 0x02, "TOKEN_SUM": 0x04, "POS_OOR": 0x08,
     "LB_OOR": 0x10, "BLOCK_OOR": 0x20, "SLOT_OOR": 0x40, "BAD_RANGE": 0x80,
+    "TABLE_FULL": 0x100,
 }
+NO_BLOCK = 2**31 - 1        # prefix index: an entry without a block
 MAX_BATCH = 4096
 
 _P = ctypes.c_void_p
@@ -74,6 +76,17 @@ def load_library(path: str = library_path) -> ctypes.CDLL:
     lib.pkv_gather_kv.restype = ctypes.c_int
     lib.pkv_gather_kv.argtypes = [_I32, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P, _I64,
                                   _P, _I64, _P, _P, _P]
+    lib.pkv_hash_blocks.restype = ctypes.c_int
+    lib.pkv_hash_blocks.argtypes = [_I32, _P, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P]
+    lib.pkv_prefix_clear.restype = ctypes.c_int
+    lib.pkv_prefix_clear.argtypes = [_P, _P, _I64, _P]
+    lib.pkv_prefix_lookup.restype = ctypes.c_int
+    lib.pkv_prefix_lookup.argtypes = [_I32, _P, _I32, _P, _I32, _P, _P, _I64, _P, _P, _P, _P]
+    lib.pkv_prefix_insert.restype = ctypes.c_int
+    lib.pkv_prefix_insert.argtypes = [_I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I64, _P,
+                                      _P]
+    lib.pkv_prefix_evict.restype = ctypes.c_int
+    lib.pkv_prefix_evict.argtypes = [_I32, _P, _P, _P, _P, _I64, _P]
     lib.pkv_add_requests.restype = ctypes.c_int
     lib.pkv_add_requests.argtypes = [_I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P,
                                      _I64, _I32, _P, _I32, _P, _P, _P]
@@ -539,3 +552,109 @@ class RowPool:
         h, self._h = getattr(self, "_h", None), None
         if h is not None and _lib is not None:
             _lib.pkv_row_pool_destroy(h)
+
+
+# -- prefix-cache block hashes and the prefix index ---------------------------
+def _i64t(name: str, t: Optional[torch.Tensor], shape=None, optional=False):
+    """A contiguous int64 GPU tensor (64-bit hashes travel as int64 bit patterns)."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if t.dtype != torch.int64 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int64 tensor on the GPU")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _index(keys, vals):
+    _i64t("keys", keys)
+    _idx("vals", vals, tuple(keys.shape))
+    if keys.dim() != 1 or (keys.numel() & (keys.numel() - 1)) != 0:
+        raise ValueError("the index capacity must be a power of two (1-D keys)")
+    return keys.numel()
+
+
+def hash_blocks(tokens, starts, lengths, block_size, *, hashes, num_full=None, status=None,
+                stream=None) -> None:
+    """Chained hashes of every full block of m token lists (pkv_hash_blocks).
+
+    tokens: flat int32 GPU tensor; list b is tokens[starts[b] : starts[b] +
+    lengths[b]] (starts int64 [m], lengths int32 [m]); hashes: int64 [m, MB]
+    (uint64 bit patterns); num_full: int32 [m] or None."""
+    m = lengths.shape[0]
+    _idx("tokens", tokens)
+    _i64t("starts", starts, (m,))
+    _idx("lengths", lengths, (m,))
+    _i64t("hashes", hashes)
+    if hashes.dim() != 2 or hashes.shape[0] != m:
+        raise ValueError("hashes must be [m, MB]")
+    _idx("num_full", num_full, (m,), optional=True)
+    rc = _lib.pkv_hash_blocks(m, _ptr(tokens), tokens.numel(), _ptr(starts), _ptr(lengths),
+                              int(block_size), hashes.shape[1], _ptr(hashes), _ptr(num_full),
+                              _ptr(_status(status)), _stream(stream))
+    if rc != OK:
+        raise PagedKVError("hash_blocks", rc)
+
+
+def prefix_clear(keys, vals, *, stream=None) -> None:
+    """Empty the prefix index (pkv_prefix_clear)."""
+    cap = _index(keys, vals)
+    rc = _lib.pkv_prefix_clear(_ptr(keys), _ptr(vals), cap, _stream(stream))
+    if rc != OK:
+        raise PagedKVError("prefix_clear", rc)
+
+
+def prefix_lookup(hashes, lengths, block_size, keys, vals, *, num_computed, hit_blocks=None,
+                  status=None, stream=None) -> None:
+    """Longest cached run of leading full blocks per request (pkv_prefix_lookup)."""
+    m = lengths.shape[0]
+    _i64t("hashes", hashes)
+    if hashes.dim() != 2 or hashes.shape[0] != m:
+        raise ValueError("hashes must be [m, MB]")
+    MB = hashes.shape[1]
+    _idx("lengths", lengths, (m,))
+    _idx("num_computed", num_computed, (m,))
+    _idx("hit_blocks", hit_blocks, (m, MB), optional=True)
+    cap = _index(keys, vals)
+    rc = _lib.pkv_prefix_lookup(m, _ptr(hashes), MB, _ptr(lengths), int(block_size), _ptr(keys),
+                                _ptr(vals), cap, _ptr(hit_blocks), _ptr(num_computed),
+                                _ptr(_status(status)), _stream(stream))
+    if rc != OK:
+        raise PagedKVError("prefix_lookup", rc)
+
+
+def prefix_insert(hashes, lo, hi, rows, block_table, keys, vals, *, status=None,
+                  stream=None) -> None:
+    """Register blocks [lo[b], hi[b]) of each request (pkv_prefix_insert)."""
+    m = rows.shape[0]
+    _i64t("hashes", hashes)
+    if hashes.dim() != 2 or hashes.shape[0] != m:
+        raise ValueError("hashes must be [m, MB]")
+    MB = hashes.shape[1]
+    for name, t in (("lo", lo), ("hi", hi), ("rows", rows)):
+        _idx(name, t, (m,))
+    _idx("block_table", block_table)
+    if block_table.dim() != 2 or block_table.shape[1] != MB:
+        raise ValueError("block_table must be [R, MB] with the hashes' MB")
+    cap = _index(keys, vals)
+    rc = _lib.pkv_prefix_insert(m, _ptr(hashes), MB, _ptr(lo), _ptr(hi), _ptr(rows),
+                                _ptr(block_table), block_table.shape[0], _ptr(keys), _ptr(vals),
+                                cap, _ptr(_status(status)), _stream(stream))
+    if rc != OK:
+        raise PagedKVError("prefix_insert", rc)
+
+
+def prefix_evict(hashes, blocks, keys, vals, *, stream=None) -> None:
+    """Drop entries hashes[i] -> blocks[i] (pkv_prefix_evict)."""
+    count = hashes.numel()
+    _i64t("hashes", hashes)
+    _idx("blocks", blocks)
+    if blocks.numel() != count:
+        raise ValueError("hashes and blocks must have the same length")
+    cap = _index(keys, vals)
+    rc = _lib.pkv_prefix_evict(count, _ptr(hashes), _ptr(blocks), _ptr(keys), _ptr(vals), cap,
+                               _stream(stream))
+    if rc != OK:
+        raise PagedKVError("prefix_evict", rc)

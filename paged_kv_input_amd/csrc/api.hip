@@ -211,6 +211,75 @@ int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block
                                        static_cast<hipStream_t>(stream)));
 }
 
+int pkv_hash_blocks(int32_t m, const int32_t* tokens, int64_t total, const int64_t* starts,
+                    const int32_t* lengths, int32_t block_size, int32_t MB, uint64_t* hashes,
+                    int32_t* num_full, uint32_t* status, void* stream)
+{
+    if (m < 0 || total < 0 || block_size <= 0 || MB < 0)
+        return PKV_EINVAL;
+    if (m > 0 && (starts == nullptr || lengths == nullptr || (MB > 0 && hashes == nullptr) ||
+                  (total > 0 && tokens == nullptr)))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_hash_blocks(m, tokens, total, starts, lengths, block_size, MB,
+                                            hashes, num_full, status,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+bool bad_capacity(int64_t capacity) { return capacity < 0 || (capacity & (capacity - 1)) != 0; }
+}  // namespace
+
+int pkv_prefix_clear(uint64_t* keys, int32_t* vals, int64_t capacity, void* stream)
+{
+    if (bad_capacity(capacity) || (capacity > 0 && (keys == nullptr || vals == nullptr)))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_prefix_clear(keys, vals, capacity, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_prefix_lookup(int32_t m, const uint64_t* hashes, int32_t MB, const int32_t* lengths,
+                      int32_t block_size, const uint64_t* keys, const int32_t* vals,
+                      int64_t capacity, int32_t* hit_blocks, int32_t* num_computed,
+                      uint32_t* status, void* stream)
+{
+    if (m < 0 || MB < 0 || block_size <= 0 || bad_capacity(capacity))
+        return PKV_EINVAL;
+    if (m > 0 && (lengths == nullptr || num_computed == nullptr ||
+                  (MB > 0 && hashes == nullptr) ||
+                  (capacity > 0 && (keys == nullptr || vals == nullptr))))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_prefix_lookup(m, hashes, MB, lengths, block_size, keys, vals,
+                                              capacity, hit_blocks, num_computed, status,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int pkv_prefix_insert(int32_t m, const uint64_t* hashes, int32_t MB, const int32_t* lo,
+                      const int32_t* hi, const int32_t* rows, const int32_t* block_table,
+                      int32_t R, uint64_t* keys, int32_t* vals, int64_t capacity,
+                      uint32_t* status, void* stream)
+{
+    if (m < 0 || MB < 0 || R < 0 || bad_capacity(capacity))
+        return PKV_EINVAL;
+    if (m > 0 && (lo == nullptr || hi == nullptr || rows == nullptr ||
+                  (MB > 0 && (hashes == nullptr || (R > 0 && block_table == nullptr))) ||
+                  (capacity > 0 && (keys == nullptr || vals == nullptr))))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_prefix_insert(m, hashes, MB, lo, hi, rows, block_table, R, keys,
+                                              vals, capacity, status,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int pkv_prefix_evict(int32_t count, const uint64_t* hashes, const int32_t* blocks,
+                     uint64_t* keys, int32_t* vals, int64_t capacity, void* stream)
+{
+    if (count < 0 || bad_capacity(capacity))
+        return PKV_EINVAL;
+    if (count > 0 && (hashes == nullptr || blocks == nullptr ||
+                      (capacity > 0 && (keys == nullptr || vals == nullptr))))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_prefix_evict(count, hashes, blocks, keys, vals, capacity,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int pkv_add_requests(int32_t m, const int32_t* rows, const int32_t* num_computed,
                      const int32_t* prompt_start, const int32_t* prompt_tokens,
                      int32_t num_prompt_tokens, const int32_t* block_start, const int32_t* blocks,

@@ -64,4 +64,27 @@ hipError_t launch_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k
                           int64_t num_slots, const int32_t* slot_mapping, uint32_t* status,
                           hipStream_t stream);
 
+hipError_t launch_hash_blocks(int32_t m, const int32_t* tokens, int64_t total,
+                              const int64_t* starts, const int32_t* lengths, int32_t block_size,
+                              int32_t MB, uint64_t* hashes, int32_t* num_full, uint32_t* status,
+                              hipStream_t stream);
+
+hipError_t launch_prefix_lookup(int32_t m, const uint64_t* hashes, int32_t MB,
+                                const int32_t* lengths, int32_t block_size, const uint64_t* keys,
+                                const int32_t* vals, int64_t capacity, int32_t* hit_blocks,
+                                int32_t* num_computed, uint32_t* status, hipStream_t stream);
+
+hipError_t launch_prefix_insert(int32_t m, const uint64_t* hashes, int32_t MB, const int32_t* lo,
+                                const int32_t* hi, const int32_t* rows,
+                                const int32_t* block_table, int32_t R, uint64_t* keys,
+                                int32_t* vals, int64_t capacity, uint32_t* status,
+                                hipStream_t stream);
+
+hipError_t launch_prefix_evict(int32_t count, const uint64_t* hashes, const int32_t* blocks,
+                               uint64_t* keys, int32_t* vals, int64_t capacity,
+                               hipStream_t stream);
+
+hipError_t launch_prefix_clear(uint64_t* keys, int32_t* vals, int64_t capacity,
+                               hipStream_t stream);
+
 }  // namespace pkv

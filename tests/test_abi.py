@@ -35,7 +35,9 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["pkv_abi_version", "pkv_add_requests", "pkv_advance_state",
                      "pkv_append_blocks", "pkv_compute_slot_mapping", "pkv_error_string",
-                     "pkv_gather_kv", "pkv_prepare_batch", "pkv_row_pool_acquire", "pkv_row_pool_create",
+                     "pkv_gather_kv", "pkv_hash_blocks", "pkv_prefix_clear", "pkv_prefix_evict",
+                     "pkv_prefix_insert", "pkv_prefix_lookup",
+                     "pkv_prepare_batch", "pkv_row_pool_acquire", "pkv_row_pool_create",
                      "pkv_row_pool_destroy", "pkv_row_pool_num_free", "pkv_row_pool_release",
                      "pkv_scatter_kv", "pkv_step"]
     for name in names:
@@ -151,6 +153,33 @@ def test_gather_host_argument_errors(lib):
     assert call(a0=4097) == -3                     # beyond PKV_MAX_BATCH
     assert call(a9=1 << 31) == -3                  # out_tokens > INT32_MAX
     assert call(a0=0, a1=N, a2=N, a14=N) == 0      # nothing to do: nothing enqueued
+
+
+def test_prefix_host_argument_errors(lib):
+    N = None
+    fake = ctypes.c_void_p(0x1000)
+    h = lib.pkv_hash_blocks
+    assert h(-1, fake, 8, fake, fake, 4, 2, fake, N, N, N) == -1       # m < 0
+    assert h(1, fake, 8, fake, fake, 0, 2, fake, N, N, N) == -1        # block_size <= 0
+    assert h(1, fake, -1, fake, fake, 4, 2, fake, N, N, N) == -1       # total < 0
+    assert h(1, N, 8, fake, fake, 4, 2, fake, N, N, N) == -1           # tokens NULL
+    assert h(1, fake, 8, fake, fake, 4, 2, N, N, N, N) == -1           # hashes NULL
+    assert h(0, N, 0, N, N, 4, 2, N, N, N, N) == 0                     # nothing to do
+    assert lib.pkv_prefix_clear(fake, fake, 12, N) == -1               # not a power of two
+    assert lib.pkv_prefix_clear(N, fake, 16, N) == -1
+    assert lib.pkv_prefix_clear(N, N, 0, N) == 0
+    lk = lib.pkv_prefix_lookup
+    assert lk(1, fake, 2, fake, 4, fake, fake, 6, N, fake, N, N) == -1  # capacity 6
+    assert lk(1, fake, 2, fake, 4, fake, fake, 8, N, N, N, N) == -1     # num_computed NULL
+    assert lk(1, fake, 2, fake, 0, fake, fake, 8, N, fake, N, N) == -1  # block_size 0
+    ins = lib.pkv_prefix_insert
+    assert ins(1, fake, 2, fake, fake, fake, fake, 4, fake, fake, -8, N, N) == -1
+    assert ins(1, fake, 2, N, fake, fake, fake, 4, fake, fake, 8, N, N) == -1
+    assert ins(1, fake, 2, fake, fake, fake, N, 4, fake, fake, 8, N, N) == -1
+    ev = lib.pkv_prefix_evict
+    assert ev(-1, fake, fake, fake, fake, 8, N) == -1
+    assert ev(1, N, fake, fake, fake, 8, N) == -1
+    assert ev(0, N, N, N, N, 8, N) == 0
 
 
 def test_state_host_argument_errors(lib):
