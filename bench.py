@@ -280,6 +280,90 @@ def gather_calls(batch, steps_dev, steps, warmup, stream, workload):
             "traffic_per_launch": traffic_from_profile("gather_kv", workload)}
 
 
+def prefix_calls(batch, step, steps, warmup, stream):
+    """Prefix-cache work on this batch's shape: every scheduled request's whole
+    token list after the step (seq_len tokens, read from the persistent token
+    table) hashed block by block (group 0's block size), its full blocks
+    registered in an index of twice their number, and the lookup that then
+    hits each request's cap; each call timed back to back.  Hashing is bound by
+    the FNV-1a multiply chain (ALU), lookup and registration by memory latency."""
+    import numpy as np
+    import torch
+
+    from paged_kv_input_amd import api
+
+    g = batch.groups[0]
+    bs = g.block_size
+    rows = batch.sched_rows.astype(np.int64)
+    lengths = np.minimum(batch.completed[rows].astype(np.int64)
+                         + np.maximum(batch.num_scheduled, 0), batch.L).astype(np.int32)
+    full = lengths // bs
+    MB = max(int(full.max()), 1)
+    dev = step.device
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)   # noqa: E731
+    tokens = step.token_ids.view(-1)
+    starts = up(rows * batch.L)
+    lens = up(lengths)
+    m = batch.n
+    hashes = torch.zeros((m, MB), dtype=torch.int64, device=dev)
+    num_full = torch.empty(m, dtype=torch.int32, device=dev)
+    cap = 1 << max(4, int(2 * full.sum()).bit_length())
+    keys = torch.empty(cap, dtype=torch.int64, device=dev)
+    vals = torch.empty(cap, dtype=torch.int32, device=dev)
+    api.prefix_clear(keys, vals)
+    table = up(np.arange(m * MB, dtype=np.int32).reshape(m, MB))
+    zero, rid = up(np.zeros(m, np.int32)), up(np.arange(m, dtype=np.int32))
+    nc = torch.empty(m, dtype=torch.int32, device=dev)
+    hits = torch.empty((m, MB), dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def hash_():
+        api.hash_blocks(tokens, starts, lens, bs, hashes=hashes, num_full=num_full,
+                        status=status, stream=stream)
+
+    def insert():
+        api.prefix_insert(hashes, zero, num_full, rid, table, keys, vals, status=status,
+                          stream=stream)
+
+    def lookup():
+        api.prefix_lookup(hashes, lens, bs, keys, vals, num_computed=nc, hit_blocks=hits,
+                          status=status, stream=stream)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    out = {}
+    tok = int(lengths.sum())
+    nblk = int(full.sum())
+    for name, fn in (("hash_blocks", hash_), ("prefix_insert", insert),
+                     ("prefix_lookup", lookup)):
+        ms = timed(fn)
+        out[name] = {"ms": ms}
+    want = ((np.maximum(lengths, 1) - 1) // bs) * bs
+    if status.item() != 0 or not np.array_equal(nc.cpu().numpy(), want):
+        raise RuntimeError("prefix calls: unexpected status or hits")
+    hs = out["hash_blocks"]
+    hs["tokens_per_s"] = tok / (hs["ms"] * 1e-3)
+    # FNV-1a over 4 bytes per token, then 8 bytes per block for its hash:
+    # one xor and one 64-bit multiply by the prime per byte.
+    hs["fnv_bytes_per_s"] = (4 * tok + 8 * nblk) / (hs["ms"] * 1e-3)
+    hs["bound"] = "alu"
+    out["prefix_insert"]["blocks_per_s"] = nblk / (out["prefix_insert"]["ms"] * 1e-3)
+    out["prefix_lookup"]["blocks_per_s"] = nblk / (out["prefix_lookup"]["ms"] * 1e-3)
+    out["note"] = (f"{m} requests, {tok} tokens, {nblk} full blocks of {bs}; index of {cap} "
+                   "entries; every lookup hits its cap")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +471,7 @@ def main():
             raise RuntimeError(f"device status bits set: {s.status_bits():#x}")
     state = state_calls(batch, steps[0], args.steps, args.warmup, stream)
     gather = gather_calls(batch, steps, args.steps, args.warmup, stream, args.workload)
+    prefix = prefix_calls(batch, steps[0], args.steps, args.warmup, stream)
 
     ab = algorithmic_bytes(batch)
     cb = call_bytes(batch)
@@ -446,6 +531,7 @@ def main():
         },
         "state_calls": state,
         "gather_kv": gather,
+        "prefix_cache": prefix,
         "cold_single_step": {
             "ms_median": statistics.median(cold),
             "note": "1 GiB rewrite before each step; HIP events around the single launch",
