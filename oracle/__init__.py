@@ -56,7 +56,7 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
                                       _P, _P, _P, _P, _P, _P]
     lib.orc_compute_slot_mapping.restype = ctypes.c_int
     lib.orc_compute_slot_mapping.argtypes = [_I32, _I32, _P, _P, _P, _P, _P, _I32, _I32,
-                                             _I32, _I32, _P, _P, _P]
+                                             _I32, _I32, _I32, _P, _P, _P]
     lib.orc_scatter_kv.restype = ctypes.c_int
     lib.orc_scatter_kv.argtypes = [_I32, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _P]
     lib.orc_add_requests.restype = ctypes.c_int
@@ -67,8 +67,14 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_advance_state.restype = ctypes.c_int
     lib.orc_advance_state.argtypes = [_I32, _P, _P, _P, _I32, _P, _P, _I64, _I32, _P]
     lib.orc_gather_kv.restype = ctypes.c_int
-    lib.orc_gather_kv.argtypes = [_I32, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P, _I64,
-                                  _P, _I64, _P, _P]
+    lib.orc_gather_kv.argtypes = [_I32, _P, _P, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _I64,
+                                  _P, _I64, _P, _I64, _P, _P]
+    lib.orc_window_free.restype = ctypes.c_int
+    lib.orc_window_free.argtypes = [_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P]
+    lib.orc_lookahead_slots.restype = ctypes.c_int
+    lib.orc_lookahead_slots.argtypes = [_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]
+    lib.orc_blocks_needed.restype = ctypes.c_int
+    lib.orc_blocks_needed.argtypes = [_I32, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P]
     lib.orc_fnv1a64.restype = ctypes.c_uint64
     lib.orc_fnv1a64.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
     lib.orc_hash_blocks.restype = ctypes.c_int
@@ -141,8 +147,9 @@ IBT_UNWRITTEN = -9  # fill value of input_block_tables entries the call must not
 
 
 def compute_slot_mapping(index_mapping, query_start_loc, seq_lens, positions, block_table,
-                         block_size, num_blocks, *, with_ibt=True, lib=None):
-    """Oracle of ``compute_slot_mapping`` for one KV-cache group."""
+                         block_size, num_blocks, *, with_ibt=True, sliding_window=0, lib=None):
+    """Oracle of ``compute_slot_mapping`` for one KV-cache group (sliding_window
+    0 = full attention)."""
     lib = lib or load()
     im, qsl, sl, pos = _i32(index_mapping), _i32(query_start_loc), _i32(seq_lens), _i32(positions)
     bt = _i32(block_table)
@@ -154,7 +161,8 @@ def compute_slot_mapping(index_mapping, query_start_loc, seq_lens, positions, bl
     }
     st = np.zeros(1, np.uint32)
     rc = lib.orc_compute_slot_mapping(n, T, _ptr(im), _ptr(qsl), _ptr(sl), _ptr(pos), _ptr(bt),
-                                      R, MB, block_size, num_blocks, _ptr(out["slot_mapping"]),
+                                      R, MB, block_size, num_blocks, sliding_window,
+                                      _ptr(out["slot_mapping"]),
                                       _ptr(out["input_block_tables"]), _ptr(st))
     out["status"], out["rc"] = int(st[0]), int(rc)
     return out
@@ -186,7 +194,8 @@ def scatter_kv(k, v, k_cache, v_cache, slot_mapping, *, lib=None):
 
 
 def gather_kv(seq_lens, input_block_tables, block_size, num_blocks, k_cache, v_cache,
-              out_tokens=None, *, out_fill=0xFFFF, lib=None):
+              out_tokens=None, *, out_fill=0xFFFF, query_start_loc=None, sliding_window=0,
+              lib=None):
     """Oracle of the paged K/V read: the rows of every position < seq_len,
     request after request.  ``k_cache``/``v_cache`` are C-contiguous
     [num_blocks * block_size, ...] arrays.  Returns a dict with ``k``, ``v``
@@ -194,10 +203,15 @@ def gather_kv(seq_lens, input_block_tables, block_size, num_blocks, k_cache, v_c
     ``kv_start`` [n+1], ``status`` and ``rc``."""
     lib = lib or load()
     sl, ibt = _i32(seq_lens), _i32(input_block_tables)
+    qsl = None if query_start_loc is None else _i32(query_start_loc)
     n = sl.shape[0]
     MB = ibt.shape[1] if ibt.ndim == 2 else 0
     if out_tokens is None:
-        out_tokens = int(np.maximum(sl.astype(np.int64), 0).sum())
+        lens = np.maximum(sl.astype(np.int64), 0)
+        if sliding_window > 0:
+            cnt = np.maximum(np.diff(qsl.astype(np.int64)), 0)
+            lens = lens - np.maximum(lens - cnt - sliding_window + 1, 0)
+        out_tokens = int(lens.sum())
     assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
     assert k_cache.shape[0] >= num_blocks * block_size
     row_shape = k_cache.shape[1:]
@@ -206,7 +220,8 @@ def gather_kv(seq_lens, input_block_tables, block_size, num_blocks, k_cache, v_c
            "v": np.full((out_tokens, *row_shape), out_fill, v_cache.dtype),
            "kv_start": np.full(n + 1, -7, np.int32)}
     st = np.zeros(1, np.uint32)
-    rc = lib.orc_gather_kv(n, _ptr(sl), _ptr(ibt) if MB else None, MB, block_size, num_blocks,
+    rc = lib.orc_gather_kv(n, _ptr(sl), _ptr(qsl), sliding_window,
+                           _ptr(ibt) if MB else None, MB, block_size, num_blocks,
                            row_bytes, _ptr(k_cache), _ptr(v_cache), out_tokens, _ptr(out["k"]),
                            row_bytes, _ptr(out["v"]), row_bytes, _ptr(out["kv_start"]), _ptr(st))
     out["status"], out["rc"] = int(st[0]), int(rc)
@@ -425,3 +440,49 @@ class PrefixIndex:
     def known(self):
         """Every hash that takes room (with or without a block)."""
         return {int(k) for k in self.keys[:self.capacity] if k != 0}
+
+
+# ---------------------------------------------------------------------------
+# sliding-window holes and speculative lookahead
+# ---------------------------------------------------------------------------
+
+def window_free(rows, completed, block_table, block_size, sliding_window, *, lib=None):
+    """Free the blocks wholly before every window (block_table updated in
+    place).  Returns dict(freed [m, MB] (-7 where not written), num_freed [m],
+    status, rc)."""
+    lib = lib or load()
+    rows, comp = _i32(rows), _i32(completed)
+    assert block_table.dtype == np.int32 and block_table.flags.c_contiguous
+    R, MB = block_table.shape
+    m = rows.size
+    freed = np.full((m, max(MB, 1)), -7, np.int32)
+    nf = np.full(m, -7, np.int32)
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_window_free(m, _ptr(rows), _ptr(comp), _ptr(block_table), R, MB, block_size,
+                             sliding_window, _ptr(freed), _ptr(nf), _ptr(st))
+    return {"freed": freed[:, :MB], "num_freed": nf, "status": int(st[0]), "rc": int(rc)}
+
+
+def lookahead_slots(index_mapping, seq_lens, block_table, block_size, num_blocks, k, *, lib=None):
+    """Slots of the k positions after each request's seq_len."""
+    lib = lib or load()
+    im, sl, bt = _i32(index_mapping), _i32(seq_lens), _i32(block_table)
+    R, MB = bt.shape
+    n = im.size
+    out = np.full((n, max(k, 1)), -7, np.int32)
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_lookahead_slots(n, _ptr(im), _ptr(sl), _ptr(bt), R, MB, block_size, num_blocks,
+                                 k, _ptr(out), _ptr(st))
+    return {"slots": out[:, :k], "status": int(st[0]), "rc": int(rc)}
+
+
+def blocks_needed(rows, num_new, k, block_size, completed, row_blocks, *, lib=None):
+    """New blocks each request still needs for its new and lookahead tokens."""
+    lib = lib or load()
+    rows, nn, comp, rb = _i32(rows), _i32(num_new), _i32(completed), _i32(row_blocks)
+    n = rows.size
+    need = np.full(max(n, 1), -7, np.int32)
+    st = np.zeros(1, np.uint32)
+    rc = lib.orc_blocks_needed(n, _ptr(rows), _ptr(nn), k, block_size, _ptr(comp), _ptr(rb),
+                               comp.size, _ptr(need), _ptr(st))
+    return {"need": need[:n], "status": int(st[0]), "rc": int(rc)}

@@ -244,16 +244,33 @@ int orc_prepare_batch(int32_t n, int32_t T,
  *     LB_OOR and cut to MB.  seq_len <= 0 shows no page.
  * R6 (continued): a bad row, a negative position, a logic_block >= MB or a
  *     physical block outside [0, num_blocks) is flagged and gives slot -1.
+ * R21 (sliding-window groups, [CF] "allocate_slots()": blocks a sliding-window
+ *     group no longer needs are freed first): with window W > 0 the token at
+ *     position p attends positions p-W+1 .. p, so batch row b (count c =
+ *     query_start_loc[b+1] - query_start_loc[b], seq_len s) needs positions
+ *     from first = max(0, s - c - W + 1) on.  Visible pages before
+ *     first / block_size lie outside every window of the step: they are
+ *     copied as they are and a -1 there (a freed block, a hole) is not
+ *     flagged.  W = 0 is full attention.
  */
+static int64_t window_first(int32_t seq_len, int64_t count, int32_t window)
+{
+    if (window <= 0)
+        return 0;
+    int64_t first = (int64_t)seq_len - count - window + 1;
+    return first > 0 ? first : 0;
+}
+
 int orc_compute_slot_mapping(int32_t n, int32_t T,
                              const int32_t* index_mapping, const int32_t* query_start_loc,
                              const int32_t* seq_lens, const int32_t* positions,
                              const int32_t* block_table, int32_t R, int32_t MB,
-                             int32_t block_size, int32_t num_blocks,
+                             int32_t block_size, int32_t num_blocks, int32_t sliding_window,
                              int32_t* slot_mapping, int32_t* input_block_tables,
                              uint32_t* status)
 {
-    if (n < 0 || T < 0 || R < 0 || MB < 0 || num_blocks < 0 || block_size <= 0)
+    if (n < 0 || T < 0 || R < 0 || MB < 0 || num_blocks < 0 || block_size <= 0 ||
+        sliding_window < 0)
         return ORC_EINVAL;
     if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX + 1)
         return ORC_EINVAL;                       /* slot ids must fit in int32 */
@@ -318,9 +335,13 @@ int orc_compute_slot_mapping(int32_t n, int32_t T,
                 st |= ORC_ST_LB_OOR;
                 visible = MB;
             }
+            int64_t count = (int64_t)query_start_loc[batch_index + 1] - query_start_loc[batch_index];
+            int64_t first_block =
+                window_first(seq_len, count > 0 ? count : 0, sliding_window) / block_size;
             for (int64_t i = 0; i < visible; ++i) {
                 int32_t blk = block_table[(int64_t)request_state_index * MB + i];
-                if (blk < 0 || blk >= num_blocks)
+                int hole = i < first_block && blk == -1;                      /* R21 */
+                if ((blk < 0 || blk >= num_blocks) && !hole)
                     st |= ORC_ST_BLOCK_OOR;
                 input_block_tables[(int64_t)batch_index * MB + i] = blk;
             }
@@ -397,22 +418,28 @@ int orc_scatter_kv(int32_t T, int64_t row_bytes,
  *     the seq_lens (kv_start[0] = 0, n+1 entries, int64 sum kept in int32,
  *     saturating at INT32_MAX).  This is the layout of a non-paged varlen
  *     attention input and the exact inverse of the scatter.
+ * R22 (sliding-window groups, W > 0): only the positions some new token of
+ *     the step attends are read, first .. seq_len-1 with first as in R21, to
+ *     rows kv_start[b] + (p - first); kv_start sums seq_len - first.
  * R15 (data errors): a negative seq_len counts as 0 (BAD_COUNT); a position
  *     whose logical block is >= MB is not read (LB_OOR); a visible page
  *     outside [0, num_blocks) is not read (BLOCK_OOR); rows at or past
  *     out_tokens are not written (TOKEN_SUM).  Rows not read keep their
  *     previous contents.  The cache holds num_blocks * block_size slots.
  */
-int orc_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
+int orc_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* query_start_loc,
+                  int32_t sliding_window, const int32_t* input_block_tables,
                   int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
                   const void* k_cache, const void* v_cache, int64_t out_tokens, void* k_out,
                   int64_t k_out_stride, void* v_out, int64_t v_out_stride, int32_t* kv_start,
                   uint32_t* status)
 {
     if (n < 0 || MB < 0 || block_size <= 0 || num_blocks < 0 || row_bytes <= 0 ||
-        out_tokens < 0 || k_out_stride < row_bytes || v_out_stride < row_bytes)
+        out_tokens < 0 || k_out_stride < row_bytes || v_out_stride < row_bytes ||
+        sliding_window < 0)
         return ORC_EINVAL;
-    if (n > 0 && (seq_lens == NULL || (MB > 0 && input_block_tables == NULL)))
+    if (n > 0 && (seq_lens == NULL || (MB > 0 && input_block_tables == NULL) ||
+                  (sliding_window > 0 && query_start_loc == NULL)))
         return ORC_EINVAL;
     if (out_tokens > 0 && (k_out == NULL || v_out == NULL))
         return ORC_EINVAL;
@@ -433,8 +460,13 @@ int orc_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block
             st |= ORC_ST_BAD_COUNT;
             seq_len = 0;
         }
-        for (int64_t position = 0; position < seq_len; ++position) {
-            int64_t out_row = start + position;
+        int64_t first = 0;                                     /* R22 */
+        if (sliding_window > 0) {
+            int64_t count = (int64_t)query_start_loc[batch_index + 1] - query_start_loc[batch_index];
+            first = window_first((int32_t)seq_len, count > 0 ? count : 0, sliding_window);
+        }
+        for (int64_t position = first; position < seq_len; ++position) {
+            int64_t out_row = start + (position - first);
             if (out_row >= out_tokens) {
                 st |= ORC_ST_TOKEN_SUM;
                 break;
@@ -455,7 +487,7 @@ int orc_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block
             memcpy(ko + out_row * k_out_stride, kc + slot_id * row_bytes, (size_t)row_bytes);
             memcpy(vo + out_row * v_out_stride, vc + slot_id * row_bytes, (size_t)row_bytes);
         }
-        start += seq_len;
+        start += seq_len - first;
     }
     if (kv_start != NULL)
         kv_start[n] = start > INT32_MAX ? INT32_MAX : (int32_t)start;
@@ -906,5 +938,149 @@ int orc_prefix_evict(int32_t count, const uint64_t* hashes, const int32_t* block
         if (at >= 0 && vals[at] == blocks[i])
             vals[at] = ORC_NO_BLOCK;
     }
+    return ORC_OK;
+}
+
+/*
+ * Freeing the blocks a sliding-window group no longer needs ([CF]
+ * "allocate_slots()": before new blocks are counted, the old blocks that
+ * sliding-window attention no longer needs are released).  R23: before a step
+ * the request's next token is at position completed[row], which attends
+ * completed-W+1 .. completed; later positions attend further right.  So every
+ * block wholly before completed-W+1, logical blocks i < max(0, completed-W+1) /
+ * block_size, is freed: its id (if >= 0) is listed in freed[b*MB ..] in block
+ * order, num_freed[b] counts them, and its entry becomes -1, a hole.  W = 0
+ * frees nothing.  A bad row is flagged (BAD_ROW) and frees nothing.
+ */
+int orc_window_free(int32_t m, const int32_t* rows, const int32_t* completed,
+                    int32_t* block_table, int32_t R, int32_t MB, int32_t block_size,
+                    int32_t sliding_window, int32_t* freed, int32_t* num_freed, uint32_t* status)
+{
+    if (m < 0 || R < 0 || MB < 0 || block_size <= 0 || sliding_window < 0)
+        return ORC_EINVAL;
+    if (m > 0 && (rows == NULL || num_freed == NULL || (R > 0 && completed == NULL) ||
+                  (MB > 0 && (freed == NULL || (R > 0 && block_table == NULL)))))
+        return ORC_EINVAL;
+    uint32_t st = 0;
+    for (int32_t b = 0; b < m; ++b) {
+        int32_t r = rows[b];
+        int32_t count = 0;
+        if (r < 0 || r >= R) {
+            st |= ORC_ST_BAD_ROW;
+        } else if (sliding_window > 0) {
+            int64_t first = (int64_t)completed[r] - sliding_window + 1;
+            int64_t blocks = first > 0 ? first / block_size : 0;
+            if (blocks > MB)
+                blocks = MB;
+            for (int64_t i = 0; i < blocks; ++i) {
+                int32_t* entry = &block_table[(int64_t)r * MB + i];
+                if (*entry >= 0) {
+                    freed[(int64_t)b * MB + count] = *entry;
+                    ++count;
+                    *entry = -1;
+                }
+            }
+        }
+        num_freed[b] = count;
+    }
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * Speculative lookahead ([CF] "Scheduler.schedule()": a request advances
+ * towards num_tokens_with_spec, so speculative tokens are scheduled like any
+ * others; "allocate_slots()": the slots needed count computed, prefix-hit, new
+ * and speculative lookahead tokens, and only the missing blocks are new).
+ * R24: after this step's seq_len tokens, the next k positions seq_len ..
+ * seq_len+k-1 are where the draft tokens' K/V will go: lookahead_slots[b*k +
+ * j] is the slot of position seq_lens[b] + j by the same chain as the slot
+ * mapping (and the same flags and -1 for a bad row, a logical block >= MB or a
+ * page outside the pool).
+ */
+int orc_lookahead_slots(int32_t n, const int32_t* index_mapping, const int32_t* seq_lens,
+                        const int32_t* block_table, int32_t R, int32_t MB, int32_t block_size,
+                        int32_t num_blocks, int32_t k, int32_t* lookahead_slots, uint32_t* status)
+{
+    if (n < 0 || R < 0 || MB < 0 || block_size <= 0 || num_blocks < 0 || k < 0)
+        return ORC_EINVAL;
+    if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX + 1)
+        return ORC_EINVAL;
+    if (n > 0 && k > 0 && (index_mapping == NULL || seq_lens == NULL || lookahead_slots == NULL ||
+                           (R > 0 && MB > 0 && block_table == NULL)))
+        return ORC_EINVAL;
+    uint32_t st = 0;
+    for (int32_t b = 0; b < n; ++b) {
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t slot = -1;
+            int32_t row = index_mapping[b];
+            int64_t position = (int64_t)seq_lens[b] + j;
+            if (row < 0 || row >= R) {
+                st |= ORC_ST_BAD_ROW;
+            } else if (position < 0 || position > INT32_MAX) {
+                st |= ORC_ST_POS_OOR;
+            } else {
+                int64_t logic_block = position / block_size;
+                int64_t offset = position % block_size;
+                if (logic_block >= MB) {
+                    st |= ORC_ST_LB_OOR;
+                } else {
+                    int32_t physical_block_id = block_table[(int64_t)row * MB + logic_block];
+                    if (physical_block_id < 0 || physical_block_id >= num_blocks)
+                        st |= ORC_ST_BLOCK_OOR;
+                    else
+                        slot = (int32_t)((int64_t)physical_block_id * block_size + offset);
+                }
+            }
+            lookahead_slots[(int64_t)b * k + j] = slot;
+        }
+    }
+    if (status != NULL)
+        *status |= st;
+    return ORC_OK;
+}
+
+/*
+ * How many new blocks each request still needs ([CF] "allocate_slots()": from
+ * computed, new and lookahead tokens the needed slots, and from them the
+ * blocks actually missing).  R25: need[b] = max(0, ceil((completed[row] +
+ * num_new[b] + k) / block_size) - row_blocks[row]); row_blocks counts the
+ * row's logical blocks, holes included.  A bad row gives 0 (BAD_ROW); a
+ * negative num_new counts as 0 (BAD_COUNT).
+ */
+int orc_blocks_needed(int32_t n, const int32_t* rows, const int32_t* num_new, int32_t k,
+                      int32_t block_size, const int32_t* completed, const int32_t* row_blocks,
+                      int32_t R, int32_t* need, uint32_t* status)
+{
+    if (n < 0 || k < 0 || block_size <= 0 || R < 0)
+        return ORC_EINVAL;
+    if (n > 0 && (rows == NULL || num_new == NULL || need == NULL ||
+                  (R > 0 && (completed == NULL || row_blocks == NULL))))
+        return ORC_EINVAL;
+    uint32_t st = 0;
+    for (int32_t b = 0; b < n; ++b) {
+        int32_t r = rows[b];
+        int64_t want = 0;
+        if (r < 0 || r >= R) {
+            st |= ORC_ST_BAD_ROW;
+        } else {
+            int64_t add = num_new[b];
+            if (add < 0) {
+                st |= ORC_ST_BAD_COUNT;
+                add = 0;
+            }
+            int64_t tokens = (int64_t)completed[r] + add + k;
+            int64_t blocks = tokens <= 0 ? 0 : (tokens + block_size - 1) / block_size;
+            want = blocks - row_blocks[r];
+            if (want < 0)
+                want = 0;
+            if (want > INT32_MAX)
+                want = INT32_MAX;
+        }
+        need[b] = (int32_t)want;
+    }
+    if (status != NULL)
+        *status |= st;
     return ORC_OK;
 }

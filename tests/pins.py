@@ -868,3 +868,152 @@ def pin_prefix_model(lib, seeds=range(40)):
 PREFIX_PINS = [pin_fnv_vectors, pin_hash_closed_form, pin_hash_prefix_context,
                pin_prefix_cf_example, pin_prefix_hit_cap, pin_prefix_model]
 ALL_PINS += PREFIX_PINS
+
+
+# ---------------------------------------------------------------------------
+# sliding-window holes and speculative lookahead
+# ---------------------------------------------------------------------------
+
+def _needed_positions(prep, bi, W):
+    """Brute force: every position some new token of batch row bi attends with
+    window W (token at p attends p-W+1 .. p), as a sorted list."""
+    need = set()
+    for t in range(int(prep["query_start_loc"][bi]), int(prep["query_start_loc"][bi + 1])):
+        p = int(prep["positions"][t])
+        need.update(q for q in range(p - W + 1, p + 1) if q >= 0)
+    return sorted(need)
+
+
+def pin_window_bruteforce(lib, seeds=range(80)):
+    """Sliding windows on tiny random batches: the blocks window_free releases
+    are exactly those wholly before every position the step's tokens attend
+    (found by enumeration, no division); after freeing, the visible pages copy
+    the holes unflagged while full attention flags them; the windowed read
+    returns exactly the attended positions, request after request."""
+    for seed in seeds:
+        b = workloads.random_tiny(seed)
+        g = b.groups[0]
+        bs = g.block_size
+        W = int(np.random.default_rng(seed).integers(1, 3 * bs + 5))
+        bt = g.block_table.copy()
+        fr = oracle.window_free(b.sched_rows, b.completed, bt, bs, W, lib=lib)
+        assert fr["rc"] == 0 and fr["status"] == 0
+        prep = oracle.prepare_batch(b.sched_rows, b.num_scheduled, b.completed, b.token_ids, lib=lib)
+        order = prep["index_mapping"].tolist()
+        for i, r in enumerate(b.sched_rows.tolist()):
+            bi = order.index(r)
+            need = _needed_positions(prep, bi, W)
+            first_need = need[0] if need else int(b.completed[r])
+            # wholly before: every slot position of the block is below first_need
+            gone = [blk for blk_i, blk in enumerate(g.block_table[r])
+                    if blk >= 0 and all(blk_i * bs + o < first_need for o in range(bs))
+                    and int(b.completed[r]) - W + 1 > 0]
+            _eq(fr["freed"][i, :fr["num_freed"][i]], gone, f"seed {seed} freed of row {r}")
+            for blk_i in range(g.max_blocks):
+                want = -1 if g.block_table[r, blk_i] in gone and g.block_table[r, blk_i] >= 0 \
+                    and all(blk_i * bs + o < first_need for o in range(bs)) else g.block_table[r, blk_i]
+                assert bt[r, blk_i] == want, (seed, r, blk_i)
+        full = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                           prep["seq_lens"], prep["positions"], bt, bs,
+                                           g.num_blocks, lib=lib)
+        win = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                          prep["seq_lens"], prep["positions"], bt, bs,
+                                          g.num_blocks, sliding_window=W, lib=lib)
+        _eq(win["slot_mapping"], full["slot_mapping"], f"seed {seed} slots")
+        _eq(win["input_block_tables"], full["input_block_tables"], f"seed {seed} pages")
+        assert win["status"] == 0, (seed, win["status"])
+        holes_visible = any(
+            (full["input_block_tables"][bi, :-(-int(prep["seq_lens"][bi]) // bs)] == -1).any()
+            for bi in range(b.n))
+        assert bool(full["status"] & oracle.ST_BLOCK_OOR) == holes_visible, seed
+        # the windowed read: exactly the attended positions, from a patterned cache
+        kc = (np.arange(g.num_slots * 2, dtype=np.uint32) * 2654435761 >> 16).astype(np.uint16)
+        kc = kc.reshape(g.num_slots, 2, 1)
+        out = oracle.gather_kv(prep["seq_lens"], win["input_block_tables"], bs, g.num_blocks, kc, kc,
+                               query_start_loc=prep["query_start_loc"], sliding_window=W, lib=lib)
+        assert out["rc"] == 0 and out["status"] == 0, (seed, out["status"])
+        rows_want = []
+        for bi in range(b.n):
+            need = _needed_positions(prep, bi, W)
+            assert out["kv_start"][bi + 1] - out["kv_start"][bi] == len(need)
+            r = int(prep["index_mapping"][bi])
+            for p in need:
+                space = [int(x) * bs + o for x in g.block_table[r] for o in range(bs)]
+                rows_want.append(kc[space[p]])
+        if rows_want:
+            _eq(out["k"], np.stack(rows_want), f"seed {seed} windowed read")
+
+
+def pin_window_zero_is_full_attention(lib):
+    """W = 0 frees nothing and reads every position, as without a window."""
+    b = workloads.make("seeded_16req")
+    g = b.groups[0]
+    bt = g.block_table.copy()
+    fr = oracle.window_free(b.sched_rows, b.completed, bt, g.block_size, 0, lib=lib)
+    assert fr["num_freed"].sum() == 0 and np.array_equal(bt, g.block_table)
+    prep, groups = oracle.run_chain(b, lib=lib)
+    a = oracle.gather_kv(prep["seq_lens"], groups[0]["input_block_tables"], g.block_size,
+                         g.num_blocks, groups[0]["k_cache"], groups[0]["v_cache"], lib=lib)
+    w = oracle.gather_kv(prep["seq_lens"], groups[0]["input_block_tables"], g.block_size,
+                         g.num_blocks, groups[0]["k_cache"], groups[0]["v_cache"],
+                         query_start_loc=prep["query_start_loc"], sliding_window=0, lib=lib)
+    _eq(a["k"], w["k"], "W=0 read")
+
+
+def pin_lookahead(lib, seeds=range(60)):
+    """The lookahead slots of a step are the slots the next step would write
+    with k new tokens per request (the oracle's slot mapping of that step),
+    and by enumeration of each request's address space."""
+    for seed in seeds:
+        b = workloads.random_tiny(seed)
+        g = b.groups[0]
+        k = int(np.random.default_rng(seed).integers(0, 5))
+        prep = oracle.prepare_batch(b.sched_rows, b.num_scheduled, b.completed, b.token_ids, lib=lib)
+        la = oracle.lookahead_slots(prep["index_mapping"], prep["seq_lens"], g.block_table,
+                                    g.block_size, g.num_blocks, k, lib=lib)
+        assert la["rc"] == 0
+        # the following step: completed = seq_len, k tokens each
+        comp2 = b.completed.copy()
+        comp2[prep["index_mapping"]] = prep["seq_lens"]
+        nxt = oracle.prepare_batch(prep["index_mapping"], np.full(b.n, k, np.int32), comp2,
+                                   np.zeros((b.R, 0), np.int32), with_input_ids=False, lib=lib)
+        sm = oracle.compute_slot_mapping(nxt["index_mapping"], nxt["query_start_loc"],
+                                         nxt["seq_lens"], nxt["positions"], g.block_table,
+                                         g.block_size, g.num_blocks, with_ibt=False, lib=lib)
+        assert la["status"] == sm["status"], (seed, la["status"], sm["status"])
+        # the next step orders its batch by row (equal counts): map back
+        nxt_rows = nxt["index_mapping"].tolist()
+        for bi, r in enumerate(prep["index_mapping"].tolist()):
+            j = nxt_rows.index(r)
+            q0 = int(nxt["query_start_loc"][j])
+            _eq(la["slots"][bi], sm["slot_mapping"][q0:q0 + k], f"seed {seed} row {r}")
+            space = [(-1 if x < 0 or x >= g.num_blocks else int(x) * g.block_size + o)
+                     for x in g.block_table[r] for o in range(g.block_size)]
+            s0 = int(prep["seq_lens"][bi])
+            want = [space[p] if p < len(space) else -1 for p in range(s0, s0 + k)]
+            _eq(la["slots"][bi], want, f"seed {seed} row {r} by enumeration")
+
+
+def pin_blocks_needed(lib, seeds=range(60)):
+    """caffein.top: B has 8 tokens computed (P1, P2 reused), 2 new, block size
+    4 and two blocks: only B3 is new (one block).  Random cases against a count
+    of the distinct blocks the positions 0 .. completed+new+k-1 touch."""
+    r = oracle.blocks_needed([1], [2], 0, 4, [0, 8], [0, 2], lib=lib)
+    assert r["need"].tolist() == [1] and r["status"] == 0
+    for seed in seeds:
+        rng = np.random.default_rng(900 + seed)
+        R, n = 10, int(rng.integers(1, 8))
+        rows = rng.choice(R, n, replace=False)
+        comp = rng.integers(0, 60, R).astype(np.int32)
+        rb = rng.integers(0, 20, R).astype(np.int32)
+        new = rng.integers(0, 30, n).astype(np.int32)
+        k, bs = int(rng.integers(0, 6)), int(rng.choice([1, 3, 4, 16]))
+        got = oracle.blocks_needed(rows, new, k, bs, comp, rb, lib=lib)
+        for i, r_ in enumerate(rows):
+            touched = {p // bs for p in range(int(comp[r_] + new[i] + k))}
+            assert got["need"][i] == max(0, len(touched) - int(rb[r_])), (seed, i)
+
+
+NEXT4_PINS = [pin_window_bruteforce, pin_window_zero_is_full_attention, pin_lookahead,
+              pin_blocks_needed]
+ALL_PINS += NEXT4_PINS

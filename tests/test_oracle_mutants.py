@@ -128,6 +128,24 @@ MUTANTS = {
     "evict_unconditional": (
         "        if (at >= 0 && vals[at] == blocks[i])",
         "        if (at >= 0)"),
+    "window_first_off_by_one": (
+        "    int64_t first = (int64_t)seq_len - count - window + 1;",
+        "    int64_t first = (int64_t)seq_len - count - window;"),
+    "window_hole_flagged": (
+        "                int hole = i < first_block && blk == -1;                      /* R21 */",
+        "                int hole = 0;"),
+    "window_read_from_zero": (
+        "            first = window_first((int32_t)seq_len, count > 0 ? count : 0, sliding_window);",
+        "            first = 0 * window_first((int32_t)seq_len, count > 0 ? count : 0, sliding_window);"),
+    "window_free_one_too_many": (
+        "            int64_t blocks = first > 0 ? first / block_size : 0;",
+        "            int64_t blocks = first > 0 ? (first + block_size - 1) / block_size : 0;"),
+    "lookahead_from_last_token": (
+        "            int64_t position = (int64_t)seq_lens[b] + j;",
+        "            int64_t position = (int64_t)seq_lens[b] + j - 1;"),
+    "blocks_needed_ignores_lookahead": (
+        "            int64_t tokens = (int64_t)completed[r] + add + k;",
+        "            int64_t tokens = (int64_t)completed[r] + add;"),
     "pool_fifo": (
         "        int32_t r = free_rows[*num_free - 1];",
         "        int32_t r = free_rows[R - *num_free];"),
