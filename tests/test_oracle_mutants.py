@@ -93,8 +93,8 @@ MUTANTS = {
         "int64_t slot_id = (int64_t)physical_block_id * block_size + offset;",
         "int64_t slot_id = (int64_t)physical_block_id * block_size;"),
     "gather_start_not_running": (
-        "        start += seq_len;",
-        "        start = seq_len;"),
+        "        start += seq_len - first;",
+        "        start = seq_len - first;"),
     "gather_page_of_next_request": (
         "input_block_tables[(int64_t)batch_index * MB + logic_block];",
         "input_block_tables[((int64_t)batch_index * MB + logic_block + MB) % ((int64_t)n * MB)];"),
@@ -102,8 +102,8 @@ MUTANTS = {
         "memcpy(vo + out_row * v_out_stride, vc + slot_id * row_bytes, (size_t)row_bytes);",
         "memcpy(vo + out_row * v_out_stride, kc + slot_id * row_bytes, (size_t)row_bytes);"),
     "gather_one_row_short": (
-        "        for (int64_t position = 0; position < seq_len; ++position) {",
-        "        for (int64_t position = 0; position + 1 < seq_len; ++position) {"),
+        "        for (int64_t position = first; position < seq_len; ++position) {",
+        "        for (int64_t position = first; position + 1 < seq_len; ++position) {"),
     "hash_chain_drops_parent": (
         "            s = s * 1099511628211ull + c;",
         "            s = c;"),
