@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 /* Return codes. */
 #define PKV_OK            0
@@ -140,21 +140,31 @@ int pkv_prepare_batch(int32_t n, int32_t T,
  *   input_block_tables[n * MB]  (may be NULL) row b = the first
  *                        ceil(seq_lens[b] / block_size) entries of the request's
  *                        block-table row; entries past them are not written.
+ *   sliding_window       0 for full attention; W > 0 for a sliding-window
+ *                        group (the token at position p attends p-W+1 .. p).
+ *                        Batch row b (count c = query_start_loc[b+1] -
+ *                        query_start_loc[b], seq_len s) then needs positions
+ *                        from max(0, s - c - W + 1) on; its visible pages
+ *                        before that position's block may be -1 holes left by
+ *                        pkv_window_free ("allocate_slots()" of the caffein.top
+ *                        page: blocks a sliding-window group no longer needs
+ *                        are freed).
  * Data errors give slot -1: row outside [0, R) (BAD_ROW), position < 0
  *   (POS_OOR), logical block >= MB (LB_OOR), block id outside [0, num_blocks)
  *   (BLOCK_OOR).  Tokens outside [query_start_loc[0], query_start_loc[n]) get
  *   slot -1 unflagged.  In input_block_tables, visible entries are copied as they
- *   are (an out-of-pool one flags BLOCK_OOR), a visible count above MB flags
- *   LB_OOR and is cut to MB, a bad row's output row is not written.
+ *   are (an out-of-pool one flags BLOCK_OOR, except a -1 hole before the
+ *   window), a visible count above MB flags LB_OOR and is cut to MB, a bad
+ *   row's output row is not written.
  * Host errors: EINVAL for n < 0, T < 0, R < 0, MB < 0, num_blocks < 0,
- *   block_size <= 0, num_blocks * block_size > 2^31, or a NULL pointer an
- *   enabled output needs; EUNSUPPORTED for n > PKV_MAX_BATCH.
+ *   block_size <= 0, sliding_window < 0, num_blocks * block_size > 2^31, or a
+ *   NULL pointer an enabled output needs; EUNSUPPORTED for n > PKV_MAX_BATCH.
  */
 int pkv_compute_slot_mapping(int32_t n, int32_t T,
                              const int32_t* index_mapping, const int32_t* query_start_loc,
                              const int32_t* seq_lens, const int32_t* positions,
                              const int32_t* block_table, int32_t R, int32_t MB,
-                             int32_t block_size, int32_t num_blocks,
+                             int32_t block_size, int32_t num_blocks, int32_t sliding_window,
                              int32_t* slot_mapping, int32_t* input_block_tables,
                              uint32_t* status, void* stream);
 
@@ -196,9 +206,9 @@ int pkv_scatter_kv(int32_t T, int64_t row_bytes,
  *   slot_mapping[T] (out), input_block_tables[n * MB] (out, may be NULL)
  *   k, k_stride, v, v_stride, k_cache, v_cache, num_slots, row_bytes
  *                                                   as for pkv_scatter_kv
- *   reserved                                        must be 0
+ *   sliding_window                                  as for pkv_compute_slot_mapping
  * Host errors: those of the three calls for the same arguments; EINVAL also for
- *   num_groups < 0, groups == NULL with num_groups > 0, or reserved != 0.
+ *   num_groups < 0 or groups == NULL with num_groups > 0.
  */
 #define PKV_STEP_MAX_BATCH 512
 #define PKV_STEP_MAX_GROUPS 4
@@ -218,7 +228,7 @@ typedef struct pkv_group {
     int32_t MB;
     int32_t block_size;
     int32_t num_blocks;
-    int32_t reserved;
+    int32_t sliding_window;     /* 0: full attention */
 } pkv_group;
 
 int pkv_step(int32_t n, int32_t T,
@@ -241,6 +251,14 @@ int pkv_step(int32_t n, int32_t T,
  *
  * Inputs (device):
  *   seq_lens[n]             as produced by pkv_prepare_batch
+ *   query_start_loc[n+1], sliding_window
+ *                           sliding_window 0: every position 0 .. seq_len-1 is
+ *                           read (query_start_loc may be NULL).  W > 0: only
+ *                           the positions some new token attends, from
+ *                           first = max(0, seq_len - count - W + 1) on (count
+ *                           from query_start_loc, as for
+ *                           pkv_compute_slot_mapping), to rows kv_start[b] +
+ *                           p - first; kv_start then sums seq_len - first.
  *   input_block_tables[n * MB]  visible pages, as produced by
  *                           pkv_compute_slot_mapping (entries past
  *                           ceil(seq_len / block_size) are never read)
@@ -257,16 +275,54 @@ int pkv_step(int32_t n, int32_t T,
  *   counts as 0 (BAD_COUNT); a logical block >= MB (LB_OOR); a page outside
  *   [0, num_blocks) (BLOCK_OOR); rows at or past out_tokens (TOKEN_SUM).
  * Host errors: EINVAL for negative sizes, block_size <= 0, row_bytes <= 0,
- *   strides < row_bytes, num_blocks * block_size > 2^31, or a NULL pointer
- *   that data is needed from; EALIGN unless row_bytes, the strides and every
+ *   sliding_window < 0, strides < row_bytes, num_blocks * block_size > 2^31,
+ *   or a NULL pointer that data is needed from; EALIGN unless row_bytes, the strides and every
  *   K/V pointer are multiples of 16 bytes; EUNSUPPORTED for n > PKV_MAX_BATCH,
  *   out_tokens > INT32_MAX or rows of 2^23 or more 16-byte chunks.
  */
-int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
+int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* query_start_loc,
+                  int32_t sliding_window, const int32_t* input_block_tables,
                   int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
                   const void* k_cache, const void* v_cache, int64_t out_tokens, void* k_out,
                   int64_t k_out_stride, void* v_out, int64_t v_out_stride, int32_t* kv_start,
                   uint32_t* status, void* stream);
+
+/*
+ * Allocation-side variants ("从源码读 vLLM Scheduler：一轮调度如何分配请求与 KV
+ * Cache", caffein.top, "Scheduler.schedule()" and "allocate_slots()": a
+ * request advances towards num_tokens_with_spec, so speculative draft tokens
+ * are scheduled like any others; the slots needed count computed, prefix-hit,
+ * new and speculative lookahead tokens; a sliding-window group first frees the
+ * blocks its attention no longer needs, and only the missing blocks are new).
+ *
+ * pkv_window_free: before a step, for each row rows[b], the blocks wholly
+ *   before position completed[row] - W + 1 (logical blocks i < max(0,
+ *   completed - W + 1) / block_size) are released: each entry >= 0 is listed
+ *   in freed[b*MB ..] in block order, num_freed[b] counts them, and the entry
+ *   becomes -1 (a hole).  W = 0 frees nothing.  Rows must be distinct.  Data
+ *   errors: a bad row frees nothing (BAD_ROW).
+ * pkv_lookahead_slots: lookahead_slots[b*k + j] = the slot of position
+ *   seq_lens[b] + j of batch row b (j < k), where the next step's draft
+ *   tokens go; same chain, flags and -1 as pkv_compute_slot_mapping.
+ * pkv_blocks_needed: need[b] = max(0, ceil((completed[row] + num_new[b] + k) /
+ *   block_size) - row_blocks[row]) for row = rows[b]: the new blocks the
+ *   request must get for this step's tokens and k lookahead tokens.  Data
+ *   errors: a bad row gives 0 (BAD_ROW); num_new < 0 counts as 0 (BAD_COUNT).
+ * Host errors: EINVAL for negative sizes, block_size <= 0, sliding_window <
+ *   0, k < 0, num_blocks * block_size > 2^31, or a NULL pointer that data is
+ *   needed from.
+ */
+int pkv_window_free(int32_t m, const int32_t* rows, const int32_t* completed,
+                    int32_t* block_table, int32_t R, int32_t MB, int32_t block_size,
+                    int32_t sliding_window, int32_t* freed, int32_t* num_freed,
+                    uint32_t* status, void* stream);
+int pkv_lookahead_slots(int32_t n, const int32_t* index_mapping, const int32_t* seq_lens,
+                        const int32_t* block_table, int32_t R, int32_t MB, int32_t block_size,
+                        int32_t num_blocks, int32_t k, int32_t* lookahead_slots,
+                        uint32_t* status, void* stream);
+int pkv_blocks_needed(int32_t n, const int32_t* rows, const int32_t* num_new, int32_t k,
+                      int32_t block_size, const int32_t* completed, const int32_t* row_blocks,
+                      int32_t R, int32_t* need, uint32_t* status, void* stream);
 
 /*
  * Prefix-cache block hashes ("从源码读 vLLM Scheduler：一轮调度如何分配请求与

@@ -7,7 +7,9 @@ same call names: ``prepare_batch``, ``compute_slot_mapping`` (one call per
 KV-cache group), ``scatter_kv`` (one call per group and layer) and ``step``
 (all of them for a step's first layer, in one launch), the read side
 ``gather_kv`` (each request's KV range through its visible pages), the
-prefix-cache block hashes and index (``hash_blocks``, ``prefix_*``), the persistent
+prefix-cache block hashes and index (``hash_blocks``, ``prefix_*``), the
+sliding-window and speculative-lookahead variants (``window_free``,
+``lookahead_slots``, ``blocks_needed``), the persistent
 request-state updates ``add_requests``, ``append_blocks`` and
 ``advance_state`` and the host-side ``RowPool`` that hands out state rows.  It takes
 torch tensors for device memory and uses torch's current HIP stream; every
@@ -18,6 +20,7 @@ from __future__ import annotations
 
 _API = ("prepare_batch", "compute_slot_mapping", "scatter_kv", "step", "gather_kv",
         "hash_blocks", "prefix_clear", "prefix_lookup", "prefix_insert", "prefix_evict",
+        "window_free", "lookahead_slots", "blocks_needed",
         "NO_BLOCK",
         "prepared_gather_kv", "add_requests",
         "append_blocks", "advance_state", "prepared_prepare_batch",

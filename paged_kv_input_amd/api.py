@@ -44,7 +44,7 @@ class Group(ctypes.Structure):
         ("block_table", _P), ("slot_mapping", _P), ("input_block_tables", _P),
         ("k", _P), ("v", _P), ("k_cache", _P), ("v_cache", _P),
         ("k_stride", _I64), ("v_stride", _I64), ("num_slots", _I64), ("row_bytes", _I64),
-        ("MB", _I32), ("block_size", _I32), ("num_blocks", _I32), ("reserved", _I32),
+        ("MB", _I32), ("block_size", _I32), ("num_blocks", _I32), ("sliding_window", _I32),
     ]
 
 
@@ -67,15 +67,22 @@ def load_library(path: str = library_path) -> ctypes.CDLL:
                                       _P, _P, _P, _P, _P, _P, _P]
     lib.pkv_compute_slot_mapping.restype = ctypes.c_int
     lib.pkv_compute_slot_mapping.argtypes = [_I32, _I32, _P, _P, _P, _P, _P, _I32, _I32,
-                                             _I32, _I32, _P, _P, _P, _P]
+                                             _I32, _I32, _I32, _P, _P, _P, _P]
     lib.pkv_scatter_kv.restype = ctypes.c_int
     lib.pkv_scatter_kv.argtypes = [_I32, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _P, _P]
     lib.pkv_step.restype = ctypes.c_int
     lib.pkv_step.argtypes = [_I32, _I32, _P, _P, _P, _I32, _P, _I64, _I32, _P, _P, _P, _P, _P,
                              _I32, ctypes.POINTER(Group), _P, _P]
     lib.pkv_gather_kv.restype = ctypes.c_int
-    lib.pkv_gather_kv.argtypes = [_I32, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P, _I64,
-                                  _P, _I64, _P, _P, _P]
+    lib.pkv_gather_kv.argtypes = [_I32, _P, _P, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _I64,
+                                  _P, _I64, _P, _I64, _P, _P, _P]
+    lib.pkv_window_free.restype = ctypes.c_int
+    lib.pkv_window_free.argtypes = [_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
+    lib.pkv_lookahead_slots.restype = ctypes.c_int
+    lib.pkv_lookahead_slots.argtypes = [_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P,
+                                        _P]
+    lib.pkv_blocks_needed.restype = ctypes.c_int
+    lib.pkv_blocks_needed.argtypes = [_I32, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P]
     lib.pkv_hash_blocks.restype = ctypes.c_int
     lib.pkv_hash_blocks.argtypes = [_I32, _P, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P]
     lib.pkv_prefix_clear.restype = ctypes.c_int
@@ -220,11 +227,14 @@ def prepared_compute_slot_mapping(index_mapping: torch.Tensor, query_start_loc: 
                                   block_table: torch.Tensor, block_size: int, num_blocks: int,
                                   *, slot_mapping: torch.Tensor,
                                   input_block_tables: Optional[torch.Tensor] = None,
-                                  status: Optional[torch.Tensor] = None):
+                                  status: Optional[torch.Tensor] = None,
+                                  sliding_window: int = 0):
     """Write slots (and optionally visible pages) of ONE KV-cache group.
 
     block_table: int32 [R, MB] contiguous; slot_mapping: int32 [T];
-    input_block_tables: int32 [n, MB] or None.
+    input_block_tables: int32 [n, MB] or None; sliding_window: 0 for full
+    attention, else the group's window (visible pages before every window of
+    the step may then be -1 holes).
     """
     n = index_mapping.shape[0]
     T = positions.shape[0]
@@ -240,8 +250,8 @@ def prepared_compute_slot_mapping(index_mapping: torch.Tensor, query_start_loc: 
     if input_block_tables is not None:
         _idx("seq_lens", seq_lens, (n,))
     args = (n, T, _ptr(index_mapping), _ptr(query_start_loc), _ptr(seq_lens), _ptr(positions),
-            _ptr(block_table), R, MB, int(block_size), int(num_blocks), _ptr(slot_mapping),
-            _ptr(input_block_tables), _ptr(status))
+            _ptr(block_table), R, MB, int(block_size), int(num_blocks), int(sliding_window),
+            _ptr(slot_mapping), _ptr(input_block_tables), _ptr(status))
     return _prepared("compute_slot_mapping", _lib.pkv_compute_slot_mapping, args,
                      (index_mapping, query_start_loc, seq_lens, positions, block_table,
                       slot_mapping, input_block_tables, status))
@@ -283,7 +293,8 @@ def prepared_gather_kv(seq_lens: torch.Tensor, input_block_tables: torch.Tensor,
                        block_size: int, num_blocks: int, k_cache: torch.Tensor,
                        v_cache: torch.Tensor, *, k_out: torch.Tensor, v_out: torch.Tensor,
                        kv_start: Optional[torch.Tensor] = None,
-                       status: Optional[torch.Tensor] = None):
+                       status: Optional[torch.Tensor] = None,
+                       query_start_loc: Optional[torch.Tensor] = None, sliding_window: int = 0):
     """Copy positions 0 .. seq_len-1 of every batch row, read through its
     visible pages, to rows kv_start[b] + p of k_out / v_out (ONE group, ONE layer).
 
@@ -291,6 +302,8 @@ def prepared_gather_kv(seq_lens: torch.Tensor, input_block_tables: torch.Tensor,
     contiguous [num_slots, ...] with num_slots >= num_blocks * block_size;
     k_out, v_out: [out_tokens, ...] with rows of the cache's size (contiguous
     rows, the token stride may be larger); kv_start: int32 [n+1] or None.
+    sliding_window > 0 reads only the positions some new token attends
+    (query_start_loc [n+1] is then required).
     """
     n = seq_lens.shape[0]
     _idx("seq_lens", seq_lens, (n,))
@@ -299,16 +312,18 @@ def prepared_gather_kv(seq_lens: torch.Tensor, input_block_tables: torch.Tensor,
         raise ValueError("input_block_tables must be [n, MB]")
     MB = input_block_tables.shape[1]
     _idx("kv_start", kv_start, (n + 1,), optional=True)
+    _idx("query_start_loc", query_start_loc, (n + 1,), optional=not sliding_window)
     out_tokens = k_out.shape[0]
     row_bytes, (ks, vs) = _kv_layout("", k_out, v_out, k_cache, v_cache, out_tokens)
     if k_cache.shape[0] < int(num_blocks) * int(block_size):
         raise ValueError("the caches hold fewer than num_blocks * block_size slots")
-    args = (n, _ptr(seq_lens), _ptr(input_block_tables), MB, int(block_size), int(num_blocks),
+    args = (n, _ptr(seq_lens), _ptr(query_start_loc), int(sliding_window),
+            _ptr(input_block_tables), MB, int(block_size), int(num_blocks),
             row_bytes, _ptr(k_cache), _ptr(v_cache), out_tokens, _ptr(k_out), ks, _ptr(v_out), vs,
             _ptr(kv_start), _ptr(_status(status)))
     return _prepared("gather_kv", _lib.pkv_gather_kv, args,
                      (seq_lens, input_block_tables, k_cache, v_cache, k_out, v_out, kv_start,
-                      status))
+                      status, query_start_loc))
 
 
 def _kv_layout(name_k, k, v, k_cache, v_cache, T):
@@ -339,7 +354,8 @@ def step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, completed: torch
     compute_slot_mapping and scatter_kv, with identical results.
 
     groups: sequence of dicts with keys block_table, block_size, num_blocks,
-    slot_mapping, input_block_tables (or None), k, v, k_cache, v_cache.
+    slot_mapping, input_block_tables (or None), k, v, k_cache, v_cache, and
+    optionally sliding_window (default 0, full attention).
     """
     prepared_step(sched_rows, num_scheduled, completed, token_ids, num_tokens, groups,
                   index_mapping=index_mapping, query_start_loc=query_start_loc,
@@ -392,7 +408,7 @@ def prepared_step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, complet
                        _ptr(g.get("input_block_tables")), g["k"].data_ptr(), g["v"].data_ptr(),
                        g["k_cache"].data_ptr(), g["v_cache"].data_ptr(), ks, vs,
                        g["k_cache"].shape[0], row_bytes, MB, int(g["block_size"]),
-                       int(g["num_blocks"]), 0)
+                       int(g["num_blocks"]), int(g.get("sliding_window", 0)))
     args = (n, T, _ptr(sched_rows), _ptr(num_scheduled), _ptr(completed), R, _ptr(token_ids),
             stride, L, _ptr(index_mapping), _ptr(query_start_loc), _ptr(seq_lens),
             _ptr(positions), _ptr(input_ids), len(groups), arr, _ptr(status))
@@ -658,3 +674,66 @@ def prefix_evict(hashes, blocks, keys, vals, *, stream=None) -> None:
                                _stream(stream))
     if rc != OK:
         raise PagedKVError("prefix_evict", rc)
+
+
+# -- allocation-side variants: sliding-window holes, speculative lookahead ------
+def window_free(rows, completed, block_table, block_size, sliding_window, *, freed, num_freed,
+                status=None, stream=None) -> None:
+    """Release the blocks wholly before every window (pkv_window_free):
+    block_table [R, MB] is updated in place (freed entries become -1), freed
+    [m, MB] lists each row's released ids in block order, num_freed [m] counts
+    them."""
+    m = rows.shape[0]
+    _idx("rows", rows, (m,))
+    _idx("completed", completed)
+    R = completed.shape[0]
+    _idx("block_table", block_table)
+    if block_table.dim() != 2 or block_table.shape[0] != R:
+        raise ValueError("block_table must be [R, MB]")
+    MB = block_table.shape[1]
+    _idx("freed", freed, (m, MB))
+    _idx("num_freed", num_freed, (m,))
+    rc = _lib.pkv_window_free(m, _ptr(rows), _ptr(completed), _ptr(block_table), R, MB,
+                              int(block_size), int(sliding_window), _ptr(freed), _ptr(num_freed),
+                              _ptr(_status(status)), _stream(stream))
+    if rc != OK:
+        raise PagedKVError("window_free", rc)
+
+
+def lookahead_slots(index_mapping, seq_lens, block_table, block_size, num_blocks, *, out,
+                    status=None, stream=None) -> None:
+    """Slots of the k = out.shape[1] positions after each request's seq_len
+    (pkv_lookahead_slots)."""
+    n = index_mapping.shape[0]
+    _idx("index_mapping", index_mapping, (n,))
+    _idx("seq_lens", seq_lens, (n,))
+    _idx("block_table", block_table)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [R, MB]")
+    R, MB = block_table.shape
+    _idx("out", out)
+    if out.dim() != 2 or out.shape[0] != n:
+        raise ValueError("out must be [n, k]")
+    rc = _lib.pkv_lookahead_slots(n, _ptr(index_mapping), _ptr(seq_lens), _ptr(block_table), R,
+                                  MB, int(block_size), int(num_blocks), out.shape[1], _ptr(out),
+                                  _ptr(_status(status)), _stream(stream))
+    if rc != OK:
+        raise PagedKVError("lookahead_slots", rc)
+
+
+def blocks_needed(rows, num_new, k, block_size, completed, row_blocks, *, need, status=None,
+                  stream=None) -> None:
+    """New blocks each request needs for its new and k lookahead tokens
+    (pkv_blocks_needed)."""
+    n = rows.shape[0]
+    _idx("rows", rows, (n,))
+    _idx("num_new", num_new, (n,))
+    _idx("completed", completed)
+    R = completed.shape[0]
+    _idx("row_blocks", row_blocks, (R,))
+    _idx("need", need, (n,))
+    rc = _lib.pkv_blocks_needed(n, _ptr(rows), _ptr(num_new), int(k), int(block_size),
+                                _ptr(completed), _ptr(row_blocks), R, _ptr(need),
+                                _ptr(_status(status)), _stream(stream))
+    if rc != OK:
+        raise PagedKVError("blocks_needed", rc)

@@ -39,10 +39,11 @@ int check_prepare(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t
 int check_slots(int32_t n, int32_t T, const int32_t* index_mapping,
                 const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
                 const int32_t* block_table, int32_t R, int32_t MB, int32_t block_size,
-                int32_t num_blocks, const int32_t* slot_mapping,
+                int32_t num_blocks, int32_t sliding_window, const int32_t* slot_mapping,
                 const int32_t* input_block_tables)
 {
-    if (n < 0 || T < 0 || R < 0 || MB < 0 || num_blocks < 0 || block_size <= 0)
+    if (n < 0 || T < 0 || R < 0 || MB < 0 || num_blocks < 0 || block_size <= 0 ||
+        sliding_window < 0)
         return PKV_EINVAL;
     if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX + 1)
         return PKV_EINVAL;
@@ -102,17 +103,17 @@ int pkv_compute_slot_mapping(int32_t n, int32_t T, const int32_t* index_mapping,
                              const int32_t* query_start_loc, const int32_t* seq_lens,
                              const int32_t* positions, const int32_t* block_table, int32_t R,
                              int32_t MB, int32_t block_size, int32_t num_blocks,
-                             int32_t* slot_mapping, int32_t* input_block_tables,
-                             uint32_t* status, void* stream)
+                             int32_t sliding_window, int32_t* slot_mapping,
+                             int32_t* input_block_tables, uint32_t* status, void* stream)
 {
     const int rc = check_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,
-                               block_table, R, MB, block_size, num_blocks, slot_mapping,
-                               input_block_tables);
+                               block_table, R, MB, block_size, num_blocks, sliding_window,
+                               slot_mapping, input_block_tables);
     if (rc != PKV_OK)
         return rc;
     return from_hip(pkv::launch_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,
-                                      block_table, R, MB, block_size, num_blocks, slot_mapping,
-                                      input_block_tables, status,
+                                      block_table, R, MB, block_size, num_blocks, sliding_window,
+                                      slot_mapping, input_block_tables, status,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -143,10 +144,8 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
         return rc;
     for (int i = 0; i < num_groups; ++i) {
         const pkv_group& g = groups[i];
-        if (g.reserved != 0)
-            return PKV_EINVAL;
         rc = check_slots(n, T, index_mapping, query_start_loc, seq_lens, positions, g.block_table,
-                         R, g.MB, g.block_size, g.num_blocks, g.slot_mapping,
+                         R, g.MB, g.block_size, g.num_blocks, g.sliding_window, g.slot_mapping,
                          g.input_block_tables);
         if (rc != PKV_OK)
             return rc;
@@ -172,8 +171,8 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
     for (int i = 0; e == hipSuccess && i < num_groups; ++i) {
         const pkv_group& g = groups[i];
         e = pkv::launch_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,
-                              g.block_table, R, g.MB, g.block_size, g.num_blocks, g.slot_mapping,
-                              g.input_block_tables, status, s);
+                              g.block_table, R, g.MB, g.block_size, g.num_blocks,
+                              g.sliding_window, g.slot_mapping, g.input_block_tables, status, s);
     }
     for (int i = 0; e == hipSuccess && i < num_groups; ++i) {
         const pkv_group& g = groups[i];
@@ -183,18 +182,21 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
     return from_hip(e);
 }
 
-int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
+int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* query_start_loc,
+                  int32_t sliding_window, const int32_t* input_block_tables,
                   int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
                   const void* k_cache, const void* v_cache, int64_t out_tokens, void* k_out,
                   int64_t k_out_stride, void* v_out, int64_t v_out_stride, int32_t* kv_start,
                   uint32_t* status, void* stream)
 {
     if (n < 0 || MB < 0 || block_size <= 0 || num_blocks < 0 || row_bytes <= 0 ||
-        out_tokens < 0 || k_out_stride < row_bytes || v_out_stride < row_bytes)
+        out_tokens < 0 || k_out_stride < row_bytes || v_out_stride < row_bytes ||
+        sliding_window < 0)
         return PKV_EINVAL;
     if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX + 1)
         return PKV_EINVAL;
-    if (n > 0 && (seq_lens == nullptr || (MB > 0 && input_block_tables == nullptr)))
+    if (n > 0 && (seq_lens == nullptr || (MB > 0 && input_block_tables == nullptr) ||
+                  (sliding_window > 0 && query_start_loc == nullptr)))
         return PKV_EINVAL;
     if (out_tokens > 0 && (k_out == nullptr || v_out == nullptr))
         return PKV_EINVAL;
@@ -205,10 +207,57 @@ int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* input_block
         return PKV_EALIGN;
     if (n > PKV_MAX_BATCH || out_tokens > INT32_MAX || row_bytes / 16 >= (int64_t)1 << 23)
         return PKV_EUNSUPPORTED;
-    return from_hip(pkv::launch_gather(n, seq_lens, input_block_tables, MB, block_size, num_blocks,
+    return from_hip(pkv::launch_gather(n, seq_lens, query_start_loc, sliding_window,
+                                       input_block_tables, MB, block_size, num_blocks,
                                        row_bytes, k_cache, v_cache, (int32_t)out_tokens, k_out,
                                        k_out_stride, v_out, v_out_stride, kv_start, status,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int pkv_window_free(int32_t m, const int32_t* rows, const int32_t* completed,
+                    int32_t* block_table, int32_t R, int32_t MB, int32_t block_size,
+                    int32_t sliding_window, int32_t* freed, int32_t* num_freed,
+                    uint32_t* status, void* stream)
+{
+    if (m < 0 || R < 0 || MB < 0 || block_size <= 0 || sliding_window < 0)
+        return PKV_EINVAL;
+    if (m > 0 && (rows == nullptr || num_freed == nullptr || (R > 0 && completed == nullptr) ||
+                  (MB > 0 && (freed == nullptr || (R > 0 && block_table == nullptr)))))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_window_free(m, rows, completed, block_table, R, MB, block_size,
+                                            sliding_window, freed, num_freed, status,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int pkv_lookahead_slots(int32_t n, const int32_t* index_mapping, const int32_t* seq_lens,
+                        const int32_t* block_table, int32_t R, int32_t MB, int32_t block_size,
+                        int32_t num_blocks, int32_t k, int32_t* lookahead_slots,
+                        uint32_t* status, void* stream)
+{
+    if (n < 0 || R < 0 || MB < 0 || block_size <= 0 || num_blocks < 0 || k < 0)
+        return PKV_EINVAL;
+    if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX + 1)
+        return PKV_EINVAL;
+    if (n > 0 && k > 0 && (index_mapping == nullptr || seq_lens == nullptr ||
+                           lookahead_slots == nullptr || (R > 0 && MB > 0 && block_table == nullptr)))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_lookahead_slots(n, index_mapping, seq_lens, block_table, R, MB,
+                                                block_size, num_blocks, k, lookahead_slots, status,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int pkv_blocks_needed(int32_t n, const int32_t* rows, const int32_t* num_new, int32_t k,
+                      int32_t block_size, const int32_t* completed, const int32_t* row_blocks,
+                      int32_t R, int32_t* need, uint32_t* status, void* stream)
+{
+    if (n < 0 || k < 0 || block_size <= 0 || R < 0)
+        return PKV_EINVAL;
+    if (n > 0 && (rows == nullptr || num_new == nullptr || need == nullptr ||
+                  (R > 0 && (completed == nullptr || row_blocks == nullptr))))
+        return PKV_EINVAL;
+    return from_hip(pkv::launch_blocks_needed(n, rows, num_new, k, block_size, completed,
+                                              row_blocks, R, need, status,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int pkv_hash_blocks(int32_t m, const int32_t* tokens, int64_t total, const int64_t* starts,

@@ -10,7 +10,9 @@
 // block p / block_size, offset p % block_size, the physical block from the
 // visible pages, slot = block * block_size + offset.  The K and V rows at that
 // slot go to row kv_start[b] + p of the outputs, kv_start being the running sum
-// of the seq_lens.  It is the exact inverse of the scatter.
+// of the seq_lens.  It is the exact inverse of the scatter.  For a
+// sliding-window group only the positions some new token attends are read,
+// from first = max(0, seq_len - count - W + 1) on.
 //
 // Design (gfx950): a persistent grid, 256 threads per workgroup.  Every
 // workgroup first forms the running sum of the seq_lens in LDS (at most
@@ -60,6 +62,7 @@ constexpr int kScanPer = PKV_MAX_BATCH / kThreads;  // seq_lens per thread in th
 
 struct GatherArgs {
     const int32_t* seq_lens;
+    const int32_t* qsl;              // query_start_loc (read only for a sliding window)
     const int32_t* pages;            // input_block_tables [n, MB]
     const u32x4* k_cache;
     const u32x4* v_cache;
@@ -76,6 +79,7 @@ struct GatherArgs {
     int32_t num_blocks;
     int32_t chunks_per_row;
     int32_t row_shift;               // log2(chunks_per_row), or -1
+    int32_t window;                  // sliding window, 0 = full attention
     int32_t tile;                    // output rows per tile (a power of two <= kTile)
     int32_t out_tokens;
 };
@@ -92,6 +96,7 @@ __device__ inline bool is_index_wave()
 // at or past it are never written), by every thread of the workgroup.
 // Workgroup 0 also writes kv_start (saturated at INT32_MAX) and the flags of
 // the batch as a whole.
+template <bool kWindow>
 __device__ inline void start_offsets(const GatherArgs& a, int32_t* s_start, int64_t* s_wave,
                                      uint32_t& flags)
 {
@@ -108,6 +113,15 @@ __device__ inline void start_offsets(const GatherArgs& a, int32_t* s_start, int6
         if (i >= a.n)
             v[k] = 0;
     }
+    int32_t q[kScanPer + 1];
+    const bool windowed = kWindow && a.n > 0;         // uniform; qsl is read only then
+    if (windowed) {
+#pragma unroll
+        for (int k = 0; k <= kScanPer; ++k) {
+            const int i = i0 + k;
+            q[k] = a.qsl[i < a.n ? i : a.n];
+        }
+    }
     int64_t total = 0;
 #pragma unroll
     for (int k = 0; k < kScanPer; ++k) {
@@ -115,6 +129,9 @@ __device__ inline void start_offsets(const GatherArgs& a, int32_t* s_start, int6
             flags |= PKV_ST_BAD_COUNT;
             v[k] = 0;
         }
+        // A sliding window reads only from the first attended position on.
+        if (windowed && i0 + k < a.n)
+            v[k] -= window_first(v[k], (int64_t)q[k + 1] - q[k], a.window);
         total += v[k];
     }
     const int64_t incl = wave_inclusive_scan(total);
@@ -148,12 +165,33 @@ __device__ inline void start_offsets(const GatherArgs& a, int32_t* s_start, int6
 
 // Index wavefront: the source slot of each row of a tile, -1 where no page
 // can be read (flagged).  All of a lane's page loads are issued together.
+template <bool kWindow>
 __device__ inline void tile_slots(const GatherArgs& a, const int32_t* s_start, int64_t u0,
                                   int len, int32_t* s_slot, uint32_t& flags)
 {
     const int lane = threadIdx.x & (kWave - 1);
     int64_t src[kRowsPerLane];
     int32_t off[kRowsPerLane];
+    int owner[kRowsPerLane];
+    int64_t first[kRowsPerLane];
+#pragma unroll
+    for (int k = 0; k < kRowsPerLane; ++k) {
+        const int j = k * kWave + lane;
+        owner[k] = j < len ? owner_of(s_start, a.n, u0 + j) : 0;   // in [0, n): u < s_start[n]
+        first[k] = 0;
+    }
+    if (kWindow) {                                    // the window's first position
+        int32_t sl[kRowsPerLane], q0[kRowsPerLane], q1[kRowsPerLane];
+#pragma unroll
+        for (int k = 0; k < kRowsPerLane; ++k) {
+            sl[k] = a.seq_lens[owner[k]];
+            q0[k] = a.qsl[owner[k]];
+            q1[k] = a.qsl[owner[k] + 1];
+        }
+#pragma unroll
+        for (int k = 0; k < kRowsPerLane; ++k)
+            first[k] = window_first(sl[k] > 0 ? sl[k] : 0, (int64_t)q1[k] - q0[k], a.window);
+    }
 #pragma unroll
     for (int k = 0; k < kRowsPerLane; ++k) {
         const int j = k * kWave + lane;
@@ -162,8 +200,8 @@ __device__ inline void tile_slots(const GatherArgs& a, const int32_t* s_start, i
         if (j >= len)
             continue;
         const int64_t u = u0 + j;
-        const int b = owner_of(s_start, a.n, u);      // in [0, n): u < s_start[n]
-        const int32_t p = (int32_t)(u - s_start[b]);
+        const int b = owner[k];
+        const int32_t p = (int32_t)(u - s_start[b] + first[k]);
         const int32_t lb = a.bs_shift >= 0 ? (p >> a.bs_shift) : p / a.block_size;
         off[k] = p - lb * a.block_size;
         if (lb >= a.MB)
@@ -284,7 +322,7 @@ __device__ inline void copy_tile(const GatherArgs& a, const int32_t* s_slot, int
 #endif
 }
 
-template <bool kPow2Row>
+template <bool kPow2Row, bool kWindow>
 __global__ __launch_bounds__(kThreads) void k_gather(const GatherArgs a)
 {
     __shared__ int32_t s_start[PKV_MAX_BATCH + 1];
@@ -292,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void k_gather(const GatherArgs a)
     __shared__ int32_t s_slot[2 * kTile];
 
     uint32_t flags = 0;
-    start_offsets(a, s_start, s_wave, flags);
+    start_offsets<kWindow>(a, s_start, s_wave, flags);
     __syncthreads();
     const int64_t rows = s_start[a.n];                   // rows to write (uniform)
     const int64_t tiles = (rows + a.tile - 1) / a.tile;
@@ -306,13 +344,13 @@ __global__ __launch_bounds__(kThreads) void k_gather(const GatherArgs a)
     if (is_index_wave()) {
         int64_t tile = blockIdx.x;
         if (tile < tiles)
-            tile_slots(a, s_start, tile * a.tile, tile_len(tile), s_slot, flags);
+            tile_slots<kWindow>(a, s_start, tile * a.tile, tile_len(tile), s_slot, flags);
         __syncthreads();
         for (; tile < tiles; tile += G) {
             const int64_t next = tile + G;
             if (next < tiles)
-                tile_slots(a, s_start, next * a.tile, tile_len(next), s_slot + (buf ^ 1) * kTile,
-                           flags);
+                tile_slots<kWindow>(a, s_start, next * a.tile, tile_len(next),
+                                    s_slot + (buf ^ 1) * kTile, flags);
             __syncthreads();
             buf ^= 1;
         }
@@ -329,8 +367,9 @@ __global__ __launch_bounds__(kThreads) void k_gather(const GatherArgs a)
 
 }  // namespace
 
-hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
-                         int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
+hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* query_start_loc,
+                         int32_t sliding_window, const int32_t* input_block_tables, int32_t MB,
+                         int32_t block_size, int32_t num_blocks, int64_t row_bytes,
                          const void* k_cache, const void* v_cache, int32_t out_tokens,
                          void* k_out, int64_t k_out_stride, void* v_out, int64_t v_out_stride,
                          int32_t* kv_start, uint32_t* status, hipStream_t stream)
@@ -339,6 +378,8 @@ hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* inpu
         return hipSuccess;
     GatherArgs a;
     a.seq_lens = seq_lens;
+    a.qsl = query_start_loc;
+    a.window = sliding_window;
     a.pages = input_block_tables;
     a.k_cache = static_cast<const u32x4*>(k_cache);
     a.v_cache = static_cast<const u32x4*>(v_cache);
@@ -366,10 +407,17 @@ hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* inpu
     a.out_tokens = out_tokens;
     const int64_t tiles = ((int64_t)out_tokens + a.tile - 1) / a.tile;
     const int64_t grid = tiles < 1 ? 1 : (tiles < PKV_GATHER_WGS ? tiles : PKV_GATHER_WGS);
-    if (a.row_shift >= 0)
-        k_gather<true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(a);
+    // The window's extra index work gets instantiations of its own, so that
+    // full-attention reads keep their register budget.
+    const dim3 g((unsigned)grid), b(kThreads);
+    if (a.row_shift >= 0 && a.window == 0)
+        k_gather<true, false><<<g, b, 0, stream>>>(a);
+    else if (a.row_shift >= 0)
+        k_gather<true, true><<<g, b, 0, stream>>>(a);
+    else if (a.window == 0)
+        k_gather<false, false><<<g, b, 0, stream>>>(a);
     else
-        k_gather<false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(a);
+        k_gather<false, true><<<g, b, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -61,6 +61,17 @@ __device__ inline int owner_of(const int32_t* qsl, int n, int64_t t)
     return lo;
 }
 
+// Sliding-window groups: the first position any new token of a request
+// attends, when the token at position p attends p-W+1 .. p and the request
+// has `count` new tokens ending at seq_len (0 for W == 0: full attention).
+__device__ inline int64_t window_first(int64_t seq_len, int64_t count, int32_t window)
+{
+    if (window <= 0)
+        return 0;
+    const int64_t first = seq_len - (count > 0 ? count : 0) - window + 1;
+    return first > 0 ? first : 0;
+}
+
 // Ascending order of (count, row) as unsigned 64-bit keys: the count (>= 0) in
 // the high word, the row with its sign bit flipped in the low word so that
 // signed row order equals unsigned key order.

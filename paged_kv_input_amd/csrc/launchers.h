@@ -22,8 +22,8 @@ hipError_t launch_slots(int32_t n, int32_t T, const int32_t* index_mapping,
                         const int32_t* query_start_loc, const int32_t* seq_lens,
                         const int32_t* positions, const int32_t* block_table, int32_t R,
                         int32_t MB, int32_t block_size, int32_t num_blocks,
-                        int32_t* slot_mapping, int32_t* input_block_tables, uint32_t* status,
-                        hipStream_t stream);
+                        int32_t sliding_window, int32_t* slot_mapping,
+                        int32_t* input_block_tables, uint32_t* status, hipStream_t stream);
 
 hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
                        const int32_t* num_scheduled, const int32_t* completed, int32_t R,
@@ -35,8 +35,9 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
 // Work-items of the grid launch_step would launch.
 int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
 
-hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* input_block_tables,
-                         int32_t MB, int32_t block_size, int32_t num_blocks, int64_t row_bytes,
+hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* query_start_loc,
+                         int32_t sliding_window, const int32_t* input_block_tables, int32_t MB,
+                         int32_t block_size, int32_t num_blocks, int64_t row_bytes,
                          const void* k_cache, const void* v_cache, int32_t out_tokens,
                          void* k_out, int64_t k_out_stride, void* v_out, int64_t v_out_stride,
                          int32_t* kv_start, uint32_t* status, hipStream_t stream);
@@ -63,6 +64,21 @@ hipError_t launch_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k
                           const void* v, int64_t v_stride, void* k_cache, void* v_cache,
                           int64_t num_slots, const int32_t* slot_mapping, uint32_t* status,
                           hipStream_t stream);
+
+hipError_t launch_window_free(int32_t m, const int32_t* rows, const int32_t* completed,
+                              int32_t* block_table, int32_t R, int32_t MB, int32_t block_size,
+                              int32_t sliding_window, int32_t* freed, int32_t* num_freed,
+                              uint32_t* status, hipStream_t stream);
+
+hipError_t launch_lookahead_slots(int32_t n, const int32_t* index_mapping, const int32_t* seq_lens,
+                                  const int32_t* block_table, int32_t R, int32_t MB,
+                                  int32_t block_size, int32_t num_blocks, int32_t k,
+                                  int32_t* lookahead_slots, uint32_t* status, hipStream_t stream);
+
+hipError_t launch_blocks_needed(int32_t n, const int32_t* rows, const int32_t* num_new, int32_t k,
+                                int32_t block_size, const int32_t* completed,
+                                const int32_t* row_blocks, int32_t R, int32_t* need,
+                                uint32_t* status, hipStream_t stream);
 
 hipError_t launch_hash_blocks(int32_t m, const int32_t* tokens, int64_t total,
                               const int64_t* starts, const int32_t* lengths, int32_t block_size,

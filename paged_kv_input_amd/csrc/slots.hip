@@ -7,7 +7,10 @@
 // remainder, (row, logical block) -> physical block through the block table,
 // physical block * block_size + offset -> slot id ("Address Calculation
 // Example").  The visible pages per request (input_block_tables) come from its
-// "Complete Input Preparation for the Attention Module".
+// "Complete Input Preparation for the Attention Module"; in a sliding-window
+// group the pages before every window of the step may be -1 holes, the blocks
+// freed once the window moved past them ("allocate_slots()" of the
+// caffein.top scheduler page).
 //
 // Design (gfx950): the grid has two kinds of workgroups.  Token workgroups
 // stage query_start_loc and index_mapping in LDS, find each token's request by
@@ -31,7 +34,7 @@ __global__ __launch_bounds__(kSlotThreads) void k_slots(
     int32_t n, int32_t T, const int32_t* __restrict__ index_mapping,
     const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ positions, const int32_t* __restrict__ block_table, int32_t R,
-    int32_t MB, int32_t block_size, int32_t bs_shift, int32_t num_blocks,
+    int32_t MB, int32_t block_size, int32_t bs_shift, int32_t num_blocks, int32_t window,
     int32_t* __restrict__ slot_mapping, int32_t* __restrict__ input_block_tables,
     uint32_t* __restrict__ status, int32_t token_blocks)
 {
@@ -121,6 +124,12 @@ __global__ __launch_bounds__(kSlotThreads) void k_slots(
                     flags |= PKV_ST_LB_OOR;
                     visible = MB;
                 }
+                // Pages before the window may be -1 holes (freed blocks).
+                int64_t first_block = 0;
+                if (window > 0) {                                   // uniform
+                    const int64_t count = (int64_t)query_start_loc[b + 1] - query_start_loc[b];
+                    first_block = window_first(sl, count, window) / block_size;
+                }
                 const int32_t* src = block_table + (int64_t)row * MB;
                 int32_t* dst = input_block_tables + (int64_t)b * MB;
                 for (int64_t i0 = 0; i0 < visible; i0 += kWave * kPageUnroll) {
@@ -134,7 +143,8 @@ __global__ __launch_bounds__(kSlotThreads) void k_slots(
                     for (int u = 0; u < kPageUnroll; ++u) {
                         const int64_t i = i0 + u * kWave + lane;
                         if (i < visible) {
-                            if (v[u] < 0 || v[u] >= num_blocks)
+                            const bool hole = i < first_block && v[u] == -1;
+                            if ((v[u] < 0 || v[u] >= num_blocks) && !hole)
                                 flags |= PKV_ST_BLOCK_OOR;
                             dst[i] = v[u];
                         }
@@ -152,8 +162,8 @@ hipError_t launch_slots(int32_t n, int32_t T, const int32_t* index_mapping,
                         const int32_t* query_start_loc, const int32_t* seq_lens,
                         const int32_t* positions, const int32_t* block_table, int32_t R,
                         int32_t MB, int32_t block_size, int32_t num_blocks,
-                        int32_t* slot_mapping, int32_t* input_block_tables, uint32_t* status,
-                        hipStream_t stream)
+                        int32_t sliding_window, int32_t* slot_mapping,
+                        int32_t* input_block_tables, uint32_t* status, hipStream_t stream)
 {
     const int64_t token_blocks = ((int64_t)T + kSlotTokensPerBlock - 1) / kSlotTokensPerBlock;
     const int64_t page_blocks =
@@ -166,7 +176,8 @@ hipError_t launch_slots(int32_t n, int32_t T, const int32_t* index_mapping,
         bs_shift = __builtin_ctz((unsigned)block_size);
     k_slots<<<dim3((unsigned)blocks), dim3(kSlotThreads), 0, stream>>>(
         n, T, index_mapping, query_start_loc, seq_lens, positions, block_table, R, MB, block_size,
-        bs_shift, num_blocks, slot_mapping, input_block_tables, status, (int32_t)token_blocks);
+        bs_shift, num_blocks, sliding_window, slot_mapping, input_block_tables, status,
+        (int32_t)token_blocks);
     return hipGetLastError();
 }
 

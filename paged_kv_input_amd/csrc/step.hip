@@ -83,6 +83,7 @@ struct StepGroup {
     int32_t tiles;           // ceil(T / tile_tokens)
     int32_t tile_blocks;     // persistent workgroups walking those tiles
     int32_t page_blocks;
+    int32_t window;          // sliding window, 0 = full attention
 };
 
 struct StepArgs {
@@ -284,6 +285,9 @@ __device__ inline void copy_pages(const StepArgs& a, const StepGroup& g,
         flags |= PKV_ST_LB_OOR;
         visible = g.MB;
     }
+    // Pages before the window may be -1 holes (freed blocks).
+    const int64_t first_block =
+        window_first(sl, (int64_t)lds.qsl[b + 1] - lds.qsl[b], g.window) / g.block_size;
     const int32_t* src = g.block_table + (int64_t)row * g.MB;
     int32_t* dst = g.input_block_tables + (int64_t)b * g.MB;
     for (int64_t i0 = 0; i0 < visible; i0 += kWave * 4) {
@@ -297,7 +301,8 @@ __device__ inline void copy_pages(const StepArgs& a, const StepGroup& g,
         for (int u = 0; u < 4; ++u) {
             const int64_t i = i0 + u * kWave + lane;
             if (i < visible) {
-                if (v[u] < 0 || v[u] >= g.num_blocks)
+                const bool hole = i < first_block && v[u] == -1;
+                if ((v[u] < 0 || v[u] >= g.num_blocks) && !hole)
                     flags |= PKV_ST_BLOCK_OOR;
                 dst[i] = v[u];
             }
@@ -476,6 +481,7 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
         g.block_size = in.block_size;
         g.bs_shift = (in.block_size & (in.block_size - 1)) == 0 ? __builtin_ctz(in.block_size) : -1;
         g.num_blocks = in.num_blocks;
+        g.window = in.sliding_window;
         const int64_t cpr = in.row_bytes / 16;
         g.chunks_per_row = (int32_t)cpr;
         g.row_shift = (cpr & (cpr - 1)) == 0 ? __builtin_ctzll((unsigned long long)cpr) : -1;

@@ -24,6 +24,7 @@ class GroupSpec:
     num_blocks: int
     k: np.ndarray               # [T, H, D] payload words (any dtype, copied as bits)
     v: np.ndarray
+    sliding_window: int = 0     # 0: full attention
 
 
 class DeviceStep:
@@ -93,7 +94,8 @@ class DeviceStep:
                 if ibt_fill is not None:
                     ibt.fill_(ibt_fill)
             self.groups.append(dict(block_table=bt, block_size=int(g.block_size),
-                                    num_blocks=int(g.num_blocks), k=k, v=v, k_cache=kc,
+                                    num_blocks=int(g.num_blocks),
+                                    sliding_window=int(g.sliding_window), k=k, v=v, k_cache=kc,
                                     v_cache=vc, slot_mapping=torch.empty(self.T, **i32),
                                     input_block_tables=ibt))
 
@@ -114,7 +116,7 @@ class DeviceStep:
                 self.index_mapping, self.query_start_loc, self.seq_lens, self.positions,
                 g["block_table"], g["block_size"], g["num_blocks"],
                 slot_mapping=g["slot_mapping"], input_block_tables=g["input_block_tables"],
-                status=self.status)
+                status=self.status, sliding_window=g["sliding_window"])
         g["_slots"](stream)
 
     def scatter(self, gi: int, stream=None):
@@ -139,7 +141,8 @@ class DeviceStep:
             self._fused = api.prepared_step(
                 self.sched_rows, self.num_scheduled, self.completed, self.token_ids, self.T,
                 [dict(block_table=g["block_table"], block_size=g["block_size"],
-                      num_blocks=g["num_blocks"], slot_mapping=g["slot_mapping"],
+                      num_blocks=g["num_blocks"], sliding_window=g["sliding_window"],
+                      slot_mapping=g["slot_mapping"],
                       input_block_tables=g["input_block_tables"], k=g["k"], v=g["v"],
                       k_cache=g["k_cache"], v_cache=g["v_cache"]) for g in self.groups],
                 index_mapping=self.index_mapping, query_start_loc=self.query_start_loc,

@@ -33,13 +33,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert names == ["pkv_abi_version", "pkv_add_requests", "pkv_advance_state",
-                     "pkv_append_blocks", "pkv_compute_slot_mapping", "pkv_error_string",
+    assert names == sorted(["pkv_abi_version", "pkv_add_requests", "pkv_advance_state",
+                     "pkv_append_blocks", "pkv_blocks_needed", "pkv_compute_slot_mapping",
+                     "pkv_error_string",
                      "pkv_gather_kv", "pkv_hash_blocks", "pkv_prefix_clear", "pkv_prefix_evict",
-                     "pkv_prefix_insert", "pkv_prefix_lookup",
+                     "pkv_lookahead_slots", "pkv_prefix_insert", "pkv_prefix_lookup",
                      "pkv_prepare_batch", "pkv_row_pool_acquire", "pkv_row_pool_create",
                      "pkv_row_pool_destroy", "pkv_row_pool_num_free", "pkv_row_pool_release",
-                     "pkv_scatter_kv", "pkv_step"]
+                     "pkv_scatter_kv", "pkv_step", "pkv_window_free"])
     for name in names:
         assert hasattr(lib, name), name
     so = os.path.join(ROOT, "paged_kv_input_amd", "libpagedkv.so")
@@ -84,12 +85,13 @@ def test_host_argument_errors(lib):
     assert prep(1, 1, fake, fake, fake, 1, fake, 3, 4, fake, fake, fake, fake, fake, N, N) == EINVAL
     assert prep(4097, 1, fake, fake, fake, 1, fake, 1, 1, fake, fake, fake, fake, fake, N, N) == EUNSUP
     slots = lib.pkv_compute_slot_mapping
-    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 0, 4, fake, N, N, N) == EINVAL
-    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 16, -1, fake, N, N, N) == EINVAL
-    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 1 << 16, 1 << 16, fake, N, N, N) == EINVAL
-    assert slots(1, 1, fake, fake, N, fake, fake, 1, 1, 16, 4, fake, fake, N, N) == EINVAL
-    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 16, 4, N, N, N, N) == EINVAL
-    assert slots(4097, 1, fake, fake, fake, fake, fake, 1, 1, 16, 4, fake, N, N, N) == EUNSUP
+    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 0, 4, 0, fake, N, N, N) == EINVAL
+    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 16, -1, 0, fake, N, N, N) == EINVAL
+    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 16, 4, -1, fake, N, N, N) == EINVAL
+    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 1 << 16, 1 << 16, 0, fake, N, N, N) == EINVAL
+    assert slots(1, 1, fake, fake, N, fake, fake, 1, 1, 16, 4, 0, fake, fake, N, N) == EINVAL
+    assert slots(1, 1, fake, fake, fake, fake, fake, 1, 1, 16, 4, 0, N, N, N, N) == EINVAL
+    assert slots(4097, 1, fake, fake, fake, fake, fake, 1, 1, 16, 4, 0, fake, N, N, N) == EUNSUP
     sc = lib.pkv_scatter_kv
     assert sc(-1, 16, fake, 16, fake, 16, fake, fake, 4, fake, N, N) == EINVAL
     assert sc(1, 16, fake, 8, fake, 16, fake, fake, 4, fake, N, N) == EINVAL
@@ -111,9 +113,9 @@ def test_step_host_argument_errors(lib):
     args = [1, 1, fake, fake, fake, 1, fake, 1, 1, fake, fake, fake, fake, fake]
     assert st(*args, -1, arr, None, None) == -1          # num_groups < 0
     assert st(*args, 1, None, None, None) == -1          # groups NULL
-    arr[0].reserved = 1
-    assert st(*args, 1, arr, None, None) == -1           # reserved must be 0
-    arr[0].reserved = 0
+    arr[0].sliding_window = -1
+    assert st(*args, 1, arr, None, None) == -1           # negative window
+    arr[0].sliding_window = 0
     arr[0].block_size = 0
     assert st(*args, 1, arr, None, None) == -1           # group's block size
     arr[0].block_size = 16
@@ -130,7 +132,9 @@ def test_gather_host_argument_errors(lib):
     P = ctypes.c_void_p
     fake = P(0x1000)
     g = lib.pkv_gather_kv
-    ok = [2, fake, fake, 4, 16, 8, 256, fake, fake, 64, fake, 256, fake, 256, N, N, N]
+    # n, seq_lens, qsl, window, pages, MB, bs, NB, row_bytes, kc, vc, out_tokens, k_out,
+    # k_stride, v_out, v_stride, kv_start, status, stream
+    ok = [2, fake, fake, 0, fake, 4, 16, 8, 256, fake, fake, 64, fake, 256, fake, 256, N, N, N]
 
     def call(**kw):
         a = list(ok)
@@ -139,20 +143,22 @@ def test_gather_host_argument_errors(lib):
         return g(*a)
 
     assert call(a0=-1) == -1                       # n < 0
-    assert call(a4=0) == -1                        # block_size <= 0
-    assert call(a6=0) == -1                        # row_bytes <= 0
-    assert call(a9=-1) == -1                       # out_tokens < 0
-    assert call(a11=128) == -1                     # k_out stride < row_bytes
-    assert call(a5=1 << 27, a4=32) == -1           # num_blocks * block_size > 2^31
+    assert call(a6=0) == -1                        # block_size <= 0
+    assert call(a8=0) == -1                        # row_bytes <= 0
+    assert call(a11=-1) == -1                      # out_tokens < 0
+    assert call(a13=128) == -1                     # k_out stride < row_bytes
+    assert call(a7=1 << 27, a6=32) == -1           # num_blocks * block_size > 2^31
+    assert call(a3=-1) == -1                       # negative window
+    assert call(a3=8, a2=N) == -1                  # a window needs query_start_loc
     assert call(a1=N) == -1                        # seq_lens NULL
-    assert call(a2=N) == -1                        # pages NULL with MB > 0
-    assert call(a10=N) == -1                       # k_out NULL
-    assert call(a7=N) == -1                        # cache NULL
-    assert call(a6=24, a11=32, a13=32) == -2       # row not a multiple of 16
-    assert call(a10=P(0x1008)) == -2               # misaligned output
+    assert call(a4=N) == -1                        # pages NULL with MB > 0
+    assert call(a12=N) == -1                       # k_out NULL
+    assert call(a9=N) == -1                        # cache NULL
+    assert call(a8=24, a13=32, a15=32) == -2       # row not a multiple of 16
+    assert call(a12=P(0x1008)) == -2               # misaligned output
     assert call(a0=4097) == -3                     # beyond PKV_MAX_BATCH
-    assert call(a9=1 << 31) == -3                  # out_tokens > INT32_MAX
-    assert call(a0=0, a1=N, a2=N, a14=N) == 0      # nothing to do: nothing enqueued
+    assert call(a11=1 << 31) == -3                 # out_tokens > INT32_MAX
+    assert call(a0=0, a1=N, a4=N, a16=N) == 0      # nothing to do: nothing enqueued
 
 
 def test_prefix_host_argument_errors(lib):
@@ -180,6 +186,28 @@ def test_prefix_host_argument_errors(lib):
     assert ev(-1, fake, fake, fake, fake, 8, N) == -1
     assert ev(1, N, fake, fake, fake, 8, N) == -1
     assert ev(0, N, N, N, N, 8, N) == 0
+
+
+def test_alloc_host_argument_errors(lib):
+    N = None
+    fake = ctypes.c_void_p(0x1000)
+    wf = lib.pkv_window_free
+    assert wf(-1, fake, fake, fake, 4, 4, 16, 8, fake, fake, N, N) == -1
+    assert wf(1, fake, fake, fake, 4, 4, 0, 8, fake, fake, N, N) == -1      # block_size 0
+    assert wf(1, fake, fake, fake, 4, 4, 16, -1, fake, fake, N, N) == -1    # window < 0
+    assert wf(1, fake, fake, fake, 4, 4, 16, 8, N, fake, N, N) == -1        # freed NULL
+    assert wf(1, fake, fake, N, 4, 4, 16, 8, fake, fake, N, N) == -1        # table NULL
+    assert wf(0, N, N, N, 4, 4, 16, 8, N, N, N, N) == 0
+    la = lib.pkv_lookahead_slots
+    assert la(1, fake, fake, fake, 4, 4, 16, 8, -1, fake, N, N) == -1       # k < 0
+    assert la(1, fake, fake, fake, 4, 4, 16, 8, 2, N, N, N) == -1           # out NULL
+    assert la(1, fake, fake, fake, 4, 4, 1 << 16, 1 << 16, 2, fake, N, N) == -1
+    assert la(3, N, N, N, 4, 4, 16, 8, 0, N, N, N) == 0                      # k = 0
+    bn = lib.pkv_blocks_needed
+    assert bn(1, fake, fake, -1, 16, fake, fake, 4, fake, N, N) == -1      # k < 0
+    assert bn(1, fake, fake, 0, 0, fake, fake, 4, fake, N, N) == -1        # block_size 0
+    assert bn(1, fake, fake, 0, 16, fake, fake, 4, N, N, N) == -1          # need NULL
+    assert bn(0, N, N, 0, 16, N, N, 4, N, N, N) == 0
 
 
 def test_state_host_argument_errors(lib):

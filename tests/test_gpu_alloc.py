@@ -1,0 +1,345 @@
+"""Sliding-window holes and speculative lookahead on the GPU against the CPU
+oracle: freeing the blocks behind the window, visible pages with holes (calls
+and the fused step), the windowed read, lookahead slots and the blocks each
+request still needs; then a sliding-window serving loop with everything on
+the device.  Integer outputs, so every comparison is bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import SENTINEL16, assert_equal, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_input_amd  # noqa: F401  (raises if the library is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+def up(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def zeros_i32(*shape):
+    import torch
+
+    return torch.zeros(shape, dtype=torch.int32, device="cuda")
+
+
+def device_window_free(rows, completed, bt, bs, W):
+    import torch
+    from paged_kv_input_amd import api
+
+    m, MB = len(rows), bt.shape[1]
+    table = up(bt)
+    freed = torch.full((m, MB), -7, dtype=torch.int32, device="cuda")
+    nf = torch.full((m,), -7, dtype=torch.int32, device="cuda")
+    st = zeros_i32(1)
+    api.window_free(up(np.asarray(rows, np.int32)), up(completed), table, bs, W, freed=freed,
+                    num_freed=nf, status=st)
+    torch.cuda.synchronize()
+    return table.cpu().numpy(), freed.cpu().numpy(), nf.cpu().numpy(), int(st.item())
+
+
+def check_free(rows, completed, bt, bs, W, what):
+    got_bt, got_fr, got_nf, got_st = device_window_free(rows, completed, bt, bs, W)
+    want_bt = bt.copy()
+    want = oracle.window_free(rows, completed, want_bt, bs, W)
+    assert got_st == want["status"], (what, got_st, want["status"])
+    assert_equal(f"{what} num_freed", got_nf, want["num_freed"])
+    assert_equal(f"{what} table", got_bt, want_bt)
+    for i, c in enumerate(want["num_freed"]):
+        assert_equal(f"{what} freed {i}", got_fr[i, :c], want["freed"][i, :c])
+    return want_bt
+
+
+def window_for(b, seed):
+    bs = b.groups[0].block_size
+    return int(np.random.default_rng(seed).integers(1, 4 * bs + 9))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_window_step_and_read_tiny(seed):
+    """Free behind the window, then the step with a windowed group (both the
+    three calls and pkv_step), then the windowed read: all against the oracle."""
+    import torch
+    from paged_kv_input_amd import api
+    from paged_kv_input_amd.step import DeviceStep, GroupSpec
+
+    b = workloads.random_tiny(seed)
+    g = b.groups[0]
+    W = window_for(b, seed)
+    say(f"[case] window tiny seed={seed} W={W} bs={g.block_size} n={b.n}")
+    bt = check_free(b.sched_rows, b.completed, g.block_table, g.block_size, W, f"seed {seed}")
+    mode = ["calls", "fused"][seed % 2]
+    step = DeviceStep(b.sched_rows, b.num_scheduled, b.completed, b.token_ids,
+                      [GroupSpec(bt, g.block_size, g.num_blocks, g.k, g.v, sliding_window=W)],
+                      cache_fill=SENTINEL16, ibt_fill=oracle.IBT_UNWRITTEN)
+    step.run_fused() if mode == "fused" else step.run()
+    prep = oracle.prepare_batch(b.sched_rows, b.num_scheduled, b.completed, b.token_ids)
+    sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                     prep["seq_lens"], prep["positions"], bt, g.block_size,
+                                     g.num_blocks, sliding_window=W)
+    kc = np.full((g.num_slots, g.num_heads, g.head_dim), 0xFFFF, np.uint16)
+    vc = kc.copy()
+    oracle.scatter_kv(g.k, g.v, kc, vc, sm["slot_mapping"])
+    assert step.status_bits() == prep["status"] | sm["status"], (step.status_bits(), sm["status"])
+    assert sm["status"] == 0
+    assert_equal("slot_mapping", step.host("slot_mapping", 0), sm["slot_mapping"])
+    assert_equal("input_block_tables", step.host("input_block_tables", 0),
+                 sm["input_block_tables"])
+    want = oracle.gather_kv(prep["seq_lens"], sm["input_block_tables"], g.block_size,
+                            g.num_blocks, kc, vc, query_start_loc=prep["query_start_loc"],
+                            sliding_window=W)
+    rows = int(want["kv_start"][-1])
+    k_out = torch.full((rows, g.num_heads, g.head_dim), SENTINEL16, dtype=torch.int16,
+                       device="cuda")
+    v_out = torch.full_like(k_out, SENTINEL16)
+    ks = zeros_i32(b.n + 1)
+    st = zeros_i32(1)
+    api.gather_kv(step.seq_lens, step.groups[0]["input_block_tables"], g.block_size, g.num_blocks,
+                  step.groups[0]["k_cache"], step.groups[0]["v_cache"], k_out=k_out, v_out=v_out,
+                  kv_start=ks, status=st, query_start_loc=step.query_start_loc, sliding_window=W)
+    torch.cuda.synchronize()
+    assert int(st.item()) == want["status"] == 0
+    assert_equal("kv_start", ks.cpu().numpy(), want["kv_start"])
+    assert_equal("k read", k_out.cpu().numpy().view(np.uint16), want["k"])
+    assert_equal("v read", v_out.cpu().numpy().view(np.uint16), want["v"])
+
+
+@pytest.mark.parametrize("name,W", [("decode_256x1", 1024), ("mixed_8192", 512),
+                                    ("two_groups_512req", 300), ("seeded_16req", 40)])
+def test_window_reduced_configs(name, W):
+    """Reduced configurations: free, step (fused), windowed read of group 0."""
+    import torch
+    from paged_kv_input_amd import api
+    from paged_kv_input_amd.step import DeviceStep, GroupSpec
+
+    b = workloads.make(name, reduced=True)
+    say(f"[case] window {b.name} W={W}")
+    specs, tables = [], []
+    for gi, g in enumerate(b.groups):
+        bt = check_free(b.sched_rows, b.completed, g.block_table, g.block_size, W, f"g{gi}")
+        tables.append(bt)
+        specs.append(GroupSpec(bt, g.block_size, g.num_blocks, g.k, g.v, sliding_window=W))
+    step = DeviceStep(b.sched_rows, b.num_scheduled, b.completed, b.token_ids, specs,
+                      cache_fill=SENTINEL16, ibt_fill=oracle.IBT_UNWRITTEN)
+    step.run_fused()
+    prep = oracle.prepare_batch(b.sched_rows, b.num_scheduled, b.completed, b.token_ids)
+    status = prep["status"]
+    for gi, (g, bt) in enumerate(zip(b.groups, tables)):
+        sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                         prep["seq_lens"], prep["positions"], bt, g.block_size,
+                                         g.num_blocks, sliding_window=W)
+        status |= sm["status"]
+        assert_equal(f"g{gi} slots", step.host("slot_mapping", gi), sm["slot_mapping"])
+        assert_equal(f"g{gi} pages", step.host("input_block_tables", gi), sm["input_block_tables"])
+        if gi == 0:
+            kc = np.full((g.num_slots, g.num_heads, g.head_dim), 0xFFFF, np.uint16)
+            vc = kc.copy()
+            oracle.scatter_kv(g.k, g.v, kc, vc, sm["slot_mapping"])
+            want = oracle.gather_kv(prep["seq_lens"], sm["input_block_tables"], g.block_size,
+                                    g.num_blocks, kc, vc,
+                                    query_start_loc=prep["query_start_loc"], sliding_window=W)
+            rows = int(want["kv_start"][-1])
+            k_out = torch.empty((rows, g.num_heads, g.head_dim), dtype=torch.int16, device="cuda")
+            v_out = torch.empty_like(k_out)
+            st = zeros_i32(1)
+            api.gather_kv(step.seq_lens, step.groups[0]["input_block_tables"], g.block_size,
+                          g.num_blocks, step.groups[0]["k_cache"], step.groups[0]["v_cache"],
+                          k_out=k_out, v_out=v_out, status=st,
+                          query_start_loc=step.query_start_loc, sliding_window=W)
+            torch.cuda.synchronize()
+            assert int(st.item()) == want["status"] == 0
+            assert_equal("k read", k_out.cpu().numpy().view(np.uint16), want["k"])
+            assert_equal("v read", v_out.cpu().numpy().view(np.uint16), want["v"])
+    assert step.status_bits() == status == 0
+
+
+def test_window_free_edges():
+    """Bad rows, W = 0, W = 1, windows past every block, tables already holed."""
+    rng = np.random.default_rng(2)
+    R, MB, bs = 9, 200, 4
+    bt = rng.integers(-1, 1000, (R, MB)).astype(np.int32)
+    completed = rng.integers(0, MB * bs + 20, R).astype(np.int32)
+    for W in (0, 1, 3, 17, 400, 10**6):
+        rows = rng.choice(R, 6, replace=False).astype(np.int32)
+        rows[0] = -3
+        check_free(rows, completed, bt, bs, W, f"W={W}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_lookahead_and_blocks_needed(seed):
+    """Lookahead slots after a step and the blocks each request still needs,
+    on tiny random batches and with bad rows and counts."""
+    import torch
+    from paged_kv_input_amd import api
+    from paged_kv_input_amd.step import DeviceStep, GroupSpec
+
+    b = workloads.random_tiny(seed)
+    g = b.groups[0]
+    k = int(np.random.default_rng(seed).integers(0, 7))
+    say(f"[case] lookahead seed={seed} k={k}")
+    step = DeviceStep(b.sched_rows, b.num_scheduled, b.completed, b.token_ids,
+                      [GroupSpec(g.block_table, g.block_size, g.num_blocks, g.k, g.v)])
+    step.run()
+    prep = oracle.prepare_batch(b.sched_rows, b.num_scheduled, b.completed, b.token_ids)
+    out = torch.full((b.n, k), -7, dtype=torch.int32, device="cuda")
+    st = zeros_i32(1)
+    api.lookahead_slots(step.index_mapping, step.seq_lens, step.groups[0]["block_table"],
+                        g.block_size, g.num_blocks, out=out, status=st)
+    want = oracle.lookahead_slots(prep["index_mapping"], prep["seq_lens"], g.block_table,
+                                  g.block_size, g.num_blocks, k)
+    torch.cuda.synchronize()
+    assert int(st.item()) == want["status"]
+    assert_equal("lookahead slots", out.cpu().numpy(), want["slots"])
+    rng = np.random.default_rng(100 + seed)
+    row_blocks = rng.integers(0, g.max_blocks + 2, b.R).astype(np.int32)
+    rows = b.sched_rows.copy()
+    new = b.num_scheduled.copy()
+    if seed % 3 == 0:
+        rows[0], new[-1] = b.R + 2, -4
+    need = torch.full((b.n,), -7, dtype=torch.int32, device="cuda")
+    st.zero_()
+    api.blocks_needed(up(rows), up(new), k, g.block_size, up(b.completed), up(row_blocks),
+                      need=need, status=st)
+    want = oracle.blocks_needed(rows, new, k, g.block_size, b.completed, row_blocks)
+    torch.cuda.synchronize()
+    assert int(st.item()) == want["status"]
+    assert_equal("blocks needed", need.cpu().numpy(), want["need"])
+
+
+def test_sliding_window_serving_loop():
+    """Everything on the device for 30 steps of a sliding-window group:
+    window_free (freed blocks go back to the pool), blocks_needed for the new
+    tokens plus 2 lookahead tokens, append_blocks, pkv_step, the windowed read,
+    lookahead_slots and advance_state; the oracle runs the same loop."""
+    import torch
+    from paged_kv_input_amd import RowPool, api
+    from paged_kv_input_amd.state import DeviceState, pack_csr
+    from paged_kv_input_amd.step import DeviceStep, GroupSpec
+
+    rng = np.random.default_rng(808)
+    R, L, MB, bs, NB, H, D, W, k, chunk = 16, 1024, 64, 8, 400, 1, 32, 37, 2, 48
+    ds = DeviceState(R, L, MB)
+    st = oracle.empty_state(R, L, MB)
+    pool, pool_o = RowPool(R), oracle.RowPool(R)
+    free_blocks = rng.permutation(NB).tolist()
+    active = {}
+    kc_o = np.full((NB * bs, H, D), 0xFFFF, np.uint16)
+    vc_o = kc_o.copy()
+    caches = None
+    freed_total = 0
+    for s in range(30):
+        arrive = int(rng.integers(0, 3)) if len(active) < 10 else 0
+        if arrive:
+            rows = pool.acquire(arrive)
+            assert pool_o.acquire(arrive) == (0, rows)
+            plens = rng.integers(1, 120, arrive).tolist()
+            prompts = [rng.integers(0, 1 << 20, p).tolist() for p in plens]
+            ds.add_requests(rows, [0] * arrive, prompts, [[] for _ in rows])
+            oracle.add_requests(st, rows, [0] * arrive, prompts, [[] for _ in rows])
+            for r, p in zip(rows, plens):
+                active[r] = [p, p + int(rng.integers(5, 60))]
+        rows = list(active)
+        if not rows:
+            continue
+        rows_d = up(np.array(rows, np.int32))
+        # 1. free the blocks behind every window
+        fr = torch.full((len(rows), MB), -7, dtype=torch.int32, device="cuda")
+        nf = zeros_i32(len(rows))
+        api.window_free(rows_d, ds.completed, ds.block_table, bs, W, freed=fr, num_freed=nf,
+                        status=ds.status)
+        want_fr = oracle.window_free(rows, st["completed"], st["block_table"], bs, W)
+        torch.cuda.synchronize()
+        assert_equal(f"step {s} num_freed", nf.cpu().numpy(), want_fr["num_freed"])
+        for i, c in enumerate(want_fr["num_freed"].tolist()):
+            got = fr[i, :c].cpu().numpy()
+            assert_equal(f"step {s} freed", got, want_fr["freed"][i, :c])
+            free_blocks.extend(got.tolist())
+            freed_total += c
+        # 2. how many blocks each request needs for this step plus the lookahead
+        counts = [min(active[r][0] - int(st["completed"][r]), chunk)
+                  if st["completed"][r] < active[r][0] else 1 for r in rows]
+        need = zeros_i32(len(rows))
+        api.blocks_needed(rows_d, up(np.array(counts, np.int32)), k, bs, ds.completed,
+                          ds.row_blocks, need=need, status=ds.status)
+        want_need = oracle.blocks_needed(rows, counts, k, bs, st["completed"], st["row_blocks"])
+        torch.cuda.synchronize()
+        assert_equal(f"step {s} need", need.cpu().numpy(), want_need["need"])
+        new_blocks = [[free_blocks.pop() for _ in range(c)] for c in want_need["need"].tolist()]
+        ds.append_blocks(rows, new_blocks)
+        oracle.append_blocks(st, rows, new_blocks)
+        # 3. the step, fused, windowed group
+        T = int(sum(counts))
+        kk = rng.integers(-30000, 30000, (T, H, D)).astype(np.int16)
+        vv = rng.integers(-30000, 30000, (T, H, D)).astype(np.int16)
+        step = DeviceStep(rows, counts, ds.completed, ds.token_ids,
+                          [GroupSpec(ds.block_table, bs, NB, kk, vv, sliding_window=W)],
+                          cache_fill=SENTINEL16 if caches is None else None,
+                          ibt_fill=oracle.IBT_UNWRITTEN, caches=caches)
+        caches = [(step.groups[0]["k_cache"], step.groups[0]["v_cache"])]
+        step.run_fused()
+        prep = oracle.prepare_batch(rows, counts, st["completed"], st["token_ids"])
+        sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                         prep["seq_lens"], prep["positions"], st["block_table"],
+                                         bs, NB, sliding_window=W)
+        oracle.scatter_kv(kk.view(np.uint16), vv.view(np.uint16), kc_o, vc_o, sm["slot_mapping"])
+        say(f"[case] sliding-window loop step={s} n={len(rows)} T={T} freed={freed_total}")
+        assert step.status_bits() == prep["status"] | sm["status"] == 0
+        assert_equal(f"step {s} slots", step.host("slot_mapping", 0), sm["slot_mapping"])
+        assert_equal(f"step {s} pages", step.host("input_block_tables", 0),
+                     sm["input_block_tables"])
+        # 4. the windowed read
+        want = oracle.gather_kv(prep["seq_lens"], sm["input_block_tables"], bs, NB, kc_o, vc_o,
+                                query_start_loc=prep["query_start_loc"], sliding_window=W)
+        nrow = int(want["kv_start"][-1])
+        k_out = torch.empty((nrow, H, D), dtype=torch.int16, device="cuda")
+        v_out = torch.empty_like(k_out)
+        gst = zeros_i32(1)
+        api.gather_kv(step.seq_lens, step.groups[0]["input_block_tables"], bs, NB, caches[0][0],
+                      caches[0][1], k_out=k_out, v_out=v_out, status=gst,
+                      query_start_loc=step.query_start_loc, sliding_window=W)
+        # 5. lookahead slots for the next step's draft tokens
+        la = torch.empty((len(rows), k), dtype=torch.int32, device="cuda")
+        api.lookahead_slots(step.index_mapping, step.seq_lens, ds.block_table, bs, NB, out=la,
+                            status=gst)
+        want_la = oracle.lookahead_slots(prep["index_mapping"], prep["seq_lens"],
+                                         st["block_table"], bs, NB, k)
+        torch.cuda.synchronize()
+        assert int(gst.item()) == want["status"] | want_la["status"] == 0
+        assert_equal(f"step {s} read K", k_out.cpu().numpy().view(np.uint16), want["k"])
+        assert_equal(f"step {s} read V", v_out.cpu().numpy().view(np.uint16), want["v"])
+        assert_equal(f"step {s} lookahead", la.cpu().numpy(), want_la["slots"])
+        # 6. advance; finished requests give back their row and remaining blocks
+        sampled = rng.integers(0, 1 << 20, len(rows)).astype(np.int32)
+        for b_, r in enumerate(prep["index_mapping"].tolist()):
+            if prep["seq_lens"][b_] < active[r][0]:
+                sampled[b_] = -1
+        ds.advance(step.index_mapping, step.seq_lens, sampled)
+        oracle.advance_state(st, prep["index_mapping"], prep["seq_lens"], sampled)
+        assert ds.status_bits() == 0
+        got = ds.host()
+        for key in ("completed", "token_ids", "block_table", "row_blocks"):
+            assert_equal(f"step {s} {key}", got[key], st[key])
+        done = [r for r in rows if st["completed"][r] >= active[r][1]]
+        if done:
+            pool.release(done)
+            assert pool_o.release(done) == 0
+            for r in done:
+                free_blocks.extend(int(x) for x in st["block_table"][r] if x >= 0)
+                active.pop(r)
+    torch.cuda.synchronize()
+    assert freed_total > 0, "the window never moved past a block"
+    assert_equal("k_cache", caches[0][0].cpu().numpy().view(np.uint16), kc_o)
+    assert_equal("v_cache", caches[0][1].cpu().numpy().view(np.uint16), vc_o)
