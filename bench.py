@@ -14,8 +14,11 @@ then exactly K timed steps back to back, bracketed by torch.cuda.synchronize()
 on both sides and by HIP events on the launch stream; ms_per_step is the
 event interval / K.  The step runs through pkv_step (one launch) and, timed
 the same way, through the three separate calls.  Secondary figures: the
-per-call split of the three calls and a single-step cold measurement (a 1 GiB
-rewrite before each step, events around it).
+per-call split of the three calls, a single-step cold measurement (a 1 GiB
+rewrite before each step, events around it; median, p10, p90), ceilings to
+read the step against (a same-byte device copy, the dispatch floor), and the
+calls around the path: the state updates, the paged K/V read and the
+prefix-cache calls.
 
 Prints one JSON line (N = 1 only: this build runs on one GPU).
 """
@@ -364,6 +367,37 @@ def prefix_calls(batch, step, steps, warmup, stream):
     return out
 
 
+def context_figures(step_bytes, steps, warmup, stream):
+    """Ceilings to read the step against (not targets): a device-to-device copy
+    moving the same bytes (half read, half written; torch's copy kernel, four
+    rotating buffer pairs, back to back) and the dispatch floor of a one-lane
+    kernel launched back to back."""
+    import torch
+
+    half = step_bytes // 2
+    src = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(ROTATE)]
+    dst = [torch.empty_like(x) for x in src]
+
+    def timed(fn, reps):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    copy_ms = timed(lambda i: dst[i % ROTATE].copy_(src[i % ROTATE]), steps)
+    one = torch.zeros(1, device="cuda")
+    tiny_ms = timed(lambda i: one.add_(1), max(steps, 1000))
+    return {"d2d_copy_same_bytes": {"ms": copy_ms, "bytes": 2 * half,
+                                    "gbs": 2 * half / (copy_ms * 1e-3) / 1e9},
+            "tiny_kernel_us": tiny_ms * 1e3}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -477,6 +511,8 @@ def main():
     cb = call_bytes(batch)
     use_fused = fused_ms <= calls_ms
     ms = fused_ms if use_fused else calls_ms
+    context = context_figures(ab["total"], args.steps, args.warmup, stream)
+    context["step_vs_copy"] = context["d2d_copy_same_bytes"]["ms"] / ms
     if use_fused:
         kernel, launch_ms, kbytes, prof_key = "pkv_step (k_step)", fused_ms, ab["total"], "step"
     else:
@@ -529,11 +565,14 @@ def main():
             "per_call_note": "events between the calls; prepare and slot mapping move under "
                              "1 MB here, so their time is launch and memory latency",
         },
+        "context": context,
         "state_calls": state,
         "gather_kv": gather,
         "prefix_cache": prefix,
         "cold_single_step": {
             "ms_median": statistics.median(cold),
+            "ms_p10": statistics.quantiles(cold, n=10)[0],
+            "ms_p90": statistics.quantiles(cold, n=10)[-1],
             "note": "1 GiB rewrite before each step; HIP events around the single launch",
         },
         "roofline": {
