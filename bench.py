@@ -465,6 +465,21 @@ def main():
     fused_ms, fused_wall = back_to_back(lambda s: s.run_fused(stream))
     calls_ms, calls_wall = back_to_back(lambda s: s.run(stream))
 
+    # The same steps captured once per batch in HIP graphs and replayed back to
+    # back: the three calls (three kernels per graph) and pkv_step.
+    graphs = {}
+    for name, run in (("three_calls", lambda s: s.run()), ("fused", lambda s: s.run_fused())):
+        gs = []
+        for s_ in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run(s_)
+            gs.append(g)
+        graphs[name] = gs
+    graph_ms = {name: back_to_back(lambda s, gs=gs: gs[steps.index(s)].replay())[0]
+                for name, gs in graphs.items()}
+    del graphs
+
     # Per-call split of the three calls (events between the calls add their own
     # overhead; for attribution only).
     split = {"prepare_batch": [], "compute_slot_mapping": [], "scatter_kv": []}
@@ -569,6 +584,11 @@ def main():
         "state_calls": state,
         "gather_kv": gather,
         "prefix_cache": prefix,
+        "hip_graph_replay": {
+            "three_calls_ms_per_step": graph_ms["three_calls"],
+            "fused_ms_per_step": graph_ms["fused"],
+            "note": "each batch's step captured once in a HIP graph, replays back to back",
+        },
         "cold_single_step": {
             "ms_median": statistics.median(cold),
             "ms_p10": statistics.quantiles(cold, n=10)[0],
