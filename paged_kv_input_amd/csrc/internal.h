@@ -253,9 +253,11 @@ __device__ inline void wave_sync()
 //   wave_gather  (index wavefront) loads rows and counts, then at once each
 //                row's completed count, and writes the keys and their original
 //                indices to LDS; the completed counts stay in registers;
-//   sort         bitonic sort of the keys, carrying the indices: by the index
-//                wavefront alone (wave_sort, n <= 64) or by every wavefront of
-//                the workgroup (block_sort, LDS traffic only, so the other
+//   sort         the keys put in order with their original indices: by the
+//                index wavefront alone for n <= 64 (rank_sort_wave: each key
+//                ranked by counting the keys before it, one LDS broadcast per
+//                key, no barrier), else by every wavefront of the workgroup
+//                (block_sort, a bitonic sort; LDS traffic only, so the other
 //                wavefronts' loads stay in flight);
 //   wave_finish  (index wavefront) prefix sums, rows, completed counts and the
 //                per-request outputs.
@@ -356,21 +358,8 @@ __device__ inline void bitonic_pass(WaveBatchLds<kMaxN>& w, int n_pad, int k, in
     }
 }
 
-// Sort by the index wavefront alone (call from that wavefront only).
-template <int kMaxN>
-__device__ inline void wave_sort(WaveBatchLds<kMaxN>& w, int32_t n)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int n_pad = pad_pow2(n);
-    wave_sync();
-    for (int k = 2; k <= n_pad; k <<= 1)
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            bitonic_pass(w, n_pad, k, j, lane, kWave);
-            wave_sync();
-        }
-}
-
-// Sort by all kThreads threads of the workgroup (call from every thread).
+// Bitonic sort by all kThreads threads of the workgroup (call from every
+// thread; LDS traffic only, so other wavefronts' loads stay in flight).
 template <int kThreads, int kMaxN>
 __device__ inline void block_sort(WaveBatchLds<kMaxN>& w, int32_t n)
 {
@@ -381,6 +370,46 @@ __device__ inline void block_sort(WaveBatchLds<kMaxN>& w, int32_t n)
             bitonic_pass(w, n_pad, k, j, (int)threadIdx.x, kThreads);
             __syncthreads();
         }
+}
+
+// Stable rank of each lane's key among run[0 .. len) (an LDS array holding
+// lane j's key at j; len <= 64): the number of keys that are smaller, plus the
+// equal ones held by lower lanes.  Every lane reads the same element at a
+// time (an LDS broadcast), eight reads in flight per batch.
+__device__ inline int wave_rank(const uint64_t* run, uint64_t key, int len)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    int rank = 0;
+    for (int j0 = 0; j0 < len; j0 += 8) {            // uniform
+        uint64_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = run[j0 + u < len ? j0 + u : len - 1];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u;
+            rank += (j < len && (v[u] < key || (v[u] == key && j < lane))) ? 1 : 0;
+        }
+    }
+    return rank;
+}
+
+// Batch order for n <= 64, by the index wavefront alone: each lane ranks its
+// key with wave_rank and stores key and original index at that rank.  Same
+// order as a stable sort of the keys (equal keys keep their schedule order).
+template <int kMaxN>
+__device__ inline void rank_sort_wave(WaveBatchLds<kMaxN>& w, int32_t n)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    wave_sync();                                      // wave_gather's keys are in LDS
+    const uint64_t key = lane < n ? w.b.key[lane] : ~0ull;
+    const int rank = wave_rank(w.b.key, key, n);
+    wave_sync();                                      // every key is read before any is moved
+    if (lane < n) {
+        w.b.key[rank] = key;
+        w.idx[rank] = (int16_t)lane;
+    }
+    wave_sync();
 }
 
 template <int kMaxN>

@@ -12,9 +12,10 @@
 // once (24 KiB of each per round; they depend on nothing) and wait at a
 // single barrier.
 // Meanwhile the index wavefront orders the batch itself in LDS
-// (wave_gather / wave_sort or block_sort / wave_finish: a bitonic sort of at
-// most PKV_STEP_MAX_BATCH keys, done by the index wavefront alone for small
-// batches and by every wavefront for large ones, and a wave-level scan), resolves the tile's tokens to requests by
+// (wave_gather / rank_sort_wave or block_sort / wave_finish: for at most 64
+// requests the index wavefront alone ranks every key by counting the keys
+// before it; for more, every wavefront joins a bitonic sort in LDS; then a
+// wave-level scan), resolves the tile's tokens to requests by
 // binary search, and computes positions, input ids and slots.  After the
 // barrier the copy wavefronts write the held rows to their slots.  Splitting
 // the roles across wavefronts matters: a wavefront's loads complete in issue
@@ -320,7 +321,9 @@ __device__ inline bool is_index_wave()
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)) == PKV_STEP_COPY_WAVES;
 }
 
-template <bool kPow2Row>
+// kBig: more than 64 requests, ordered by every wavefront (block_sort); the
+// two orderings get instantiations of their own.
+template <bool kPow2Row, bool kBig>
 __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a)
 {
     __shared__ WaveBatchLds<PKV_STEP_MAX_BATCH> wlds;
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a)
     const int tid = threadIdx.x;
     const int blk = blockIdx.x;
     const bool index_wave = is_index_wave();
-    const bool big = pad_pow2(a.n) > kWave;      // sort by every wavefront
+    constexpr bool big = kBig;                   // sort by every wavefront
     uint32_t flags = 0;
 
     // Which group and which part of it this workgroup serves (uniform).
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a)
             if (big)
                 block_sort<kStepThreads>(wlds, a.n);
             else
-                wave_sort(wlds, a.n);
+                rank_sort_wave(wlds, a.n);
             wave_finish(wlds, gth, a.n, a.T, a.R, blk == 0, a.index_mapping, a.query_start_loc,
                         a.seq_lens, flags);
             if (blk != 0)
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepArgs a)
             if (big)
                 block_sort<kStepThreads>(wlds, a.n);
             else
-                wave_sort(wlds, a.n);
+                rank_sort_wave(wlds, a.n);
             wave_finish(wlds, gth, a.n, a.T, a.R, blk == 0, a.index_mapping, a.query_start_loc,
                         a.seq_lens, flags);
             if (blk != 0)
@@ -501,10 +504,16 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
     bool pow2 = true;
     for (int i = 0; i < num_groups; ++i)
         pow2 = pow2 && a.g[i].row_shift >= 0;
-    if (pow2)
-        k_step<true><<<dim3((unsigned)blocks), dim3(kStepThreads), 0, stream>>>(a);
+    const bool big = n > kWave;
+    const dim3 grid((unsigned)blocks), block(kStepThreads);
+    if (pow2 && !big)
+        k_step<true, false><<<grid, block, 0, stream>>>(a);
+    else if (pow2)
+        k_step<true, true><<<grid, block, 0, stream>>>(a);
+    else if (!big)
+        k_step<false, false><<<grid, block, 0, stream>>>(a);
     else
-        k_step<false><<<dim3((unsigned)blocks), dim3(kStepThreads), 0, stream>>>(a);
+        k_step<false, true><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 
