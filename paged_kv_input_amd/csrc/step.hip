@@ -56,6 +56,19 @@ constexpr int kPageRows = kCopyThreads / kWave;           // batch rows per page
 // Persistent tile workgroups per group: every workgroup orders the batch once,
 // so large batches use fewer of them (measured on MI355X: 1536 is best for a
 // 16-request prefill, 512-1024 for 72-512 requests).
+// Tokens per tile: as many whole rows as one round of the copy wavefronts
+// moves, rounded down to a power of two, so that tiles never straddle a block
+// of a power-of-two block size (each tile writes one contiguous run of slots;
+// measured on MI355X: 8 instead of 9 rows of 2 KiB, 52.9 vs 53.9 us at the
+// 32k-token prefill).
+__host__ inline int64_t tile_tokens_for(int64_t chunks_per_row)
+{
+    int64_t tile = 1;
+    while (tile * 2 * chunks_per_row <= kStepChunks)
+        tile *= 2;
+    return tile;
+}
+
 __host__ inline int64_t tile_workgroups(int32_t n)
 {
     return n <= kWave ? PKV_STEP_WGS_PER_GROUP : PKV_STEP_WGS_PER_GROUP_BIG;
@@ -488,7 +501,7 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
         const int64_t cpr = in.row_bytes / 16;
         g.chunks_per_row = (int32_t)cpr;
         g.row_shift = (cpr & (cpr - 1)) == 0 ? __builtin_ctzll((unsigned long long)cpr) : -1;
-        int64_t tile = cpr >= kStepChunks ? 1 : kStepChunks / cpr;
+        int64_t tile = tile_tokens_for(cpr);
         if (tile > kStepMaxTile)
             tile = kStepMaxTile;
         g.tile_tokens = (int32_t)tile;
@@ -522,7 +535,7 @@ int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_gr
     int64_t blocks = 0;
     for (int i = 0; i < num_groups; ++i) {
         const int64_t cpr = groups[i].row_bytes / 16;
-        int64_t tile = cpr >= kStepChunks ? 1 : kStepChunks / cpr;
+        int64_t tile = tile_tokens_for(cpr);
         if (tile > kStepMaxTile)
             tile = kStepMaxTile;
         const int64_t tiles = ((int64_t)T + tile - 1) / tile;
