@@ -14,8 +14,9 @@ then exactly K timed steps back to back, bracketed by torch.cuda.synchronize()
 on both sides and by HIP events on the launch stream; ms_per_step is the
 event interval / K.  The step runs through pkv_step (one launch) and, timed
 the same way, through the three separate calls.  Secondary figures: the
-per-call split of the three calls, a single-step cold measurement (a 1 GiB
-rewrite before each step, events around it; median, p10, p90), ceilings to
+per-call split of the three calls, the host wall time of one step with the
+schedule uploaded from pinned host memory, a single-step cold measurement (a
+1 GiB rewrite before each step, events around it; median, p10, p90), ceilings to
 read the step against (a same-byte device copy, the dispatch floor), and the
 calls around the path: the state updates, the paged K/V read and the
 prefix-cache calls.
@@ -540,6 +541,23 @@ def main():
         split["compute_slot_mapping"].append(e[1].elapsed_time(e[2]))
         split["scatter_kv"].append(e[2].elapsed_time(e[3]))
 
+    # Host wall time of one step as a caller sees it: the schedule (rows and
+    # counts, n x 8 bytes) copied from pinned host memory, the fused step, a
+    # synchronize.  Each iteration starts on an idle GPU.
+    s0 = steps[0]
+    pin_rows = s0.sched_rows.cpu().pin_memory()
+    pin_counts = s0.num_scheduled.cpu().pin_memory()
+    upload_wall = []
+    for i in range(args.warmup + min(args.steps, 200)):
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        s0.sched_rows.copy_(pin_rows, non_blocking=True)
+        s0.num_scheduled.copy_(pin_counts, non_blocking=True)
+        s0.run_fused(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            upload_wall.append((time.perf_counter() - w0) * 1e6)
+
     # Single cold step: 1 GiB rewrite, then events around one fused step.
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
     cold = []
@@ -623,6 +641,13 @@ def main():
             "three_calls_ms_per_step": graph_ms["three_calls"],
             "fused_ms_per_step": graph_ms["fused"],
             "note": "each batch's step captured once in a HIP graph, replays back to back",
+        },
+        "host_wall_with_upload": {
+            "us_median": statistics.median(upload_wall),
+            "us_p10": statistics.quantiles(upload_wall, n=10)[0],
+            "us_p90": statistics.quantiles(upload_wall, n=10)[-1],
+            "note": "schedule (n x 8 bytes) copied from pinned host memory, pkv_step, "
+                    "synchronize; host clock, one step at a time from an idle GPU",
         },
         "cold_single_step": {
             "ms_median": statistics.median(cold),

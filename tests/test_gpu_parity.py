@@ -77,7 +77,7 @@ def test_seeded_small(name, mode):
 
 
 @pytest.mark.parametrize("name", ["decode_256x1", "mixed_8192", "prefill_16x2048",
-                                  "two_groups_512req"])
+                                  "prefill_16x2048_tp8", "two_groups_512req"])
 @pytest.mark.parametrize("mode", MODES)
 def test_reduced(name, mode):
     run_and_compare(workloads.make(name, reduced=True), full_cache=False, mode=mode)

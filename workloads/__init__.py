@@ -409,6 +409,9 @@ CONFIGS = {
     "decode_256x1": (lambda s: _decode_heavy(s), 2),
     "mixed_8192": (lambda s: _mixed_chunked(s), 3),
     "prefill_16x2048": (lambda s: _long_prefill(s), 4),
+    # One GPU's share when the KV heads are split over 8 GPUs: the same schedule,
+    # block tables and pool, one head of 128 bf16 per token (256-byte rows).
+    "prefill_16x2048_tp8": (lambda s: _long_prefill(s, H=1, name="prefill_16x2048_tp8"), 4),
     "two_groups_512req": (lambda s: _two_groups(s), 5),
 }
 
