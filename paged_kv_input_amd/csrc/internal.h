@@ -257,8 +257,9 @@ __device__ inline void wave_sync()
 //                index wavefront alone for n <= 64 (rank_sort_wave: each key
 //                ranked by counting the keys before it, one LDS broadcast per
 //                key, no barrier), else by every wavefront of the workgroup
-//                (block_sort, a bitonic sort; LDS traffic only, so the other
-//                wavefronts' loads stay in flight);
+//                (block_sort, a bitonic sort in registers with cross-lane
+//                moves and three LDS exchanges; no memory traffic, so the
+//                other wavefronts' loads stay in flight);
 //   wave_finish  (index wavefront) prefix sums, rows, completed counts and the
 //                per-request outputs.
 // The fetch of the completed counts thus overlaps the sort instead of adding a
@@ -268,6 +269,8 @@ struct WaveBatchLds {
     BatchLds<kMaxN, 1, true> b;
     int16_t idx[kMaxN];          // original index of each key during the sort
     int32_t done_by_i[kMaxN];    // completed count by original index
+    uint64_t xkey[kMaxN];        // block_sort's second exchange buffer
+    int16_t xidx[kMaxN];
 };
 
 template <int kMaxN>
@@ -336,40 +339,163 @@ __device__ inline void wave_gather(WaveBatchLds<kMaxN>& w, WaveGather<kMaxN>& gt
     }
 }
 
-// One bitonic compare-exchange pass (distance j inside sequences of size k)
-// over pairs first, first + step, ... of the n_pad / 2 pairs.
-template <int kMaxN>
-__device__ inline void bitonic_pass(WaveBatchLds<kMaxN>& w, int n_pad, int k, int j, int first,
-                                    int step)
+// Value of the same register in lane (lane ^ J) of the wavefront.  Distances
+// 1, 2, 4 and 8 stay inside a 16-lane row and use DPP moves (quad
+// permutations, the half-row mirror, the row rotation by 8); 16 uses an LDS
+// swizzle in bit mode and 32 a backward permute (neither touches LDS memory).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v)
 {
-    for (int i = first; i < (n_pad >> 1); i += step) {
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const int hi = lo + j;
-        const bool ascending = (lo & k) == 0;
-        const uint64_t a = w.b.key[lo];
-        const uint64_t b = w.b.key[hi];
-        if ((a > b) == ascending) {
-            w.b.key[lo] = b;
-            w.b.key[hi] = a;
-            const int16_t t = w.idx[lo];
-            w.idx[lo] = w.idx[hi];
-            w.idx[hi] = t;
-        }
+    const int x = (int)v;
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+    } else if constexpr (J == 4) {
+        // mirror in the 8-lane half row (i -> 7 - i), then reverse each quad
+        // (i -> 3 - i): together i -> i ^ 4
+        const int m = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);
+    } else if constexpr (J == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row rotate by 8
+    } else if constexpr (J == 16) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x1F | (16 << 10));   // and 31, xor 16
+    } else {
+        static_assert(J == 32, "lane distances 1 .. 32");
+        const int lane = (int)(threadIdx.x & (kWave - 1));
+        return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, x);
     }
 }
 
-// Bitonic sort by all kThreads threads of the workgroup (call from every
-// thread; LDS traffic only, so other wavefronts' loads stay in flight).
-template <int kThreads, int kMaxN>
-__device__ inline void block_sort(WaveBatchLds<kMaxN>& w, int32_t n)
+// Elements of the register bitonic sort: kPer per lane; element s of lane l
+// in wavefront w has sort index w * 64 * kPer + s * 64 + l.
+template <int kPer>
+struct SortRegs {
+    uint64_t key[kPer];
+    int32_t idx[kPer];
+};
+
+// Compare-exchange of the element a lane holds with the partner's (other):
+// the lower position of an ascending pair keeps the smaller key, and so on.
+// Strict comparisons on both sides, so equal keys never move and the indices
+// stay a permutation.
+__device__ __forceinline__ void keep(uint64_t& key, int32_t& idx, uint64_t okey, int32_t oidx,
+                                     bool lower, bool ascending)
 {
-    const int n_pad = pad_pow2(n);
-    __syncthreads();
-    for (int k = 2; k <= n_pad; k <<= 1)
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            bitonic_pass(w, n_pad, k, j, (int)threadIdx.x, kThreads);
-            __syncthreads();
+    const bool take = lower == ascending ? okey < key : key < okey;
+    key = take ? okey : key;
+    idx = take ? oidx : idx;
+}
+
+template <int J, int kPer>
+__device__ __forceinline__ void lane_pass(SortRegs<kPer>& r, int base, int k)
+{
+    const int lane = (int)(threadIdx.x & (kWave - 1));
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+        const uint32_t lo = lane_xor<J>((uint32_t)r.key[s]);
+        const uint32_t hi = lane_xor<J>((uint32_t)(r.key[s] >> 32));
+        const int32_t oidx = (int32_t)lane_xor<J>((uint32_t)r.idx[s]);
+        const int i = base + s * kWave + lane;
+        keep(r.key[s], r.idx[s], ((uint64_t)hi << 32) | lo, oidx, (lane & J) == 0, (i & k) == 0);
+    }
+}
+
+// Bitonic sort of n <= 64 * kPer * (kThreads / 64) keys by every wavefront of
+// the workgroup (call from every thread).  The keys and their original indices
+// stay in registers: pairs closer than 64 are exchanged between lanes, pairs
+// 64 .. 64 * (kPer - 1) apart inside a lane, and only pairs in different
+// wavefronts go through LDS, with one barrier each (three passes for both
+// sizes used, alternating between two buffers).  Input and output are
+// w.b.key[0 .. n) and w.idx[0 .. n); LDS traffic only, so the other
+// wavefronts' loads stay in flight.
+template <int kThreads, int kPer, int kMaxN>
+__device__ __forceinline__ void block_sort_regs(WaveBatchLds<kMaxN>& w, int32_t n)
+{
+    constexpr int kSpan = kWave * kPer;                  // elements per wavefront
+    constexpr int kPad = kThreads * kPer;
+    static_assert(kPad <= kMaxN, "the exchange buffers hold kPad elements");
+    const int lane = (int)(threadIdx.x & (kWave - 1));
+    const int base = (int)(threadIdx.x / kWave) * kSpan;
+    SortRegs<kPer> r;
+    __syncthreads();                                      // wave_gather's keys are in LDS
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+        const int i = base + s * kWave + lane;
+        r.key[s] = i < n ? w.b.key[i] : ~0ull;            // padding sorts last
+        r.idx[s] = i < n ? w.idx[i] : i;
+    }
+    int pass = 0;                                         // LDS passes so far
+    for (int k = 2; k <= kPad; k <<= 1) {
+        for (int j = k >> 1; j >= kWave; j >>= 1) {
+            if (j >= kSpan) {
+                // partner in another wavefront
+                uint64_t* bk = (pass & 1) ? w.b.key : w.xkey;
+                int16_t* bi = (pass & 1) ? w.idx : w.xidx;
+#pragma unroll
+                for (int s = 0; s < kPer; ++s) {
+                    const int i = base + s * kWave + lane;
+                    bk[i] = r.key[s];
+                    bi[i] = (int16_t)r.idx[s];
+                }
+                __syncthreads();
+#pragma unroll
+                for (int s = 0; s < kPer; ++s) {
+                    const int i = base + s * kWave + lane;
+                    keep(r.key[s], r.idx[s], bk[i ^ j], bi[i ^ j], (i & j) == 0, (i & k) == 0);
+                }
+                ++pass;
+            } else {
+                // partner in the same lane: slots s and s ^ (j / 64)
+                const int d = j / kWave;
+#pragma unroll
+                for (int s = 0; s < kPer; ++s) {
+                    const int o = s ^ d;
+                    if (o > s) {
+                        const int i = base + s * kWave + lane;
+                        const bool ascending = (i & k) == 0;
+                        const bool swap = ascending ? r.key[o] < r.key[s] : r.key[s] < r.key[o];
+                        const uint64_t tk = r.key[s];
+                        const int32_t ti = r.idx[s];
+                        r.key[s] = swap ? r.key[o] : r.key[s];
+                        r.idx[s] = swap ? r.idx[o] : r.idx[s];
+                        r.key[o] = swap ? tk : r.key[o];
+                        r.idx[o] = swap ? ti : r.idx[o];
+                    }
+                }
+            }
         }
+        if (k > 32) lane_pass<32>(r, base, k);
+        if (k > 16) lane_pass<16>(r, base, k);
+        if (k > 8) lane_pass<8>(r, base, k);
+        if (k > 4) lane_pass<4>(r, base, k);
+        if (k > 2) lane_pass<2>(r, base, k);
+        lane_pass<1>(r, base, k);
+    }
+    // The last LDS pass read the other buffer; when it read this one too, wait
+    // for every wavefront before overwriting it.
+    if (!(pass & 1))
+        __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+        const int i = base + s * kWave + lane;
+        if (i < n) {
+            w.b.key[i] = r.key[s];
+            w.idx[i] = (int16_t)r.idx[s];
+        }
+    }
+    __syncthreads();
+}
+
+// Bitonic sort of 64 < n <= kThreads * 2 keys by every wavefront (call from
+// every thread): one element per lane up to kThreads keys, else two.
+template <int kThreads, int kMaxN>
+__device__ __forceinline__ void block_sort(WaveBatchLds<kMaxN>& w, int32_t n)
+{
+    if (n <= kThreads)
+        block_sort_regs<kThreads, 1>(w, n);
+    else
+        block_sort_regs<kThreads, 2>(w, n);
 }
 
 // Stable rank of each lane's key among run[0 .. len) (an LDS array holding

@@ -14,8 +14,8 @@
 // Meanwhile the index wavefront orders the batch itself in LDS
 // (wave_gather / rank_sort_wave or block_sort / wave_finish: for at most 64
 // requests the index wavefront alone ranks every key by counting the keys
-// before it; for more, every wavefront joins a bitonic sort in LDS; then a
-// wave-level scan), resolves the tile's tokens to requests by
+// before it; for more, every wavefront joins a bitonic sort held in
+// registers, with three exchanges through LDS; then a wave-level scan), resolves the tile's tokens to requests by
 // binary search, and computes positions, input ids and slots.  After the
 // barrier the copy wavefronts write the held rows to their slots.  Splitting
 // the roles across wavefronts matters: a wavefront's loads complete in issue
