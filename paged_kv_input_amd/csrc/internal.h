@@ -82,6 +82,222 @@ __device__ inline uint64_t sort_key(int32_t count, int32_t row)
 __device__ inline int32_t key_count(uint64_t key) { return (int32_t)(key >> 32); }
 __device__ inline int32_t key_row(uint64_t key) { return (int32_t)((uint32_t)key ^ 0x80000000u); }
 
+__device__ inline int pad_pow2(int n)
+{
+    int n_pad = 1;
+    while (n_pad < n)
+        n_pad <<= 1;
+    return n_pad;
+}
+
+// Value of the same register in lane (lane ^ J) of the wavefront.  Distances
+// 1, 2, 4 and 8 stay inside a 16-lane row and use DPP moves (quad
+// permutations, the half-row mirror, the row rotation by 8); 16 uses an LDS
+// swizzle in bit mode and 32 a backward permute (neither touches LDS memory).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v)
+{
+    const int x = (int)v;
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+    } else if constexpr (J == 4) {
+        // mirror in the 8-lane half row (i -> 7 - i), then reverse each quad
+        // (i -> 3 - i): together i -> i ^ 4
+        const int m = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);
+    } else if constexpr (J == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row rotate by 8
+    } else if constexpr (J == 16) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x1F | (16 << 10));   // and 31, xor 16
+    } else {
+        static_assert(J == 32, "lane distances 1 .. 32");
+        const int lane = (int)(threadIdx.x & (kWave - 1));
+        return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, x);
+    }
+}
+
+// Elements of the register bitonic sort: kPer per lane (element s of lane l in
+// wavefront w has sort index w * 64 * kPer + s * 64 + l), each a 64-bit key
+// and, when kIdx, the key's original index.
+template <int kPer, bool kIdx>
+struct SortRegs {
+    uint64_t key[kPer];
+    int32_t idx[kIdx ? kPer : 1];
+};
+
+// Compare-exchange of element s with the partner's (okey, oidx): the lower
+// position of an ascending pair keeps the smaller key, and so on.  Strict
+// comparisons on both sides, so equal keys never move and the indices stay a
+// permutation.
+template <int kPer, bool kIdx>
+__device__ __forceinline__ void keep(SortRegs<kPer, kIdx>& r, int s, uint64_t okey, int32_t oidx,
+                                     bool lower, bool ascending)
+{
+    const bool take = lower == ascending ? okey < r.key[s] : r.key[s] < okey;
+    r.key[s] = take ? okey : r.key[s];
+    if constexpr (kIdx)
+        r.idx[s] = take ? oidx : r.idx[s];
+}
+
+template <int J, int kPer, bool kIdx>
+__device__ __forceinline__ void lane_pass(SortRegs<kPer, kIdx>& r, int base, int k)
+{
+    const int lane = (int)(threadIdx.x & (kWave - 1));
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+        const uint32_t lo = lane_xor<J>((uint32_t)r.key[s]);
+        const uint32_t hi = lane_xor<J>((uint32_t)(r.key[s] >> 32));
+        int32_t oidx = 0;
+        if constexpr (kIdx)
+            oidx = (int32_t)lane_xor<J>((uint32_t)r.idx[s]);
+        const int i = base + s * kWave + lane;
+        keep(r, s, ((uint64_t)hi << 32) | lo, oidx, (lane & J) == 0, (i & k) == 0);
+    }
+}
+
+// Compare-exchange of slots s and s ^ D of each lane (elements 64 * D apart).
+template <int D, int kPer, bool kIdx>
+__device__ __forceinline__ void slot_pass(SortRegs<kPer, kIdx>& r, int base, int k)
+{
+    const int lane = (int)(threadIdx.x & (kWave - 1));
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+        const int o = s ^ D;
+        if (o > s && o < kPer) {
+            const int i = base + s * kWave + lane;
+            const bool ascending = (i & k) == 0;
+            const bool swap = ascending ? r.key[o] < r.key[s] : r.key[s] < r.key[o];
+            const uint64_t tk = r.key[s];
+            r.key[s] = swap ? r.key[o] : r.key[s];
+            r.key[o] = swap ? tk : r.key[o];
+            if constexpr (kIdx) {
+                const int32_t ti = r.idx[s];
+                r.idx[s] = swap ? r.idx[o] : r.idx[s];
+                r.idx[o] = swap ? ti : r.idx[o];
+            }
+        }
+    }
+}
+
+// Ascending bitonic sort of key[0 .. n) (with idx[0 .. n), the keys' original
+// indices, when kIdx) by every wavefront of a kThreads-thread workgroup; call
+// from every thread with the same n <= kPad.  The network spans kPad (a power
+// of two, at most kThreads * kPer) positions, padded with ~0 keys, and is
+// unrolled whole.  The elements stay in registers: pairs closer than 64 are
+// exchanged between lanes, pairs 64 .. 64 * (kPer - 1) apart are swapped
+// inside a lane, and only pairs in different wavefronts go through LDS.
+// Wavefronts holding only padding skip the work but keep the barriers.  With
+// a second buffer (kTwo: xkey, xidx) an LDS exchange costs one barrier,
+// alternating between the buffers; without one, two.  LDS traffic only, so
+// the wavefronts' outstanding loads stay in flight.  key / idx hold the result
+// on return, after a barrier.
+template <int kThreads, int kPer, int kPad, bool kIdx, bool kTwo>
+__device__ __forceinline__ void bitonic_regs(uint64_t* key, int16_t* idx, uint64_t* xkey,
+                                             int16_t* xidx, int32_t n)
+{
+    constexpr int kSpan = kWave * kPer;                  // elements per wavefront
+    static_assert(kPad >= 2 && (kPad & (kPad - 1)) == 0 && kPad <= kThreads * kPer,
+                  "the network spans a power of two of the workgroup's elements");
+    const int lane = (int)(threadIdx.x & (kWave - 1));
+    const int base = (int)(threadIdx.x / kWave) * kSpan;
+    const bool active = base < kPad;                      // uniform per wavefront
+    SortRegs<kPer, kIdx> r;
+    __syncthreads();                                      // the keys are in LDS
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+        const int i = base + s * kWave + lane;
+        r.key[s] = i < n ? key[i] : ~0ull;                // padding sorts last
+        if constexpr (kIdx)
+            r.idx[s] = i < n ? idx[i] : i;
+    }
+    int pass = 0;                                         // LDS exchanges so far
+#pragma unroll
+    for (int k = 2; k <= kPad; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j >= kWave; j >>= 1) {
+            if (j >= kSpan) {
+                // partner in another wavefront
+                const bool second = kTwo && (pass & 1) == 0;
+                uint64_t* bk = second ? xkey : key;
+                int16_t* bi = second ? xidx : idx;
+                if (!kTwo)
+                    __syncthreads();                      // the buffer's last reads are done
+                if (active) {
+#pragma unroll
+                    for (int s = 0; s < kPer; ++s) {
+                        const int i = base + s * kWave + lane;
+                        bk[i] = r.key[s];
+                        if constexpr (kIdx)
+                            bi[i] = (int16_t)r.idx[s];
+                    }
+                }
+                __syncthreads();
+                if (active) {
+#pragma unroll
+                    for (int s = 0; s < kPer; ++s) {
+                        const int i = base + s * kWave + lane;
+                        int32_t oidx = 0;
+                        if constexpr (kIdx)
+                            oidx = bi[i ^ j];
+                        keep(r, s, bk[i ^ j], oidx, (i & j) == 0, (i & k) == 0);
+                    }
+                }
+                ++pass;
+            } else if (active) {
+                // partner in the same lane: slot s ^ (j / 64)
+                if (j == kWave)
+                    slot_pass<1>(r, base, k);
+                else
+                    slot_pass<2>(r, base, k);
+            }
+        }
+        if (active) {
+            if (k > 32) lane_pass<32>(r, base, k);
+            if (k > 16) lane_pass<16>(r, base, k);
+            if (k > 8) lane_pass<8>(r, base, k);
+            if (k > 4) lane_pass<4>(r, base, k);
+            if (k > 2) lane_pass<2>(r, base, k);
+            lane_pass<1>(r, base, k);
+        }
+    }
+    // key / idx were read by the initial loads or by an exchange: wait for every
+    // wavefront before overwriting them, unless the last exchange used the
+    // second buffer (every read of key / idx then came before its barrier).
+    if (!kTwo || (pass & 1) == 0)
+        __syncthreads();
+    if (active) {
+#pragma unroll
+        for (int s = 0; s < kPer; ++s) {
+            const int i = base + s * kWave + lane;
+            if (i < n) {
+                key[i] = r.key[s];
+                if constexpr (kIdx)
+                    idx[i] = (int16_t)r.idx[s];
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Ascending sort of key[0 .. n) by bitonic_regs over the smallest network of
+// kPad = 64, 128, ... positions that holds n <= kMaxN keys (one key per lane up
+// to kThreads keys, then two or four).  Call from every thread.
+template <int kThreads, int kMaxN, int kPad = kWave>
+__device__ __forceinline__ void sort_keys(uint64_t* key, int32_t n)
+{
+    constexpr int kPer = kPad <= kThreads ? 1 : kPad / kThreads;
+    if constexpr (kPad >= kMaxN) {
+        bitonic_regs<kThreads, kPer, kPad, false, false>(key, nullptr, nullptr, nullptr, n);
+    } else {
+        if (n <= kPad)
+            bitonic_regs<kThreads, kPer, kPad, false, false>(key, nullptr, nullptr, nullptr, n);
+        else
+            sort_keys<kThreads, kMaxN, kPad * 2>(key, n);
+    }
+}
+
 // LDS working set of order_batch for up to kMaxN requests.  The keys are dead
 // once ordered, so the per-request rows and completed counts reuse them.
 template <int kMaxN, int kWaves, bool kCounts = false>
@@ -98,14 +314,14 @@ struct BatchLds {
 
 // Batch assembly inside one workgroup ("Batch Construction and Sequence
 // Flattening" of the kongchang.com article): gather the n scheduled requests
-// as (count, row) keys, bitonic-sort them ascending in LDS, prefix-sum the
+// as (count, row) keys, sort them ascending (bitonic_regs), prefix-sum the
 // sorted counts (wave-level scan plus one cross-wave pass, saturating at
 // INT32_MAX) and fetch each request's completed count.  On return, after a
 // barrier, lds.qsl[0..n], lds.row()[0..n) and lds.done()[0..n) describe the
 // batch in order (and lds.count[0..n) when kCounts).  A writer workgroup also
-// stores index_mapping,
-// query_start_loc and seq_lens and collects BAD_ROW / TOKEN_SUM; every caller
-// gets BAD_COUNT for negative counts (read as 0).  n <= kMaxN.
+// stores index_mapping, query_start_loc and seq_lens and collects BAD_ROW /
+// TOKEN_SUM; every caller gets BAD_COUNT for negative counts (read as 0).
+// n <= kMaxN.
 template <int kThreads, int kMaxN, bool kCounts>
 __device__ inline void order_batch(BatchLds<kMaxN, kThreads / kWave, kCounts>& lds, int32_t n,
                                    int32_t T,
@@ -119,44 +335,18 @@ __device__ inline void order_batch(BatchLds<kMaxN, kThreads / kWave, kCounts>& l
     constexpr int kWaves = kThreads / kWave;
     constexpr int kPer = kMaxN / kThreads;       // batch rows per thread in the scan
     static_assert(kMaxN % kThreads == 0, "batch rows split evenly over threads");
+    static_assert(kPer <= 4, "the sort holds at most four keys per lane");
     const int tid = threadIdx.x;
 
-    int n_pad = 1;
-    while (n_pad < n)
-        n_pad <<= 1;
-    for (int i = tid; i < n_pad; i += kThreads) {
-        uint64_t key = ~0ull;                       // padding sorts last
-        if (i < n) {
-            int32_t c = num_scheduled[i];
-            if (c < 0) {
-                flags |= PKV_ST_BAD_COUNT;
-                c = 0;
-            }
-            key = sort_key(c, sched_rows[i]);
+    for (int i = tid; i < n; i += kThreads) {
+        int32_t c = num_scheduled[i];
+        if (c < 0) {
+            flags |= PKV_ST_BAD_COUNT;
+            c = 0;
         }
-        lds.key[i] = key;
+        lds.key[i] = sort_key(c, sched_rows[i]);
     }
-    __syncthreads();
-
-    // Bitonic sort, ascending.  Pair i of a stage with distance j compares
-    // element lo (bit log2(j) cleared) with lo + j; the sub-sequence direction
-    // comes from bit log2(k) of lo.
-    for (int k = 2; k <= n_pad; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < (n_pad >> 1); i += kThreads) {
-                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-                const int hi = lo + j;
-                const bool ascending = (lo & k) == 0;
-                const uint64_t a = lds.key[lo];
-                const uint64_t b = lds.key[hi];
-                if ((a > b) == ascending) {
-                    lds.key[lo] = b;
-                    lds.key[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
+    sort_keys<kThreads, kMaxN>(lds.key, n);
 
     // Each thread owns kPer consecutive batch rows.
     uint64_t keys[kPer];
@@ -279,14 +469,6 @@ struct WaveGather {
     int32_t done_i[kPer];        // completed count of request e * 64 + lane
 };
 
-__device__ inline int pad_pow2(int n)
-{
-    int n_pad = 1;
-    while (n_pad < n)
-        n_pad <<= 1;
-    return n_pad;
-}
-
 template <int kMaxN>
 __device__ inline void wave_gather(WaveBatchLds<kMaxN>& w, WaveGather<kMaxN>& gth, int32_t n,
                                    const int32_t* __restrict__ sched_rows,
@@ -339,163 +521,17 @@ __device__ inline void wave_gather(WaveBatchLds<kMaxN>& w, WaveGather<kMaxN>& gt
     }
 }
 
-// Value of the same register in lane (lane ^ J) of the wavefront.  Distances
-// 1, 2, 4 and 8 stay inside a 16-lane row and use DPP moves (quad
-// permutations, the half-row mirror, the row rotation by 8); 16 uses an LDS
-// swizzle in bit mode and 32 a backward permute (neither touches LDS memory).
-template <int J>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v)
-{
-    const int x = (int)v;
-    if constexpr (J == 1) {
-        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
-    } else if constexpr (J == 2) {
-        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
-    } else if constexpr (J == 4) {
-        // mirror in the 8-lane half row (i -> 7 - i), then reverse each quad
-        // (i -> 3 - i): together i -> i ^ 4
-        const int m = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
-        return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);
-    } else if constexpr (J == 8) {
-        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row rotate by 8
-    } else if constexpr (J == 16) {
-        return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x1F | (16 << 10));   // and 31, xor 16
-    } else {
-        static_assert(J == 32, "lane distances 1 .. 32");
-        const int lane = (int)(threadIdx.x & (kWave - 1));
-        return (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, x);
-    }
-}
-
-// Elements of the register bitonic sort: kPer per lane; element s of lane l
-// in wavefront w has sort index w * 64 * kPer + s * 64 + l.
-template <int kPer>
-struct SortRegs {
-    uint64_t key[kPer];
-    int32_t idx[kPer];
-};
-
-// Compare-exchange of the element a lane holds with the partner's (other):
-// the lower position of an ascending pair keeps the smaller key, and so on.
-// Strict comparisons on both sides, so equal keys never move and the indices
-// stay a permutation.
-__device__ __forceinline__ void keep(uint64_t& key, int32_t& idx, uint64_t okey, int32_t oidx,
-                                     bool lower, bool ascending)
-{
-    const bool take = lower == ascending ? okey < key : key < okey;
-    key = take ? okey : key;
-    idx = take ? oidx : idx;
-}
-
-template <int J, int kPer>
-__device__ __forceinline__ void lane_pass(SortRegs<kPer>& r, int base, int k)
-{
-    const int lane = (int)(threadIdx.x & (kWave - 1));
-#pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-        const uint32_t lo = lane_xor<J>((uint32_t)r.key[s]);
-        const uint32_t hi = lane_xor<J>((uint32_t)(r.key[s] >> 32));
-        const int32_t oidx = (int32_t)lane_xor<J>((uint32_t)r.idx[s]);
-        const int i = base + s * kWave + lane;
-        keep(r.key[s], r.idx[s], ((uint64_t)hi << 32) | lo, oidx, (lane & J) == 0, (i & k) == 0);
-    }
-}
-
-// Bitonic sort of n <= 64 * kPer * (kThreads / 64) keys by every wavefront of
-// the workgroup (call from every thread).  The keys and their original indices
-// stay in registers: pairs closer than 64 are exchanged between lanes, pairs
-// 64 .. 64 * (kPer - 1) apart inside a lane, and only pairs in different
-// wavefronts go through LDS, with one barrier each (three passes for both
-// sizes used, alternating between two buffers).  Input and output are
-// w.b.key[0 .. n) and w.idx[0 .. n); LDS traffic only, so the other
-// wavefronts' loads stay in flight.
-template <int kThreads, int kPer, int kMaxN>
-__device__ __forceinline__ void block_sort_regs(WaveBatchLds<kMaxN>& w, int32_t n)
-{
-    constexpr int kSpan = kWave * kPer;                  // elements per wavefront
-    constexpr int kPad = kThreads * kPer;
-    static_assert(kPad <= kMaxN, "the exchange buffers hold kPad elements");
-    const int lane = (int)(threadIdx.x & (kWave - 1));
-    const int base = (int)(threadIdx.x / kWave) * kSpan;
-    SortRegs<kPer> r;
-    __syncthreads();                                      // wave_gather's keys are in LDS
-#pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-        const int i = base + s * kWave + lane;
-        r.key[s] = i < n ? w.b.key[i] : ~0ull;            // padding sorts last
-        r.idx[s] = i < n ? w.idx[i] : i;
-    }
-    int pass = 0;                                         // LDS passes so far
-    for (int k = 2; k <= kPad; k <<= 1) {
-        for (int j = k >> 1; j >= kWave; j >>= 1) {
-            if (j >= kSpan) {
-                // partner in another wavefront
-                uint64_t* bk = (pass & 1) ? w.b.key : w.xkey;
-                int16_t* bi = (pass & 1) ? w.idx : w.xidx;
-#pragma unroll
-                for (int s = 0; s < kPer; ++s) {
-                    const int i = base + s * kWave + lane;
-                    bk[i] = r.key[s];
-                    bi[i] = (int16_t)r.idx[s];
-                }
-                __syncthreads();
-#pragma unroll
-                for (int s = 0; s < kPer; ++s) {
-                    const int i = base + s * kWave + lane;
-                    keep(r.key[s], r.idx[s], bk[i ^ j], bi[i ^ j], (i & j) == 0, (i & k) == 0);
-                }
-                ++pass;
-            } else {
-                // partner in the same lane: slots s and s ^ (j / 64)
-                const int d = j / kWave;
-#pragma unroll
-                for (int s = 0; s < kPer; ++s) {
-                    const int o = s ^ d;
-                    if (o > s) {
-                        const int i = base + s * kWave + lane;
-                        const bool ascending = (i & k) == 0;
-                        const bool swap = ascending ? r.key[o] < r.key[s] : r.key[s] < r.key[o];
-                        const uint64_t tk = r.key[s];
-                        const int32_t ti = r.idx[s];
-                        r.key[s] = swap ? r.key[o] : r.key[s];
-                        r.idx[s] = swap ? r.idx[o] : r.idx[s];
-                        r.key[o] = swap ? tk : r.key[o];
-                        r.idx[o] = swap ? ti : r.idx[o];
-                    }
-                }
-            }
-        }
-        if (k > 32) lane_pass<32>(r, base, k);
-        if (k > 16) lane_pass<16>(r, base, k);
-        if (k > 8) lane_pass<8>(r, base, k);
-        if (k > 4) lane_pass<4>(r, base, k);
-        if (k > 2) lane_pass<2>(r, base, k);
-        lane_pass<1>(r, base, k);
-    }
-    // The last LDS pass read the other buffer; when it read this one too, wait
-    // for every wavefront before overwriting it.
-    if (!(pass & 1))
-        __syncthreads();
-#pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-        const int i = base + s * kWave + lane;
-        if (i < n) {
-            w.b.key[i] = r.key[s];
-            w.idx[i] = (int16_t)r.idx[s];
-        }
-    }
-    __syncthreads();
-}
-
-// Bitonic sort of 64 < n <= kThreads * 2 keys by every wavefront (call from
-// every thread): one element per lane up to kThreads keys, else two.
+// Bitonic sort of 64 < n <= kThreads * 2 keys with their original indices by
+// every wavefront of the workgroup (call from every thread): one element per
+// lane up to kThreads keys, else two.  w.xkey / w.xidx serve as the second
+// exchange buffer.
 template <int kThreads, int kMaxN>
 __device__ __forceinline__ void block_sort(WaveBatchLds<kMaxN>& w, int32_t n)
 {
     if (n <= kThreads)
-        block_sort_regs<kThreads, 1>(w, n);
+        bitonic_regs<kThreads, 1, kThreads, true, true>(w.b.key, w.idx, w.xkey, w.xidx, n);
     else
-        block_sort_regs<kThreads, 2>(w, n);
+        bitonic_regs<kThreads, 2, 2 * kThreads, true, true>(w.b.key, w.idx, w.xkey, w.xidx, n);
 }
 
 // Stable rank of each lane's key among run[0 .. len) (an LDS array holding
