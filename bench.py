@@ -181,7 +181,15 @@ def cpu_baseline(workload, seed, budget_s):
     _CPU_BATCH = None
     tokens = sum(r[0] for r in runs)
     wall = max(r[1] for r in runs)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return dict(value=tokens / wall, unit="tokens/s", cores=workers, kind="oracle",
+                cpu_model=cpu_model,
                 sample=f"the full {workload} step, {workers} processes (one per host core) each "
                        f"repeating it for about {par_budget:.1f} s ({sum(r[2] for r in runs)} steps "
                        f"in all); plain C oracle, gcc -O2",
@@ -401,6 +409,28 @@ def prefix_calls(batch, step, steps, warmup, stream):
     return out
 
 
+def device_hbm_peak():
+    """HBM peak from the device's own figures: 2 transfers per memory clock x
+    the bus width (HIP's device attributes, read through the HIP runtime)."""
+    import ctypes
+
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    # hipDeviceAttribute_t values of this ROCm's hip_runtime_api.h
+    bus_attr, clock_attr = 59, 60
+    vals = []
+    for attr in (bus_attr, clock_attr):
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) != 0:
+            return None
+        vals.append(v.value)
+    bus_bits, clock_khz = vals
+    return {"bus_width_bits": bus_bits, "memory_clock_khz": clock_khz,
+            "gbs": 2.0 * clock_khz * 1e3 * bus_bits / 8 / 1e9}
+
+
 def context_figures(step_bytes, steps, warmup, stream):
     """Ceilings to read the step against (not targets): a device-to-device copy
     moving the same bytes (half read, half written; torch's copy kernel, four
@@ -429,7 +459,8 @@ def context_figures(step_bytes, steps, warmup, stream):
     tiny_ms = timed(lambda i: one.add_(1), max(steps, 1000))
     return {"d2d_copy_same_bytes": {"ms": copy_ms, "bytes": 2 * half,
                                     "gbs": 2 * half / (copy_ms * 1e-3) / 1e9},
-            "tiny_kernel_us": tiny_ms * 1e3}
+            "tiny_kernel_us": tiny_ms * 1e3,
+            "hbm_peak_from_device": device_hbm_peak()}
 
 
 def main():
