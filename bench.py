@@ -410,8 +410,10 @@ def prefix_calls(batch, step, steps, warmup, stream):
 
 
 def device_hbm_peak():
-    """HBM peak from the device's own figures: 2 transfers per memory clock x
-    the bus width (HIP's device attributes, read through the HIP runtime)."""
+    """HBM peak from the device's own figures (HIP's device attributes, read
+    through the HIP runtime): bus width x memory clock x transfers per clock.
+    HBM3E pins run at four transfers per reported memory clock (8 Gb/s at
+    2 GHz), so on MI355X this gives 8192 bits x 2 GHz x 4 / 8 = 8.19 TB/s."""
     import ctypes
 
     try:
@@ -427,8 +429,8 @@ def device_hbm_peak():
             return None
         vals.append(v.value)
     bus_bits, clock_khz = vals
-    return {"bus_width_bits": bus_bits, "memory_clock_khz": clock_khz,
-            "gbs": 2.0 * clock_khz * 1e3 * bus_bits / 8 / 1e9}
+    return {"bus_width_bits": bus_bits, "memory_clock_khz": clock_khz, "transfers_per_clock": 4,
+            "gbs": 4.0 * clock_khz * 1e3 * bus_bits / 8 / 1e9}
 
 
 def context_figures(step_bytes, steps, warmup, stream):
