@@ -39,11 +39,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define PKV_STEP_UNROLL 6
 #endif
 
-#ifndef PKV_STEP_WGS_PER_GROUP
-#define PKV_STEP_WGS_PER_GROUP 1536        // persistent tile workgroups per group, n <= 64
-#endif
-#ifndef PKV_STEP_WGS_PER_GROUP_BIG
-#define PKV_STEP_WGS_PER_GROUP_BIG 1024    // n > 64: fewer workgroups, fewer sorts
+#ifndef PKV_STEP_TILE_WGS
+#define PKV_STEP_TILE_WGS 1536             // persistent tile workgroups per step, over all groups
 #endif
 
 constexpr int kCopyThreads = PKV_STEP_COPY_WAVES * kWave; // copy wavefronts
@@ -53,9 +50,9 @@ constexpr int kStepChunks = kCopyThreads * kStepUnroll;   // 16-byte chunks per 
 constexpr int kStepMaxTile = 256;                         // tokens per tile, at most
 constexpr int kTokensPerLane = kStepMaxTile / kWave;
 constexpr int kPageRows = kCopyThreads / kWave;           // batch rows per page workgroup
-// Persistent tile workgroups per group: every workgroup orders the batch once,
-// so large batches use fewer of them (measured on MI355X: 1536 is best for a
-// 16-request prefill, 512-1024 for 72-512 requests).
+// Persistent tile workgroups: 1536 per step, split evenly over the groups
+// (measured on MI355X: best for a 16-request prefill; for 512 requests in two
+// groups 768 per group beat 512 and 1024; fewer were slower for 72 requests).
 // Tokens per tile: as many whole rows as one round of the copy wavefronts
 // moves, rounded down to a power of two, so that tiles never straddle a block
 // of a power-of-two block size (each tile writes one contiguous run of slots;
@@ -69,9 +66,10 @@ __host__ inline int64_t tile_tokens_for(int64_t chunks_per_row)
     return tile;
 }
 
-__host__ inline int64_t tile_workgroups(int32_t n)
+__host__ inline int64_t tile_workgroups(int32_t num_groups)
 {
-    return n <= kWave ? PKV_STEP_WGS_PER_GROUP : PKV_STEP_WGS_PER_GROUP_BIG;
+    const int64_t per = PKV_STEP_TILE_WGS / (num_groups > 0 ? num_groups : 1);
+    return per > 0 ? per : 1;
 }
 
 struct StepGroup {
@@ -508,7 +506,8 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
         g.rounds = (int32_t)((tile * cpr + kStepChunks - 1) / kStepChunks);
         g.first_block = (int32_t)blocks;
         g.tiles = (int32_t)(((int64_t)T + tile - 1) / tile);
-        g.tile_blocks = (int32_t)(g.tiles < tile_workgroups(n) ? g.tiles : tile_workgroups(n));
+        g.tile_blocks = (int32_t)(g.tiles < tile_workgroups(num_groups) ? g.tiles
+                                                                         : tile_workgroups(num_groups));
         g.page_blocks = in.input_block_tables != nullptr ? (n + kPageRows - 1) / kPageRows : 0;
         blocks += (int64_t)g.tile_blocks + g.page_blocks;
     }
@@ -539,7 +538,7 @@ int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_gr
         if (tile > kStepMaxTile)
             tile = kStepMaxTile;
         const int64_t tiles = ((int64_t)T + tile - 1) / tile;
-        blocks += tiles < tile_workgroups(n) ? tiles : tile_workgroups(n);
+        blocks += tiles < tile_workgroups(num_groups) ? tiles : tile_workgroups(num_groups);
         if (groups[i].input_block_tables != nullptr)
             blocks += (n + kPageRows - 1) / kPageRows;
     }
