@@ -219,6 +219,14 @@ def test_fused_batch_sizes(n):
     run_and_compare(b, mode="fused")
 
 
+@pytest.mark.parametrize("groups", [4, 5, 7])
+def test_fused_group_counts(groups):
+    """pkv_step with up to the kernel's group limit in one launch, and past it
+    (the separate kernels); mixed block sizes and row widths."""
+    b = workloads.random_tiny(900 + groups, max_n=8, max_T=64, groups=groups)
+    run_and_compare(b, mode="fused")
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_error_inputs_match_oracle(mode):
     """Bad rows, negative counts, a token-sum mismatch, positions past the table,
