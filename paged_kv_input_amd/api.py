@@ -129,12 +129,6 @@ def error_string(code: int) -> str:
     return _lib.pkv_error_string(code).decode()
 
 
-def _stream(stream) -> Optional[int]:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
-
-
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -151,12 +145,35 @@ def _idx(name: str, t: Optional[torch.Tensor], shape=None, optional=False):
     return t
 
 
+def _tensors(obj):
+    if isinstance(obj, torch.Tensor):
+        yield obj
+    elif isinstance(obj, dict):
+        for v in obj.values():
+            yield from _tensors(v)
+    elif isinstance(obj, (list, tuple)):
+        for v in obj:
+            yield from _tensors(v)
+
+
 def _prepared(name: str, fn, args: tuple, keep: tuple):
     """A launcher for one checked, marshalled call: ``launch(stream=None)``.
-    ``keep`` holds the tensors whose pointers are baked into ``args``."""
+    ``keep`` holds the tensors whose pointers are baked into ``args``; they
+    must all live on one GPU, and the call runs on that GPU's current stream
+    (or on ``stream``, which must belong to it)."""
+    devices = {t.device.index for t in _tensors(keep)}
+    if len(devices) > 1:
+        raise ValueError(f"{name}: tensors on several GPUs {sorted(devices)}")
+    dev = devices.pop() if devices else torch.cuda.current_device()
 
     def launch(stream=None, _keep=keep):
-        rc = fn(*args, _stream(stream))
+        s = torch.cuda.current_stream(dev) if stream is None else stream
+        # the null stream runs on the current device, any other on its own
+        on = torch.cuda.current_device() if s.cuda_stream == 0 else s.device.index
+        if on != dev:
+            raise ValueError(f"{name}: the tensors are on cuda:{dev}, the stream runs on "
+                             f"cuda:{on}")
+        rc = fn(*args, s.cuda_stream)
         if rc != OK:
             raise PagedKVError(name, rc)
 
@@ -607,19 +624,17 @@ def hash_blocks(tokens, starts, lengths, block_size, *, hashes, num_full=None, s
     if hashes.dim() != 2 or hashes.shape[0] != m:
         raise ValueError("hashes must be [m, MB]")
     _idx("num_full", num_full, (m,), optional=True)
-    rc = _lib.pkv_hash_blocks(m, _ptr(tokens), tokens.numel(), _ptr(starts), _ptr(lengths),
-                              int(block_size), hashes.shape[1], _ptr(hashes), _ptr(num_full),
-                              _ptr(_status(status)), _stream(stream))
-    if rc != OK:
-        raise PagedKVError("hash_blocks", rc)
+    args = (m, _ptr(tokens), tokens.numel(), _ptr(starts), _ptr(lengths), int(block_size),
+            hashes.shape[1], _ptr(hashes), _ptr(num_full), _ptr(_status(status)))
+    _prepared("hash_blocks", _lib.pkv_hash_blocks, args,
+              (tokens, starts, lengths, hashes, num_full, status))(stream)
 
 
 def prefix_clear(keys, vals, *, stream=None) -> None:
     """Empty the prefix index (pkv_prefix_clear)."""
     cap = _index(keys, vals)
-    rc = _lib.pkv_prefix_clear(_ptr(keys), _ptr(vals), cap, _stream(stream))
-    if rc != OK:
-        raise PagedKVError("prefix_clear", rc)
+    args = (_ptr(keys), _ptr(vals), cap)
+    _prepared("prefix_clear", _lib.pkv_prefix_clear, args, (keys, vals))(stream)
 
 
 def prefix_lookup(hashes, lengths, block_size, keys, vals, *, num_computed, hit_blocks=None,
@@ -634,11 +649,10 @@ def prefix_lookup(hashes, lengths, block_size, keys, vals, *, num_computed, hit_
     _idx("num_computed", num_computed, (m,))
     _idx("hit_blocks", hit_blocks, (m, MB), optional=True)
     cap = _index(keys, vals)
-    rc = _lib.pkv_prefix_lookup(m, _ptr(hashes), MB, _ptr(lengths), int(block_size), _ptr(keys),
-                                _ptr(vals), cap, _ptr(hit_blocks), _ptr(num_computed),
-                                _ptr(_status(status)), _stream(stream))
-    if rc != OK:
-        raise PagedKVError("prefix_lookup", rc)
+    args = (m, _ptr(hashes), MB, _ptr(lengths), int(block_size), _ptr(keys), _ptr(vals), cap,
+            _ptr(hit_blocks), _ptr(num_computed), _ptr(_status(status)))
+    _prepared("prefix_lookup", _lib.pkv_prefix_lookup, args,
+              (hashes, lengths, keys, vals, hit_blocks, num_computed, status))(stream)
 
 
 def prefix_insert(hashes, lo, hi, rows, block_table, keys, vals, *, status=None,
@@ -655,11 +669,10 @@ def prefix_insert(hashes, lo, hi, rows, block_table, keys, vals, *, status=None,
     if block_table.dim() != 2 or block_table.shape[1] != MB:
         raise ValueError("block_table must be [R, MB] with the hashes' MB")
     cap = _index(keys, vals)
-    rc = _lib.pkv_prefix_insert(m, _ptr(hashes), MB, _ptr(lo), _ptr(hi), _ptr(rows),
-                                _ptr(block_table), block_table.shape[0], _ptr(keys), _ptr(vals),
-                                cap, _ptr(_status(status)), _stream(stream))
-    if rc != OK:
-        raise PagedKVError("prefix_insert", rc)
+    args = (m, _ptr(hashes), MB, _ptr(lo), _ptr(hi), _ptr(rows), _ptr(block_table),
+            block_table.shape[0], _ptr(keys), _ptr(vals), cap, _ptr(_status(status)))
+    _prepared("prefix_insert", _lib.pkv_prefix_insert, args,
+              (hashes, lo, hi, rows, block_table, keys, vals, status))(stream)
 
 
 def prefix_evict(hashes, blocks, keys, vals, *, stream=None) -> None:
@@ -670,10 +683,8 @@ def prefix_evict(hashes, blocks, keys, vals, *, stream=None) -> None:
     if blocks.numel() != count:
         raise ValueError("hashes and blocks must have the same length")
     cap = _index(keys, vals)
-    rc = _lib.pkv_prefix_evict(count, _ptr(hashes), _ptr(blocks), _ptr(keys), _ptr(vals), cap,
-                               _stream(stream))
-    if rc != OK:
-        raise PagedKVError("prefix_evict", rc)
+    args = (count, _ptr(hashes), _ptr(blocks), _ptr(keys), _ptr(vals), cap)
+    _prepared("prefix_evict", _lib.pkv_prefix_evict, args, (hashes, blocks, keys, vals))(stream)
 
 
 # -- allocation-side variants: sliding-window holes, speculative lookahead ------
@@ -693,11 +704,10 @@ def window_free(rows, completed, block_table, block_size, sliding_window, *, fre
     MB = block_table.shape[1]
     _idx("freed", freed, (m, MB))
     _idx("num_freed", num_freed, (m,))
-    rc = _lib.pkv_window_free(m, _ptr(rows), _ptr(completed), _ptr(block_table), R, MB,
-                              int(block_size), int(sliding_window), _ptr(freed), _ptr(num_freed),
-                              _ptr(_status(status)), _stream(stream))
-    if rc != OK:
-        raise PagedKVError("window_free", rc)
+    args = (m, _ptr(rows), _ptr(completed), _ptr(block_table), R, MB, int(block_size),
+            int(sliding_window), _ptr(freed), _ptr(num_freed), _ptr(_status(status)))
+    _prepared("window_free", _lib.pkv_window_free, args,
+              (rows, completed, block_table, freed, num_freed, status))(stream)
 
 
 def lookahead_slots(index_mapping, seq_lens, block_table, block_size, num_blocks, *, out,
@@ -714,11 +724,10 @@ def lookahead_slots(index_mapping, seq_lens, block_table, block_size, num_blocks
     _idx("out", out)
     if out.dim() != 2 or out.shape[0] != n:
         raise ValueError("out must be [n, k]")
-    rc = _lib.pkv_lookahead_slots(n, _ptr(index_mapping), _ptr(seq_lens), _ptr(block_table), R,
-                                  MB, int(block_size), int(num_blocks), out.shape[1], _ptr(out),
-                                  _ptr(_status(status)), _stream(stream))
-    if rc != OK:
-        raise PagedKVError("lookahead_slots", rc)
+    args = (n, _ptr(index_mapping), _ptr(seq_lens), _ptr(block_table), R, MB, int(block_size),
+            int(num_blocks), out.shape[1], _ptr(out), _ptr(_status(status)))
+    _prepared("lookahead_slots", _lib.pkv_lookahead_slots, args,
+              (index_mapping, seq_lens, block_table, out, status))(stream)
 
 
 def blocks_needed(rows, num_new, k, block_size, completed, row_blocks, *, need, status=None,
@@ -732,8 +741,7 @@ def blocks_needed(rows, num_new, k, block_size, completed, row_blocks, *, need, 
     R = completed.shape[0]
     _idx("row_blocks", row_blocks, (R,))
     _idx("need", need, (n,))
-    rc = _lib.pkv_blocks_needed(n, _ptr(rows), _ptr(num_new), int(k), int(block_size),
-                                _ptr(completed), _ptr(row_blocks), R, _ptr(need),
-                                _ptr(_status(status)), _stream(stream))
-    if rc != OK:
-        raise PagedKVError("blocks_needed", rc)
+    args = (n, _ptr(rows), _ptr(num_new), int(k), int(block_size), _ptr(completed),
+            _ptr(row_blocks), R, _ptr(need), _ptr(_status(status)))
+    _prepared("blocks_needed", _lib.pkv_blocks_needed, args,
+              (rows, num_new, completed, row_blocks, need, status))(stream)
