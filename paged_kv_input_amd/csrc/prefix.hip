@@ -31,9 +31,15 @@ namespace {
 constexpr uint64_t kFnvBasis = 14695981039346656037ull;
 constexpr uint64_t kFnvPrime = 1099511628211ull;
 constexpr int32_t kNoBlock = INT32_MAX;
+// One workgroup per request.  Hashing is bound by the byte-serial FNV
+// multiplies, so 256 threads; the index probes are bound by memory latency, so
+// 1024 threads take the longest request's blocks in fewer rounds (measured on
+// MI355X, 512 requests of up to 1056 blocks: lookup 16 -> 12 us, insert
+// 19.6 -> 16.6 us; 1024-thread hashing was slower).
 constexpr int kHashThreads = 256;
-constexpr int kLookupThreads = 256;
-constexpr int kInsertThreads = 256;
+constexpr int kLookupThreads = 1024;
+constexpr int kInsertThreads = 1024;
+constexpr int kFlatThreads = 256;         // flat grids: eviction, clearing
 
 __device__ inline uint64_t fnv_byte(uint64_t h, uint32_t byte)
 {
@@ -251,11 +257,11 @@ __global__ __launch_bounds__(kInsertThreads) void k_prefix_insert(
     report_status(status, flags);
 }
 
-__global__ __launch_bounds__(kInsertThreads) void k_prefix_evict(
+__global__ __launch_bounds__(kFlatThreads) void k_prefix_evict(
     int32_t count, const uint64_t* __restrict__ hashes, const int32_t* __restrict__ blocks,
     const uint64_t* __restrict__ keys, int32_t* __restrict__ vals, int64_t capacity)
 {
-    const int64_t i = (int64_t)blockIdx.x * kInsertThreads + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * kFlatThreads + threadIdx.x;
     if (i >= count)
         return;
     const uint64_t key = hashes[i];
@@ -264,12 +270,12 @@ __global__ __launch_bounds__(kInsertThreads) void k_prefix_evict(
         atomicCAS(&vals[at], blocks[i], kNoBlock);
 }
 
-__global__ __launch_bounds__(kInsertThreads) void k_prefix_clear(uint64_t* __restrict__ keys,
+__global__ __launch_bounds__(kFlatThreads) void k_prefix_clear(uint64_t* __restrict__ keys,
                                                                  int32_t* __restrict__ vals,
                                                                  int64_t capacity)
 {
-    const int64_t stride = (int64_t)gridDim.x * kInsertThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kInsertThreads + threadIdx.x; i < capacity; i += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kFlatThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kFlatThreads + threadIdx.x; i < capacity; i += stride) {
         keys[i] = 0;
         vals[i] = kNoBlock;
     }
@@ -320,8 +326,8 @@ hipError_t launch_prefix_evict(int32_t count, const uint64_t* hashes, const int3
 {
     if (count == 0)
         return hipSuccess;
-    const unsigned grid = (unsigned)(((int64_t)count + kInsertThreads - 1) / kInsertThreads);
-    k_prefix_evict<<<dim3(grid), dim3(kInsertThreads), 0, stream>>>(count, hashes, blocks, keys,
+    const unsigned grid = (unsigned)(((int64_t)count + kFlatThreads - 1) / kFlatThreads);
+    k_prefix_evict<<<dim3(grid), dim3(kFlatThreads), 0, stream>>>(count, hashes, blocks, keys,
                                                                    vals, capacity);
     return hipGetLastError();
 }
@@ -330,9 +336,9 @@ hipError_t launch_prefix_clear(uint64_t* keys, int32_t* vals, int64_t capacity, 
 {
     if (capacity == 0)
         return hipSuccess;
-    const int64_t want = (capacity + kInsertThreads - 1) / kInsertThreads;
+    const int64_t want = (capacity + kFlatThreads - 1) / kFlatThreads;
     const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
-    k_prefix_clear<<<dim3(grid), dim3(kInsertThreads), 0, stream>>>(keys, vals, capacity);
+    k_prefix_clear<<<dim3(grid), dim3(kFlatThreads), 0, stream>>>(keys, vals, capacity);
     return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ namespace pkv {
 namespace {
 
 constexpr int kAddThreads = 256;
-constexpr int kAddUnroll = 4;
+constexpr int kAddUnroll = 16;         // 16 KiB of prompt per round trip
 constexpr int kAppendThreads = 256;
 constexpr int kAppendRows = kAppendThreads / kWave;
 constexpr int kAdvanceThreads = 256;
