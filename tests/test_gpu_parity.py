@@ -219,6 +219,35 @@ def test_fused_batch_sizes(n):
     run_and_compare(b, mode="fused")
 
 
+@pytest.mark.parametrize("wide", [False, True])
+def test_fused_many_state_rows(wide):
+    """100 requests among 2^20 state rows (rows 0 and 2^20 - 1 included), counts
+    up to 30, and with one count of 31: the fused step against the oracle."""
+    rng = np.random.default_rng(4242 + wide)
+    n, R, L, bs = 100, 1 << 20, 64, 16
+    rows = rng.choice(R - 2, n, replace=False).astype(np.int32) + 1
+    rows[3], rows[50] = 0, R - 1
+    counts = rng.integers(1, 31, n).astype(np.int32)
+    counts[rng.random(n) < 0.3] = 1
+    if wide:
+        counts[17] = 31
+    completed = np.zeros(R, np.int32)
+    completed[rows] = rng.integers(0, L - 31, n)
+    MB = L // bs
+    need = int(sum(max(0, -(-(int(completed[r]) + int(c)) // bs) - int(completed[r]) // bs)
+                   for r, c in zip(rows, counts)))
+    NB = need + 5
+    bt = workloads._block_table(rng, R, MB, NB, bs, rows, counts, completed)
+    T = int(counts.sum())
+    k = rng.integers(0, 65535, (T, 1, 64), dtype=np.uint16)
+    v = rng.integers(0, 65535, (T, 1, 64), dtype=np.uint16)
+    tok = np.zeros((R, L), np.int32)
+    tok[rows] = rng.integers(0, 1 << 20, (n, L), dtype=np.int32)
+    b = workloads.Batch(f"rows2e20_{int(wide)}", 4242 + wide, rows, counts,
+                        completed, tok, [workloads.KVGroup(bs, NB, MB, bt, 1, 64, "fp16", k, v)])
+    run_and_compare(b, mode="fused")
+
+
 @pytest.mark.parametrize("groups", [4, 5, 7])
 def test_fused_group_counts(groups):
     """pkv_step with up to the kernel's group limit in one launch, and past it
