@@ -523,12 +523,15 @@ __device__ inline void wave_gather(WaveBatchLds<kMaxN>& w, WaveGather<kMaxN>& gt
 
 // Bitonic sort of 64 < n <= kThreads * 2 keys with their original indices by
 // every wavefront of the workgroup (call from every thread): one element per
-// lane up to kThreads keys, else two.  w.xkey / w.xidx serve as the second
-// exchange buffer.
+// lane up to kThreads keys (a network of kThreads / 2 positions when that
+// holds them: 28 passes instead of 36), else two.  w.xkey / w.xidx serve as
+// the second exchange buffer.
 template <int kThreads, int kMaxN>
 __device__ __forceinline__ void block_sort(WaveBatchLds<kMaxN>& w, int32_t n)
 {
-    if (n <= kThreads)
+    if (n <= kThreads / 2)
+        bitonic_regs<kThreads, 1, kThreads / 2, true, true>(w.b.key, w.idx, w.xkey, w.xidx, n);
+    else if (n <= kThreads)
         bitonic_regs<kThreads, 1, kThreads, true, true>(w.b.key, w.idx, w.xkey, w.xidx, n);
     else
         bitonic_regs<kThreads, 2, 2 * kThreads, true, true>(w.b.key, w.idx, w.xkey, w.xidx, n);
