@@ -33,6 +33,22 @@ def build(out: str = LIB, extra=()) -> str:
     return out
 
 
+C_CALLER = os.path.join(ROOT, "tests", "c_caller", "pages_example")
+
+
+def build_c_caller(out: str = C_CALLER) -> str:
+    """Compile the test suite's C-ABI caller (host code only, no kernels): it
+    links libpagedkv.so and the HIP runtime, nothing from Python or torch."""
+    lib_dir = os.path.dirname(LIB)
+    rpath = os.path.relpath(lib_dir, os.path.dirname(out))
+    cmd = [HIPCC, "-O2", "-std=c++17", "-Wall", "-Wextra", "-Werror", f"-I{INCLUDE}",
+           out + ".cpp", f"-L{lib_dir}", "-lpagedkv", f"-Wl,-rpath,$ORIGIN/{rpath}",
+           "-o", out + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def sources_newer_than(lib: str = LIB) -> bool:
     if not os.path.exists(lib):
         return True
