@@ -27,7 +27,11 @@
  *   pkv_add_requests, pkv_append_blocks, pkv_advance_state, pkv_row_pool_*
  *                            -- the persistent request state the path reads
  *                               ("Persistent Request Context Strategy", "Design
- *                               Logic Behind the Dual-Index System").
+ *                               Logic Behind the Dual-Index System");
+ *   pkv_window_free, pkv_lookahead_slots, pkv_blocks_needed, and the
+ *   sliding_window arguments -- sliding-window groups and speculative
+ *                               lookahead ("Scheduler.schedule()" and
+ *                               "allocate_slots()" of the caffein.top article).
  *
  * Conventions shared by every call
  *   - Pointers named as device pointers must point to device memory (HBM) that
