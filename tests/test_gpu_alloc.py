@@ -226,7 +226,7 @@ def test_sliding_window_serving_loop():
     lookahead_slots and advance_state; the oracle runs the same loop."""
     import torch
     from paged_kv_input_amd import RowPool, api
-    from paged_kv_input_amd.state import DeviceState, pack_csr
+    from paged_kv_input_amd.state import DeviceState
     from paged_kv_input_amd.step import DeviceStep, GroupSpec
 
     rng = np.random.default_rng(808)
