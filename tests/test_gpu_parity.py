@@ -219,6 +219,43 @@ def test_fused_batch_sizes(n):
     run_and_compare(b, mode="fused")
 
 
+def _random_batch(seed):
+    """A seeded random step across the batch-size regimes of the fused step
+    (1-64, 65-128, 129-256 and 257-512 requests): counts with many ties and
+    some zeros, 1-3 groups with block sizes from 1 to 64 (3 included), rows of
+    16 B to 2 KiB."""
+    rng = np.random.default_rng(seed)
+    lo, hi = [(1, 65), (65, 129), (129, 257), (257, 513)][seed % 4]
+    n = int(rng.integers(lo, hi))
+    R = n + int(rng.integers(0, 2 * n + 1))
+    rows = rng.choice(R, n, replace=False).astype(np.int32)
+    base = rng.choice([1, 2, 3, 7, 16])
+    counts = np.where(rng.random(n) < 0.5, base, rng.integers(0, 24, n)).astype(np.int32)
+    L = 64 + 24
+    completed = np.zeros(R, np.int32)
+    completed[rows] = rng.integers(0, 64, n)
+    T = int(counts.sum())
+    groups = []
+    for _ in range(int(rng.integers(1, 4))):
+        bs = int(rng.choice([1, 3, 4, 8, 16, 32, 64]))
+        MB = -(-L // bs)
+        need = int(sum(max(0, -(-(int(completed[r]) + int(c)) // bs) - int(completed[r]) // bs)
+                       for r, c in zip(rows, counts)))
+        NB = need + int(rng.integers(1, 64))
+        bt = workloads._block_table(rng, R, MB, NB, bs, rows, counts, completed)
+        H, D = [(1, 8), (2, 64), (8, 128), (4, 32)][int(rng.integers(0, 4))]
+        k = rng.integers(0, 65535, (T, H, D), dtype=np.uint16)
+        v = rng.integers(0, 65535, (T, H, D), dtype=np.uint16)
+        groups.append(workloads.KVGroup(bs, NB, MB, bt, H, D, "fp16", k, v))
+    tok = rng.integers(0, 1 << 20, (R, L), dtype=np.int32)
+    return workloads.Batch(f"sweep_{seed}", seed, rows, counts, completed, tok, groups)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_fused_random_sweep(seed):
+    run_and_compare(_random_batch(1000 + seed), mode="fused")
+
+
 @pytest.mark.parametrize("wide", [False, True])
 def test_fused_many_state_rows(wide):
     """100 requests among 2^20 state rows (rows 0 and 2^20 - 1 included), counts
