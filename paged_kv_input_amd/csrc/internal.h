@@ -12,22 +12,32 @@ namespace pkv {
 
 constexpr int kWave = 64;
 
-// Inclusive prefix sum across the 64 lanes of a wavefront (Hillis-Steele over
-// __shfl_up; the 64-bit value moves as two 32-bit halves).
+// One DPP move of a 64-bit value (its two 32-bit halves from the same source
+// lane); lanes without a source, or in rows outside kRowMask, get 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp64(uint64_t x)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, kCtrl,
+                                                              kRowMask, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), kCtrl,
+                                                              kRowMask, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wavefront.
 __device__ inline int64_t wave_inclusive_scan(int64_t x)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        uint32_t lo = (uint32_t)(uint64_t)x;
-        uint32_t hi = (uint32_t)((uint64_t)x >> 32);
-        lo = __shfl_up(lo, d, kWave);
-        hi = __shfl_up(hi, d, kWave);
-        int64_t y = (int64_t)(((uint64_t)hi << 32) | lo);
-        if (lane >= d)
-            x += y;
-    }
-    return x;
+    // Hillis-Steele steps inside each 16-lane row by row shifts of 1, 2, 4 and
+    // 8 lanes, then the row totals carried on by row broadcasts: lane 15 into
+    // rows 1 and 3, then lane 31 into rows 2 and 3.  All in registers.
+    uint64_t v = (uint64_t)x;
+    v += dpp64<0x111, 0xF>(v);      // row_shr:1
+    v += dpp64<0x112, 0xF>(v);      // row_shr:2
+    v += dpp64<0x114, 0xF>(v);      // row_shr:4
+    v += dpp64<0x118, 0xF>(v);      // row_shr:8
+    v += dpp64<0x142, 0xA>(v);      // row_bcast:15
+    v += dpp64<0x143, 0xC>(v);      // row_bcast:31
+    return (int64_t)v;
 }
 
 // OR a lane's status flags into the caller's word: one atomic per wave that
