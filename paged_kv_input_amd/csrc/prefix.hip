@@ -111,7 +111,18 @@ __global__ __launch_bounds__(kHashThreads) void k_hash_blocks(
         // Content hash of block i (lanes past the last block hash block i0).
         const int32_t* blk = tokens + start + (i < full ? i : i0) * block_size;
         uint64_t c = kFnvBasis;
-        for (int32_t j = 0; j < block_size; ++j)
+        // Eight token loads in flight per wait, then their bytes in order.
+        int32_t j = 0;
+        for (; j + 8 <= block_size; j += 8) {
+            uint32_t t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                t[u] = (uint32_t)blk[j + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                c = fnv_word(c, t[u]);
+        }
+        for (; j < block_size; ++j)
             c = fnv_word(c, (uint32_t)blk[j]);
         // Compose the chunk's maps x -> x * P + c_i.
         uint64_t a = kFnvPrime, add = c;
