@@ -18,8 +18,8 @@ per-call split of the three calls, the host wall time of one step with the
 schedule uploaded from pinned host memory, a single-step cold measurement (a
 1 GiB rewrite before each step, events around it; median, p10, p90), ceilings to
 read the step against (a same-byte device copy, the dispatch floor), and the
-calls around the path: the state updates, the paged K/V read and the
-prefix-cache calls.
+calls around the path: the state updates, the paged K/V read, the
+prefix-cache calls and the sliding-window and lookahead variants.
 
 Prints one JSON line (N = 1 only: this build runs on one GPU).
 """
@@ -270,6 +270,87 @@ def state_calls(batch, step, steps, warmup, stream):
         raise RuntimeError(f"state status bits set: {ds.status_bits():#x}")
     out["note"] = (f"{n} requests; add_requests registers {ptot} prompt tokens and {btot} "
                    f"blocks into a {MB}-wide table; append_blocks adds 1 block per request")
+    return out
+
+
+def variant_calls(batch, step, steps, warmup, stream, window=1024, k=4):
+    """The allocation-side variants on this batch's shape (group 0): the slots
+    of k speculative lookahead positions after every request's seq_len, the
+    new blocks each request needs for its new and k lookahead tokens (both
+    timed back to back), and the blocks a sliding window of `window` tokens no
+    longer needs.  window_free changes the table, so each of its calls runs
+    on a fresh copy (restored untimed) with HIP events around the call alone;
+    its figure is the median.  Bytes count each required read or write once."""
+    import numpy as np
+    import torch
+
+    from paged_kv_input_amd import api
+
+    g, gd = batch.groups[0], step.groups[0]
+    dev = step.completed.device
+    n, bs, MB = batch.n, g.block_size, g.max_blocks
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    rows_d = up(batch.sched_rows)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)     # expected: unallocated lookahead
+    look_out = torch.empty((n, k), dtype=torch.int32, device=dev)
+    look = api.prepared_lookahead_slots(step.index_mapping, step.seq_lens, gd["block_table"], bs,
+                                        g.num_blocks, out=look_out, status=flags)
+    row_blocks = up((g.block_table >= 0).sum(axis=1))
+    need = torch.empty(n, dtype=torch.int32, device=dev)
+    needed = api.prepared_blocks_needed(rows_d, step.num_scheduled, k, bs, step.completed,
+                                        row_blocks, need=need, status=flags)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn(stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    out = {}
+    for name, fn, nbytes in (("lookahead_slots", look, 8 * n + 8 * n * k),
+                             ("blocks_needed", needed, 20 * n)):
+        ms = timed(fn)
+        out[name] = {"ms": ms, "algorithmic_bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "bound": "latency"}
+
+    done = batch.completed[batch.sched_rows].astype(np.int64)
+    scan = np.minimum(np.maximum(done - window + 1, 0) // bs, MB)
+    freed_n = sum(int((g.block_table[r, :c] >= 0).sum()) for r, c in zip(batch.sched_rows, scan))
+    base = gd["block_table"].clone()
+    work = base.clone()
+    freed = torch.empty((n, MB), dtype=torch.int32, device=dev)
+    num_freed = torch.empty(n, dtype=torch.int32, device=dev)
+    wf = api.prepared_window_free(rows_d, step.completed, work, bs, window, freed=freed,
+                                  num_freed=num_freed, status=flags)
+    times = []
+    for i in range(warmup + min(steps, 100)):
+        work.copy_(base)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        wf(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            times.append(e0.elapsed_time(e1))
+    if int(num_freed.sum().item()) != freed_n:
+        raise RuntimeError("window_free released an unexpected number of blocks")
+    ms = statistics.median(times)
+    nbytes = 12 * n + 4 * int(scan.sum()) + 8 * freed_n
+    out["window_free"] = {"ms": ms, "algorithmic_bytes": nbytes,
+                          "gbs": nbytes / (ms * 1e-3) / 1e9, "bound": "latency",
+                          "blocks_freed": freed_n,
+                          "timing": "events around single calls (median), table restored untimed"}
+    out["note"] = (f"{n} requests, group 0 (block size {bs}); {k} lookahead positions; "
+                   f"a {window}-token window")
     return out
 
 
@@ -608,6 +689,7 @@ def main():
         if s.status_bits() != 0:
             raise RuntimeError(f"device status bits set: {s.status_bits():#x}")
     state = state_calls(batch, steps[0], args.steps, args.warmup, stream)
+    variants = variant_calls(batch, steps[0], args.steps, args.warmup, stream)
     gather = gather_calls(batch, steps, args.steps, args.warmup, stream, args.workload)
     prefix = prefix_calls(batch, steps[0], args.steps, args.warmup, stream)
 
@@ -668,6 +750,7 @@ def main():
         },
         "context": context,
         "state_calls": state,
+        "variant_calls": variants,
         "gather_kv": gather,
         "prefix_cache": prefix,
         "hip_graph_replay": {

@@ -690,10 +690,17 @@ def prefix_evict(hashes, blocks, keys, vals, *, stream=None) -> None:
 # -- allocation-side variants: sliding-window holes, speculative lookahead ------
 def window_free(rows, completed, block_table, block_size, sliding_window, *, freed, num_freed,
                 status=None, stream=None) -> None:
-    """Release the blocks wholly before every window (pkv_window_free):
-    block_table [R, MB] is updated in place (freed entries become -1), freed
-    [m, MB] lists each row's released ids in block order, num_freed [m] counts
-    them."""
+    """Release the blocks wholly before every window (pkv_window_free); see
+    prepared_window_free."""
+    prepared_window_free(rows, completed, block_table, block_size, sliding_window, freed=freed,
+                         num_freed=num_freed, status=status)(stream)
+
+
+def prepared_window_free(rows, completed, block_table, block_size, sliding_window, *, freed,
+                         num_freed, status=None):
+    """Release the blocks wholly before every window: block_table [R, MB] is
+    updated in place (freed entries become -1), freed [m, MB] lists each row's
+    released ids in block order, num_freed [m] counts them."""
     m = rows.shape[0]
     _idx("rows", rows, (m,))
     _idx("completed", completed)
@@ -706,14 +713,21 @@ def window_free(rows, completed, block_table, block_size, sliding_window, *, fre
     _idx("num_freed", num_freed, (m,))
     args = (m, _ptr(rows), _ptr(completed), _ptr(block_table), R, MB, int(block_size),
             int(sliding_window), _ptr(freed), _ptr(num_freed), _ptr(_status(status)))
-    _prepared("window_free", _lib.pkv_window_free, args,
-              (rows, completed, block_table, freed, num_freed, status))(stream)
+    return _prepared("window_free", _lib.pkv_window_free, args,
+                     (rows, completed, block_table, freed, num_freed, status))
 
 
 def lookahead_slots(index_mapping, seq_lens, block_table, block_size, num_blocks, *, out,
                     status=None, stream=None) -> None:
-    """Slots of the k = out.shape[1] positions after each request's seq_len
-    (pkv_lookahead_slots)."""
+    """Slots of the positions after each request's seq_len (pkv_lookahead_slots);
+    see prepared_lookahead_slots."""
+    prepared_lookahead_slots(index_mapping, seq_lens, block_table, block_size, num_blocks,
+                             out=out, status=status)(stream)
+
+
+def prepared_lookahead_slots(index_mapping, seq_lens, block_table, block_size, num_blocks, *, out,
+                             status=None):
+    """Slots of the k = out.shape[1] positions after each request's seq_len."""
     n = index_mapping.shape[0]
     _idx("index_mapping", index_mapping, (n,))
     _idx("seq_lens", seq_lens, (n,))
@@ -726,14 +740,20 @@ def lookahead_slots(index_mapping, seq_lens, block_table, block_size, num_blocks
         raise ValueError("out must be [n, k]")
     args = (n, _ptr(index_mapping), _ptr(seq_lens), _ptr(block_table), R, MB, int(block_size),
             int(num_blocks), out.shape[1], _ptr(out), _ptr(_status(status)))
-    _prepared("lookahead_slots", _lib.pkv_lookahead_slots, args,
-              (index_mapping, seq_lens, block_table, out, status))(stream)
+    return _prepared("lookahead_slots", _lib.pkv_lookahead_slots, args,
+                     (index_mapping, seq_lens, block_table, out, status))
 
 
 def blocks_needed(rows, num_new, k, block_size, completed, row_blocks, *, need, status=None,
                   stream=None) -> None:
-    """New blocks each request needs for its new and k lookahead tokens
-    (pkv_blocks_needed)."""
+    """New blocks each request needs (pkv_blocks_needed); see prepared_blocks_needed."""
+    prepared_blocks_needed(rows, num_new, k, block_size, completed, row_blocks, need=need,
+                           status=status)(stream)
+
+
+def prepared_blocks_needed(rows, num_new, k, block_size, completed, row_blocks, *, need,
+                           status=None):
+    """New blocks each request needs for its new and k lookahead tokens."""
     n = rows.shape[0]
     _idx("rows", rows, (n,))
     _idx("num_new", num_new, (n,))
@@ -743,5 +763,5 @@ def blocks_needed(rows, num_new, k, block_size, completed, row_blocks, *, need, 
     _idx("need", need, (n,))
     args = (n, _ptr(rows), _ptr(num_new), int(k), int(block_size), _ptr(completed),
             _ptr(row_blocks), R, _ptr(need), _ptr(_status(status)))
-    _prepared("blocks_needed", _lib.pkv_blocks_needed, args,
-              (rows, num_new, completed, row_blocks, need, status))(stream)
+    return _prepared("blocks_needed", _lib.pkv_blocks_needed, args,
+                     (rows, num_new, completed, row_blocks, need, status))

@@ -21,6 +21,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = kThreads / kWave;
+constexpr int kFreeRounds = 4;
 
 __global__ __launch_bounds__(kThreads) void k_window_free(
     int32_t m, const int32_t* __restrict__ rows, const int32_t* __restrict__ completed,
@@ -44,16 +45,26 @@ __global__ __launch_bounds__(kThreads) void k_window_free(
             int32_t* row = block_table + (int64_t)r * MB;
             int32_t* out = freed + (int64_t)b * MB;
             const uint64_t below = (1ull << lane) - 1;
-            for (int64_t i0 = 0; i0 < blocks; i0 += kWave) {
-                const int64_t i = i0 + lane;
-                const int32_t entry = i < blocks ? row[i] : -1;
-                const bool take = entry >= 0;
-                const uint64_t mask = __ballot(take);
-                if (take) {
-                    out[count + __popcll(mask & below)] = entry;
-                    row[i] = -1;
+            // Four rounds of 64 entries loaded per wait (unconditional loads
+            // from clamped in-bounds addresses), then compacted in order.
+            for (int64_t i0 = 0; i0 < blocks; i0 += kFreeRounds * kWave) {
+                int32_t entry[kFreeRounds];
+#pragma unroll
+                for (int u = 0; u < kFreeRounds; ++u) {
+                    const int64_t i = i0 + u * kWave + lane;
+                    entry[u] = row[i < blocks ? i : 0];
                 }
-                count += __popcll(mask);
+#pragma unroll
+                for (int u = 0; u < kFreeRounds; ++u) {
+                    const int64_t i = i0 + u * kWave + lane;
+                    const bool take = i < blocks && entry[u] >= 0;
+                    const uint64_t mask = __ballot(take);
+                    if (take) {
+                        out[count + __popcll(mask & below)] = entry[u];
+                        row[i] = -1;
+                    }
+                    count += __popcll(mask);
+                }
             }
         }
         if (lane == 0)
