@@ -238,8 +238,9 @@ int pkv_lookahead_slots(int32_t n, const int32_t* index_mapping, const int32_t* 
         return PKV_EINVAL;
     if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX + 1)
         return PKV_EINVAL;
-    if (n > 0 && k > 0 && (index_mapping == nullptr || seq_lens == nullptr ||
-                           lookahead_slots == nullptr || (R > 0 && MB > 0 && block_table == nullptr)))
+    if (n > 0 && k > 0 &&
+        (index_mapping == nullptr || seq_lens == nullptr || lookahead_slots == nullptr ||
+         (R > 0 && MB > 0 && block_table == nullptr)))
         return PKV_EINVAL;
     return from_hip(pkv::launch_lookahead_slots(n, index_mapping, seq_lens, block_table, R, MB,
                                                 block_size, num_blocks, k, lookahead_slots, status,
@@ -282,7 +283,8 @@ int pkv_prefix_clear(uint64_t* keys, int32_t* vals, int64_t capacity, void* stre
 {
     if (bad_capacity(capacity) || (capacity > 0 && (keys == nullptr || vals == nullptr)))
         return PKV_EINVAL;
-    return from_hip(pkv::launch_prefix_clear(keys, vals, capacity, static_cast<hipStream_t>(stream)));
+    return from_hip(
+        pkv::launch_prefix_clear(keys, vals, capacity, static_cast<hipStream_t>(stream)));
 }
 
 int pkv_prefix_lookup(int32_t m, const uint64_t* hashes, int32_t MB, const int32_t* lengths,

@@ -21,12 +21,13 @@
 // one index wavefront split the work: the index wavefront resolves the rows of
 // the next tile of at most 256 rows (owner by binary search in LDS, page
 // lookup) while the copy wavefronts move the current tile.  Tiles are
-// shortened for short reads, so that even those spread over the whole chip.  Here the loads depend on the slots
-// and the stores do not: the copy wavefronts read whole 16-byte chunks of the
-// cache rows at the tile's slots (consecutive positions of a page are
-// consecutive slots, so a page is one contiguous span) and write the output
-// rows in order.  The index wavefront's page loads never queue behind the
-// payload, since a wavefront's memory counter only covers its own accesses.
+// shortened for short reads, so that even those spread over the whole chip.
+// Here the loads depend on the slots and the stores do not: the copy
+// wavefronts read whole 16-byte chunks of the cache rows at the tile's slots
+// (consecutive positions of a page are consecutive slots, so a page is one
+// contiguous span) and write the output rows in order.  The index wavefront's
+// page loads never queue behind the payload, since a wavefront's memory
+// counter only covers its own accesses.
 #include "internal.h"
 #include "launchers.h"
 
@@ -48,7 +49,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define PKV_GATHER_MIN_TILE 16
 #endif
 #ifndef PKV_GATHER_PIPE
-#define PKV_GATHER_PIPE 0                  // 1: next round's loads issued before this round's stores
+#define PKV_GATHER_PIPE 0     // 1: next round's loads issued before this round's stores
 #endif
 
 constexpr int kCopyWaves = 3;

@@ -24,7 +24,7 @@ namespace {
 
 constexpr int kPrepThreads = 1024;
 constexpr int kPrepTokensPerThread = 4;
-constexpr int kPrepTokensPerBlock = kPrepThreads * kPrepTokensPerThread;   // flat tokens per workgroup
+constexpr int kPrepTokensPerBlock = kPrepThreads * kPrepTokensPerThread;   // tokens per workgroup
 
 __global__ __launch_bounds__(kPrepThreads) void k_prepare(
     int32_t n, int32_t T, const int32_t* __restrict__ sched_rows,
@@ -37,9 +37,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
     __shared__ BatchLds<PKV_MAX_BATCH, kPrepThreads / kWave> lds;
     const bool leader = blockIdx.x == 0;
     uint32_t flags = 0;
-    order_batch<kPrepThreads, PKV_MAX_BATCH, false>(lds, n, T, sched_rows, num_scheduled, completed, R,
-                                             leader, index_mapping, query_start_loc, seq_lens,
-                                             flags);
+    order_batch<kPrepThreads, PKV_MAX_BATCH, false>(lds, n, T, sched_rows, num_scheduled,
+                                                    completed, R, leader, index_mapping,
+                                                    query_start_loc, seq_lens, flags);
     if (!leader)
         flags = 0;      // per-request flags come from workgroup 0 only
     const int32_t* s_row = lds.row();

@@ -167,7 +167,9 @@ hipError_t launch_slots(int32_t n, int32_t T, const int32_t* index_mapping,
 {
     const int64_t token_blocks = ((int64_t)T + kSlotTokensPerBlock - 1) / kSlotTokensPerBlock;
     const int64_t page_blocks =
-        input_block_tables != nullptr ? ((int64_t)n + kPageRowsPerBlock - 1) / kPageRowsPerBlock : 0;
+        input_block_tables != nullptr
+            ? ((int64_t)n + kPageRowsPerBlock - 1) / kPageRowsPerBlock
+            : 0;
     const int64_t blocks = token_blocks + page_blocks;
     if (blocks == 0)
         return hipSuccess;

@@ -9,14 +9,15 @@
 // Design (gfx950): the grid is the K/V copy.  Each workgroup owns a tile of
 // flat tokens of one group and has three copy wavefronts plus one index
 // wavefront, one per SIMD.  The copy wavefronts issue the tile's K/V loads at
-// once (24 KiB of each per round; they depend on nothing) and wait at a
+// once (18 KiB of each per round; they depend on nothing) and wait at a
 // single barrier.
-// Meanwhile the index wavefront orders the batch itself in LDS
-// (wave_gather / rank_sort_wave or block_sort / wave_finish: for at most 64
-// requests the index wavefront alone ranks every key by counting the keys
-// before it; for more, every wavefront joins a bitonic sort held in
-// registers, with three exchanges through LDS; then a wave-level scan), resolves the tile's tokens to requests by
-// binary search, and computes positions, input ids and slots.  After the
+// Meanwhile the index wavefront orders the batch itself (wave_gather /
+// rank_sort_wave or block_sort / wave_finish: for at most 64 requests the
+// index wavefront alone ranks every key by counting the keys before it, in
+// LDS; for more, every wavefront joins a bitonic sort held in registers, with
+// one to three exchanges through LDS; then a wave-level scan), resolves the
+// tile's tokens to requests by binary search, and computes positions, input
+// ids and slots.  After the
 // barrier the copy wavefronts write the held rows to their slots.  Splitting
 // the roles across wavefronts matters: a wavefront's loads complete in issue
 // order, so index loads issued behind the payload would wait for all of it.
@@ -506,8 +507,8 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
         g.rounds = (int32_t)((tile * cpr + kStepChunks - 1) / kStepChunks);
         g.first_block = (int32_t)blocks;
         g.tiles = (int32_t)(((int64_t)T + tile - 1) / tile);
-        g.tile_blocks = (int32_t)(g.tiles < tile_workgroups(num_groups) ? g.tiles
-                                                                         : tile_workgroups(num_groups));
+        const int64_t wgs = tile_workgroups(num_groups);
+        g.tile_blocks = (int32_t)(g.tiles < wgs ? g.tiles : wgs);
         g.page_blocks = in.input_block_tables != nullptr ? (n + kPageRows - 1) / kPageRows : 0;
         blocks += (int64_t)g.tile_blocks + g.page_blocks;
     }
