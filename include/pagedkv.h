@@ -80,8 +80,8 @@ extern "C" {
 #define PKV_ST_BAD_RANGE  0x80u /* CSR offsets decreasing or outside their array       */
 #define PKV_ST_TABLE_FULL 0x100u /* prefix index: no free slot for a new hash           */
 
-/* Largest batch (scheduled requests per step) one call accepts: the batch is
- * ordered inside one workgroup's LDS. */
+/* Largest batch (scheduled requests per step) one call accepts: every
+ * workgroup that orders the batch holds all of its keys in LDS. */
 #define PKV_MAX_BATCH 4096
 
 /*

@@ -291,25 +291,9 @@ __device__ __forceinline__ void bitonic_regs(uint64_t* key, int16_t* idx, uint64
     __syncthreads();
 }
 
-// Ascending sort of key[0 .. n) by bitonic_regs over the smallest network of
-// kPad = 64, 128, ... positions that holds n <= kMaxN keys (one key per lane up
-// to kThreads keys, then two or four).  Call from every thread.
-template <int kThreads, int kMaxN, int kPad = kWave>
-__device__ __forceinline__ void sort_keys(uint64_t* key, int32_t n)
-{
-    constexpr int kPer = kPad <= kThreads ? 1 : kPad / kThreads;
-    if constexpr (kPad >= kMaxN) {
-        bitonic_regs<kThreads, kPer, kPad, false, false>(key, nullptr, nullptr, nullptr, n);
-    } else {
-        if (n <= kPad)
-            bitonic_regs<kThreads, kPer, kPad, false, false>(key, nullptr, nullptr, nullptr, n);
-        else
-            sort_keys<kThreads, kMaxN, kPad * 2>(key, n);
-    }
-}
-
-// LDS working set of order_batch for up to kMaxN requests.  The keys are dead
-// once ordered, so the per-request rows and completed counts reuse them.
+// LDS working set of the batch ordering for up to kMaxN requests.  The keys
+// are dead once ordered, so the per-request rows and completed counts reuse
+// them.
 template <int kMaxN, int kWaves, bool kCounts = false>
 struct BatchLds {
     uint64_t key[kMaxN];
@@ -322,120 +306,6 @@ struct BatchLds {
     __device__ const int32_t* done() const { return reinterpret_cast<const int32_t*>(key) + kMaxN; }
 };
 
-// Batch assembly inside one workgroup ("Batch Construction and Sequence
-// Flattening" of the kongchang.com article): gather the n scheduled requests
-// as (count, row) keys, sort them ascending (bitonic_regs), prefix-sum the
-// sorted counts (wave-level scan plus one cross-wave pass, saturating at
-// INT32_MAX) and fetch each request's completed count.  On return, after a
-// barrier, lds.qsl[0..n], lds.row()[0..n) and lds.done()[0..n) describe the
-// batch in order (and lds.count[0..n) when kCounts).  A writer workgroup also
-// stores index_mapping, query_start_loc and seq_lens and collects BAD_ROW /
-// TOKEN_SUM; every caller gets BAD_COUNT for negative counts (read as 0).
-// n <= kMaxN.
-template <int kThreads, int kMaxN, bool kCounts>
-__device__ inline void order_batch(BatchLds<kMaxN, kThreads / kWave, kCounts>& lds, int32_t n,
-                                   int32_t T,
-                                   const int32_t* __restrict__ sched_rows,
-                                   const int32_t* __restrict__ num_scheduled,
-                                   const int32_t* __restrict__ completed, int32_t R, bool writer,
-                                   int32_t* __restrict__ index_mapping,
-                                   int32_t* __restrict__ query_start_loc,
-                                   int32_t* __restrict__ seq_lens, uint32_t& flags)
-{
-    constexpr int kWaves = kThreads / kWave;
-    constexpr int kPer = kMaxN / kThreads;       // batch rows per thread in the scan
-    static_assert(kMaxN % kThreads == 0, "batch rows split evenly over threads");
-    static_assert(kPer <= 4, "the sort holds at most four keys per lane");
-    const int tid = threadIdx.x;
-
-    for (int i = tid; i < n; i += kThreads) {
-        int32_t c = num_scheduled[i];
-        if (c < 0) {
-            flags |= PKV_ST_BAD_COUNT;
-            c = 0;
-        }
-        lds.key[i] = sort_key(c, sched_rows[i]);
-    }
-    sort_keys<kThreads, kMaxN>(lds.key, n);
-
-    // Each thread owns kPer consecutive batch rows.
-    uint64_t keys[kPer];
-    int64_t local = 0;
-    const int first = tid * kPer;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-        const int b = first + e;
-        keys[e] = b < n ? lds.key[b] : 0ull;
-        local += b < n ? key_count(keys[e]) : 0;
-    }
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int64_t incl = wave_inclusive_scan(local);
-    if (lane == kWave - 1)
-        lds.wave_total[wave] = incl;
-    __syncthreads();      // also: every key is in registers, lds.key may be reused
-    if (wave == 0) {
-        int64_t w = lane < kWaves ? lds.wave_total[lane] : 0;
-        w = wave_inclusive_scan(w);
-        if (lane < kWaves)
-            lds.wave_total[lane] = w;
-    }
-    __syncthreads();
-    int64_t run = (wave > 0 ? lds.wave_total[wave - 1] : 0) + incl - local;
-    const int64_t total = lds.wave_total[kWaves - 1];
-
-    int32_t* s_row = lds.row();
-    int32_t* s_done = lds.done();
-    // All of a thread's completed counts in one round trip: unconditional
-    // loads from a clamped in-bounds row (a load under a divergent branch is
-    // issued only after a full wait).
-    int32_t done_v[kPer];
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-        const int32_t row = key_row(keys[e]);
-        const bool ok = first + e < n && row >= 0 && row < R;
-        done_v[e] = R > 0 ? completed[ok ? row : 0] : 0;
-        if (!ok)
-            done_v[e] = 0;
-    }
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-        const int b = first + e;
-        if (b >= n)
-            break;
-        const int32_t c = key_count(keys[e]);
-        const int32_t row = key_row(keys[e]);
-        run += c;
-        const int32_t end = run > INT32_MAX ? INT32_MAX : (int32_t)run;
-        lds.qsl[b + 1] = end;
-        const bool row_ok = row >= 0 && row < R;
-        const int32_t done = done_v[e];
-        s_row[b] = row;
-        s_done[b] = done;
-        if (kCounts)
-            lds.count[b] = c;
-        if (writer) {
-            index_mapping[b] = row;
-            query_start_loc[b + 1] = end;
-            if (row_ok) {
-                seq_lens[b] = (int32_t)(uint32_t)(uint64_t)((int64_t)done + c);
-            } else {
-                seq_lens[b] = -1;
-                flags |= PKV_ST_BAD_ROW;
-            }
-        }
-    }
-    if (tid == 0) {
-        lds.qsl[0] = 0;
-        if (writer) {
-            query_start_loc[0] = 0;
-            if (total != (int64_t)T)
-                flags |= PKV_ST_TOKEN_SUM;
-        }
-    }
-    __syncthreads();
-}
-
 // Orders LDS accesses between the lanes of one wavefront (no s_barrier: the
 // other wavefronts of the workgroup are not involved).
 __device__ inline void wave_sync()
@@ -445,11 +315,14 @@ __device__ inline void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Batch ordering inside a workgroup whose global loads are all made by ONE
-// wavefront (the "index" wavefront), so that the workgroup's other wavefronts
-// can keep their own memory traffic in flight meanwhile (a wavefront's loads
-// complete in issue order).  Same results and flags as order_batch.  Three
-// phases:
+// Batch assembly ("Batch Construction and Sequence Flattening" of the
+// kongchang.com article) inside a workgroup whose global loads are all made
+// by ONE wavefront (the "index" wavefront), so that the workgroup's other
+// wavefronts can keep their own memory traffic in flight meanwhile (a
+// wavefront's loads complete in issue order): the n scheduled requests as
+// (count, row) keys in ascending order, the prefix sums of their counts
+// (saturating at INT32_MAX) and their completed counts; the same results and
+// flags as pkv_prepare_batch.  Three phases:
 //   wave_gather  (index wavefront) loads rows and counts, then at once each
 //                row's completed count, and writes the keys and their original
 //                indices to LDS; the completed counts stay in registers;

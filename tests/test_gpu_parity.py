@@ -117,7 +117,7 @@ def test_shuffled_schedule_same_outputs():
 
 @pytest.mark.parametrize("mode", MODES)
 def test_max_batch(mode):
-    """n = PKV_MAX_BATCH requests (the LDS sort's limit), counts 0..3, ties galore;
+    """n = PKV_MAX_BATCH requests (the keys held in LDS), counts 0..3, ties galore;
     in fused mode this exceeds the one-launch limit and takes the separate kernels."""
     import paged_kv_input_amd as pkv
 
