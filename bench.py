@@ -573,6 +573,7 @@ def main():
 
     import torch
 
+    from paged_kv_input_amd import api
     from paged_kv_input_amd.step import DeviceStep, GroupSpec
 
     torch.cuda.set_device(0)
@@ -695,7 +696,10 @@ def main():
 
     ab = algorithmic_bytes(batch)
     cb = call_bytes(batch)
-    use_fused = fused_ms <= calls_ms
+    # pkv_step is one launch only within the fused kernel's batch and group
+    # limits; past them it runs the three calls itself.
+    one_launch = batch.n <= api.STEP_MAX_BATCH and 1 <= ng <= api.STEP_MAX_GROUPS
+    use_fused = one_launch and fused_ms <= calls_ms
     ms = fused_ms if use_fused else calls_ms
     context = context_figures(ab["total"], args.steps, args.warmup, stream)
     context["step_vs_copy"] = context["d2d_copy_same_bytes"]["ms"] / ms

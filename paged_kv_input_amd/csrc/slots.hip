@@ -29,6 +29,7 @@ constexpr int kSlotTokensPerThread = 4;
 constexpr int kSlotTokensPerBlock = kSlotThreads * kSlotTokensPerThread;
 constexpr int kPageRowsPerBlock = kSlotThreads / kWave;   // one batch row per wave
 constexpr int kPageUnroll = 4;
+constexpr int kStageLoads = PKV_MAX_BATCH / kSlotThreads + 1;   // query_start_loc has n + 1
 
 __global__ __launch_bounds__(kSlotThreads) void k_slots(
     int32_t n, int32_t T, const int32_t* __restrict__ index_mapping,
@@ -54,10 +55,29 @@ __global__ __launch_bounds__(kSlotThreads) void k_slots(
             const int64_t t = t0 + u * kSlotThreads;
             pos[u] = positions[t < T ? t : T - 1];
         }
-        for (int i = tid; i <= n; i += kSlotThreads)
-            s_qsl[i] = query_start_loc[i];
-        for (int i = tid; i < n; i += kSlotThreads)
-            s_row[i] = index_mapping[i];
+        // The whole batch's boundaries and rows, every load of a thread in
+        // flight together (a load-then-store loop waits once per iteration).
+        int32_t q[kStageLoads];
+        int32_t r[kStageLoads];
+        // Rounds past the batch are skipped as a whole (a uniform test).
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int i = u * kSlotThreads + tid;
+            if (u * kSlotThreads <= n) {
+                q[u] = query_start_loc[i <= n ? i : 0];
+                r[u] = n > 0 ? index_mapping[i < n ? i : 0] : 0;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int i = u * kSlotThreads + tid;
+            if (u * kSlotThreads <= n) {
+                if (i <= n)
+                    s_qsl[i] = q[u];
+                if (i < n)
+                    s_row[i] = r[u];
+            }
+        }
         __syncthreads();
 
         int64_t src[kSlotTokensPerThread];
@@ -114,11 +134,14 @@ __global__ __launch_bounds__(kSlotThreads) void k_slots(
         const int b = ((int)blockIdx.x - token_blocks) * kPageRowsPerBlock + tid / kWave;
         const int lane = tid & (kWave - 1);
         if (b < n) {
-            const int32_t row = index_mapping[b];
+            int32_t row = index_mapping[b];
+            int32_t sl = seq_lens[b];
+            // Both loads issued before the branch that needs sl (otherwise it
+            // is sunk there, a second round trip after the row's).
+            __asm__ volatile("" : "+v"(row), "+v"(sl));
             if (row < 0 || row >= R) {
                 flags |= PKV_ST_BAD_ROW;
             } else {
-                const int32_t sl = seq_lens[b];
                 int64_t visible = sl <= 0 ? 0 : ((int64_t)sl + block_size - 1) / block_size;
                 if (visible > MB) {
                     flags |= PKV_ST_LB_OOR;

@@ -91,7 +91,7 @@ def test_tiny_random(seed, mode):
 
 
 @pytest.mark.parametrize("name", ["decode_256x1", "mixed_8192", "prefill_16x2048",
-                                  "two_groups_512req"])
+                                  "two_groups_512req", "decode_4096x1"])
 @pytest.mark.parametrize("mode", MODES)
 def test_full_size(name, mode):
     """Full configuration sizes, the launch configuration the benchmark times."""

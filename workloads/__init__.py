@@ -413,6 +413,10 @@ CONFIGS = {
     # block tables and pool, one head of 128 bf16 per token (256-byte rows).
     "prefill_16x2048_tp8": (lambda s: _long_prefill(s, H=1, name="prefill_16x2048_tp8"), 4),
     "two_groups_512req": (lambda s: _two_groups(s), 5),
+    # A wide decode batch: 4096 requests x 1 token among 8192 state rows,
+    # contexts U{128..2048}; past the one-launch step's batch limit.
+    "decode_4096x1": (lambda s: _decode_heavy(s, n=4096, R=8192, hi=2048,
+                                              name="decode_4096x1"), 6),
 }
 
 # Reduced versions: same structure, sizes the oracle finishes in well under a
