@@ -95,7 +95,7 @@ int pkv_prepare_batch(int32_t n, int32_t T, const int32_t* sched_rows,
         return rc;
     return from_hip(pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
                                         token_stride, L, index_mapping, query_start_loc, seq_lens,
-                                        positions, input_ids, status,
+                                        positions, input_ids, 0, nullptr, status,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -165,10 +165,14 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
                                          token_stride, L, index_mapping, query_start_loc,
                                          seq_lens, positions, input_ids, num_groups, groups,
                                          status, s));
+    // Past the one-launch limits: the batch and, for up to PKV_STEP_MAX_GROUPS
+    // groups, their slots and pages in one launch; then one scatter per group.
+    const bool with_slots = num_groups <= PKV_STEP_MAX_GROUPS;
     hipError_t e = pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
                                        token_stride, L, index_mapping, query_start_loc, seq_lens,
-                                       positions, input_ids, status, s);
-    for (int i = 0; e == hipSuccess && i < num_groups; ++i) {
+                                       positions, input_ids, with_slots ? num_groups : 0,
+                                       groups, status, s);
+    for (int i = 0; !with_slots && e == hipSuccess && i < num_groups; ++i) {
         const pkv_group& g = groups[i];
         e = pkv::launch_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,
                               g.block_table, R, g.MB, g.block_size, g.num_blocks,

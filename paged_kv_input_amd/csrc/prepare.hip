@@ -51,6 +51,26 @@ __device__ __forceinline__ void wave_add(uint32_t& less, uint64_t& sum)
     xor_add<32>(less, sum);                  // every lane holds the wavefront's totals
 }
 
+// KV-cache groups whose write slots and visible pages k_prepare<K, true>
+// produces with the batch (pkv_step past its one-launch limits).
+struct PrepGroup {
+    const int32_t* block_table;
+    int32_t* slot_mapping;
+    int32_t* input_block_tables;      // or NULL
+    int32_t MB;
+    int32_t block_size;
+    int32_t bs_shift;                 // log2(block_size), or -1
+    int32_t num_blocks;
+    int32_t window;                   // sliding window, 0 = full attention
+};
+
+struct PrepGroups {
+    int32_t num_groups;
+    PrepGroup g[PKV_STEP_MAX_GROUPS];
+};
+
+constexpr int kPagePer = 4;                                 // visible pages per thread and round
+
 // A batch of 0 <= n <= PKV_MAX_BATCH requests (n = 0: one workgroup, for
 // query_start_loc[0] and the tokens); workgroup w serves the kKeys
 // requests kKeys*w .. kKeys*w + kKeys - 1 in schedule order, with 16 / kKeys
@@ -58,15 +78,17 @@ __device__ __forceinline__ void wave_add(uint32_t& less, uint64_t& sum)
 // before its own and its first flat token the sum of their counts; the
 // workgroup then writes its requests' per-request outputs and flat tokens
 // (every token below T that belongs to one of them), and its share of the
-// tokens past the counts' sum.
-template <int kKeys>
+// tokens past the counts' sum.  With kSlots it also writes, for every group
+// in gs, those tokens' slots and those requests' visible pages, with the
+// results and flags of pkv_compute_slot_mapping.
+template <int kKeys, bool kSlots>
 __global__ __launch_bounds__(kPrepThreads) void k_prepare(
     int32_t n, int32_t T, const int32_t* __restrict__ sched_rows,
     const int32_t* __restrict__ num_scheduled, const int32_t* __restrict__ completed, int32_t R,
     const int32_t* __restrict__ token_ids, int64_t token_stride, int32_t L,
     int32_t* __restrict__ index_mapping, int32_t* __restrict__ query_start_loc,
     int32_t* __restrict__ seq_lens, int32_t* __restrict__ positions,
-    int32_t* __restrict__ input_ids, uint32_t* __restrict__ status)
+    int32_t* __restrict__ input_ids, uint32_t* __restrict__ status, const PrepGroups gs)
 {
     constexpr int kPerKey = kPrepWaves / kKeys;            // wavefronts per request
     constexpr int kLanes = kPerKey * kWave;                // lanes per request
@@ -78,6 +100,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
     __shared__ int64_t s_start[kKeys];            // first flat token of each request
     __shared__ int32_t s_row[kKeys];              // its row, or -1 when outside [0, R)
     __shared__ int32_t s_done[kKeys];             // its completed count
+    __shared__ int32_t s_b[kKeys];                // its batch row
+    __shared__ int32_t s_sl[kKeys];               // its seq_len as written
+    __shared__ int32_t s_qcount[kKeys];           // query_start_loc[b + 1] - query_start_loc[b]
+    __shared__ int64_t s_pfirst[kKeys + 1];       // offsets of the visible-page lists
+    __shared__ int64_t s_pwin[kKeys];             // first page a window may leave as a hole
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -172,17 +199,20 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
         const bool row_ok = row >= 0 && row < R;
         const int64_t start = (int64_t)sum;
         const int32_t done = have && row_ok ? completed[row] : 0;
+        const int64_t end = start + c;
+        const int32_t q_end = end > INT32_MAX ? INT32_MAX : (int32_t)end;
+        const int32_t q_start = start > INT32_MAX ? INT32_MAX : (int32_t)start;
+        const int32_t sl = row_ok ? (int32_t)(uint32_t)(uint64_t)((int64_t)done + c) : -1;
         if (have) {
-            const int64_t end = start + c;
             index_mapping[b] = row;
-            query_start_loc[b + 1] = end > INT32_MAX ? INT32_MAX : (int32_t)end;
-            if (row_ok) {
-                seq_lens[b] = (int32_t)(uint32_t)(uint64_t)((int64_t)done + c);
-            } else {
-                seq_lens[b] = -1;
+            query_start_loc[b + 1] = q_end;
+            seq_lens[b] = sl;
+            if (!row_ok)
                 flags |= PKV_ST_BAD_ROW;
-            }
         }
+        s_b[q] = b;
+        s_sl[q] = sl;
+        s_qcount[q] = q_end - q_start;
         // tokens of this request below T (those at T and beyond are dropped)
         const int64_t room = (int64_t)T - start;
         const int64_t own = !have ? 0 : (c < room ? c : (room > 0 ? room : 0));
@@ -217,12 +247,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
         int64_t t_of[kPrepTok];
         int32_t pos_out[kPrepTok];
         int64_t src[kPrepTok];
+        int w_of[kPrepTok];                                 // request within the workgroup
 #pragma unroll
         for (int u = 0; u < kPrepTok; ++u) {
             const int64_t f = f0 + (int64_t)u * kPrepThreads + tid;
             t_of[u] = -1;
             pos_out[u] = -1;
             src[u] = -1;
+            w_of[u] = 0;
             if (f >= F)
                 continue;
             int w = 0;                                      // last list starting at or before f
@@ -230,6 +262,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
             for (int step = kKeys / 2; step > 0; step >>= 1)
                 if (s_first[w + step] <= f)
                     w += step;
+            w_of[u] = w;
             const int64_t jj = f - s_first[w];
             t_of[u] = s_start[w] + jj;
             const int32_t row = s_row[w];
@@ -249,6 +282,55 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
             if (src[u] < 0)
                 id_out[u] = -1;
         }
+        if constexpr (kSlots) {
+            // Each group's slots: position -> (logical block, offset) ->
+            // physical block through the row's block table; a lane's lookups
+            // of a group are in flight together.
+            for (int gi = 0; gi < gs.num_groups; ++gi) {
+                const PrepGroup& g = gs.g[gi];
+                int64_t bsrc[kPrepTok];
+                int32_t boff[kPrepTok];
+#pragma unroll
+                for (int u = 0; u < kPrepTok; ++u) {
+                    bsrc[u] = -1;
+                    boff[u] = 0;
+                    if (t_of[u] < 0 || s_row[w_of[u]] < 0)
+                        continue;                           // no request, or a bad row
+                    const int32_t p = pos_out[u];
+                    if (p < 0) {
+                        flags |= PKV_ST_POS_OOR;
+                        continue;
+                    }
+                    const int32_t lb = g.bs_shift >= 0 ? (p >> g.bs_shift) : p / g.block_size;
+                    boff[u] = p - lb * g.block_size;
+                    if (lb >= g.MB)
+                        flags |= PKV_ST_LB_OOR;
+                    else
+                        bsrc[u] = (int64_t)s_row[w_of[u]] * g.MB + lb;
+                }
+                const bool have_bt = R > 0 && g.MB > 0;     // uniform
+                int32_t blk[kPrepTok];
+#pragma unroll
+                for (int u = 0; u < kPrepTok; ++u) {
+                    blk[u] = have_bt ? g.block_table[bsrc[u] >= 0 ? bsrc[u] : 0] : -1;
+                    if (bsrc[u] < 0)
+                        blk[u] = -1;
+                }
+#pragma unroll
+                for (int u = 0; u < kPrepTok; ++u) {
+                    if (t_of[u] < 0)
+                        continue;
+                    int32_t slot = -1;
+                    if (bsrc[u] >= 0) {
+                        if (blk[u] < 0 || blk[u] >= g.num_blocks)
+                            flags |= PKV_ST_BLOCK_OOR;
+                        else
+                            slot = blk[u] * g.block_size + boff[u];
+                    }
+                    g.slot_mapping[t_of[u]] = slot;
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < kPrepTok; ++u) {
             if (t_of[u] >= 0) {
@@ -259,12 +341,92 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
         }
     }
 
+    if constexpr (kSlots) {
+        // Each group's visible pages of this workgroup's requests: the first
+        // ceil(seq_len / block_size) block-table entries, copied as one list
+        // over the workgroup, kPagePer entries per thread and round.
+        for (int gi = 0; gi < gs.num_groups; ++gi) {
+            const PrepGroup& g = gs.g[gi];
+            if (g.input_block_tables == nullptr)
+                continue;                                   // uniform
+            if (tid < kKeys) {
+                const int qq = tid;
+                int64_t visible = 0;
+                int64_t first = 0;
+                if (s_row[qq] >= 0) {
+                    const int32_t sl = s_sl[qq];
+                    visible = sl <= 0 ? 0 : ((int64_t)sl + g.block_size - 1) / g.block_size;
+                    if (visible > g.MB) {
+                        flags |= PKV_ST_LB_OOR;
+                        visible = g.MB;
+                    }
+                    // pages before the window may be -1 holes (freed blocks)
+                    first = window_first(sl, s_qcount[qq], g.window) / g.block_size;
+                }
+                s_pfirst[qq + 1] = visible;
+                s_pwin[qq] = first;
+            }
+            __syncthreads();
+            if (tid == 0) {
+                int64_t run = 0;
+                s_pfirst[0] = 0;
+                for (int w = 0; w < kKeys; ++w) {
+                    run += s_pfirst[w + 1];
+                    s_pfirst[w + 1] = run;
+                }
+            }
+            __syncthreads();
+            const int64_t P = s_pfirst[kKeys];
+            for (int64_t f0 = 0; f0 < P; f0 += (int64_t)kPagePer * kPrepThreads) {
+                int64_t psrc[kPagePer];
+                int64_t pdst[kPagePer];
+                bool maybe_hole[kPagePer];
+#pragma unroll
+                for (int u = 0; u < kPagePer; ++u) {
+                    const int64_t f = f0 + (int64_t)u * kPrepThreads + tid;
+                    psrc[u] = -1;
+                    pdst[u] = -1;
+                    maybe_hole[u] = false;
+                    if (f >= P)
+                        continue;
+                    int w = 0;
+#pragma unroll
+                    for (int step = kKeys / 2; step > 0; step >>= 1)
+                        if (s_pfirst[w + step] <= f)
+                            w += step;
+                    const int64_t i = f - s_pfirst[w];
+                    psrc[u] = (int64_t)s_row[w] * g.MB + i;
+                    pdst[u] = (int64_t)s_b[w] * g.MB + i;
+                    maybe_hole[u] = i < s_pwin[w];
+                }
+                int32_t v[kPagePer];
+#pragma unroll
+                for (int u = 0; u < kPagePer; ++u)
+                    v[u] = g.block_table[psrc[u] >= 0 ? psrc[u] : 0];   // P > 0: a table exists
+#pragma unroll
+                for (int u = 0; u < kPagePer; ++u) {
+                    if (pdst[u] < 0)
+                        continue;
+                    const bool hole = maybe_hole[u] && v[u] == -1;
+                    if ((v[u] < 0 || v[u] >= g.num_blocks) && !hole)
+                        flags |= PKV_ST_BLOCK_OOR;
+                    g.input_block_tables[pdst[u]] = v[u];
+                }
+            }
+            __syncthreads();                                // the lists are rebuilt per group
+        }
+    }
+
     // Tokens past the counts' sum belong to no request (TOKEN_SUM).
     for (int64_t t = total + (int64_t)blockIdx.x * kPrepThreads + tid; t < T;
          t += (int64_t)gridDim.x * kPrepThreads) {
         positions[t] = -1;
         if (want_ids)
             input_ids[t] = -1;
+        if constexpr (kSlots) {
+            for (int gi = 0; gi < gs.num_groups; ++gi)
+                gs.g[gi].slot_mapping[t] = -1;
+        }
     }
     report_status(status, flags);
 }
@@ -288,24 +450,45 @@ hipError_t launch_prepare(int32_t n, int32_t T, const int32_t* sched_rows,
                           const int32_t* num_scheduled, const int32_t* completed, int32_t R,
                           const int32_t* token_ids, int64_t token_stride, int32_t L,
                           int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
-                          int32_t* positions, int32_t* input_ids, uint32_t* status,
-                          hipStream_t stream)
+                          int32_t* positions, int32_t* input_ids, int32_t num_groups,
+                          const pkv_group* groups, uint32_t* status, hipStream_t stream)
 {
+    PrepGroups gs = {};
+    gs.num_groups = num_groups;
+    for (int i = 0; i < num_groups; ++i) {
+        const pkv_group& in = groups[i];
+        PrepGroup& g = gs.g[i];
+        g.block_table = in.block_table;
+        g.slot_mapping = in.slot_mapping;
+        g.input_block_tables = in.input_block_tables;
+        g.MB = in.MB;
+        g.block_size = in.block_size;
+        g.bs_shift = (in.block_size & (in.block_size - 1)) == 0 ? __builtin_ctz(in.block_size) : -1;
+        g.num_blocks = in.num_blocks;
+        g.window = in.sliding_window;
+    }
     const int keys = prep_keys(n, T);
     const int64_t blocks = n > 0 ? ((int64_t)n + keys - 1) / keys : 1;
     const dim3 grid((unsigned)blocks), block(kPrepThreads);
-#define PKV_PREP_LAUNCH(K)                                                                        \
-    k_prepare<K><<<grid, block, 0, stream>>>(n, T, sched_rows, num_scheduled, completed, R,      \
-                                             token_ids, token_stride, L, index_mapping,           \
-                                             query_start_loc, seq_lens, positions, input_ids,     \
-                                             status)
-    switch (keys) {
-    case 1: PKV_PREP_LAUNCH(1); break;
-    case 2: PKV_PREP_LAUNCH(2); break;
-    case 4: PKV_PREP_LAUNCH(4); break;
-    case 8: PKV_PREP_LAUNCH(8); break;
-    default: PKV_PREP_LAUNCH(16); break;
+#define PKV_PREP_LAUNCH(K, S)                                                                     \
+    k_prepare<K, S><<<grid, block, 0, stream>>>(n, T, sched_rows, num_scheduled, completed, R,   \
+                                                token_ids, token_stride, L, index_mapping,        \
+                                                query_start_loc, seq_lens, positions, input_ids,  \
+                                                status, gs)
+#define PKV_PREP_KEYS(S)                                                                          \
+    switch (keys) {                                                                               \
+    case 1: PKV_PREP_LAUNCH(1, S); break;                                                         \
+    case 2: PKV_PREP_LAUNCH(2, S); break;                                                         \
+    case 4: PKV_PREP_LAUNCH(4, S); break;                                                         \
+    case 8: PKV_PREP_LAUNCH(8, S); break;                                                         \
+    default: PKV_PREP_LAUNCH(16, S); break;                                                       \
     }
+    if (num_groups > 0) {
+        PKV_PREP_KEYS(true)
+    } else {
+        PKV_PREP_KEYS(false)
+    }
+#undef PKV_PREP_KEYS
 #undef PKV_PREP_LAUNCH
     return hipGetLastError();
 }

@@ -194,3 +194,129 @@ def test_no_requests(T):
     got, want = compare_with_oracle(rows, rows.copy(), np.zeros(4, np.int32), tok, T=T)
     assert got["query_start_loc"].tolist() == [0]
     assert (got["status"] != 0) == (T > 0)
+
+
+def _random_wide(seed, n_lo=513, n_hi=1600):
+    """A seeded random step past the one-launch step's 512 requests: counts
+    with ties and zeros, 1-4 groups with block sizes 1-64 (3 included) and
+    rows of 16 B to 1 KiB."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(n_lo, n_hi))
+    R = n + int(rng.integers(0, n + 1))
+    rows = rng.choice(R, n, replace=False).astype(np.int32)
+    counts = np.where(rng.random(n) < 0.6, 1, rng.integers(0, 20, n)).astype(np.int32)
+    L = 64 + 24
+    completed = np.zeros(R, np.int32)
+    completed[rows] = rng.integers(0, 64, n)
+    T = int(counts.sum())
+    groups = []
+    for _ in range(int(rng.integers(1, 5))):
+        bs = int(rng.choice([1, 3, 4, 8, 16, 32, 64]))
+        MB = -(-L // bs)
+        need = int(sum(max(0, -(-(int(completed[r]) + int(c)) // bs) - int(completed[r]) // bs)
+                       for r, c in zip(rows, counts)))
+        NB = need + int(rng.integers(1, 64))
+        bt = workloads._block_table(rng, R, MB, NB, bs, rows, counts, completed)
+        H, D = [(1, 8), (2, 64), (4, 32), (1, 512)][int(rng.integers(0, 4))]
+        k = rng.integers(0, 65535, (T, H, D), dtype=np.uint16)
+        v = rng.integers(0, 65535, (T, H, D), dtype=np.uint16)
+        groups.append(workloads.KVGroup(bs, NB, MB, bt, H, D, "fp16", k, v))
+    tok = rng.integers(0, 1 << 20, (R, L), dtype=np.int32)
+    return workloads.Batch(f"wide_sweep_{seed}", seed, rows, counts, completed, tok, groups)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_wide_step_random_groups(seed):
+    """pkv_step past 512 requests with 1-4 groups: the batch, every group's
+    slots and visible pages in one launch, then the scatters; bit-exact."""
+    run_and_compare(_random_wide(7700 + seed), mode="fused")
+
+
+def test_wide_step_data_errors():
+    """pkv_step past 512 requests with bad rows, negative counts, missing and
+    out-of-pool blocks, logical blocks past the table and a host token count
+    above the counts' sum: same outputs, caches and status bits as the oracle."""
+    import torch
+    from paged_kv_input_amd.step import DeviceStep, GroupSpec
+    from gpu_util import SENTINEL16
+
+    b = _random_wide(7800, 900, 901)
+    rng = np.random.default_rng(7801)
+    n, R = b.n, b.completed.shape[0]
+    bad = rng.choice(n, 30, replace=False)
+    b.sched_rows[bad[:8]] = -3
+    b.sched_rows[bad[8:14]] = R + 2
+    b.num_scheduled[bad[14:20]] = -2
+    g0 = b.groups[0]
+    bt = g0.block_table
+    live = np.flatnonzero((bt >= 0).any(axis=1))
+    bt[live[:6], 0] = -1                                     # missing blocks
+    bt[live[6:12], 0] = g0.num_blocks + 5                    # blocks past the pool
+    b.completed[b.sched_rows[bad[20:30]]] = g0.max_blocks * g0.block_size + 1   # past the table
+    T = int(np.maximum(b.num_scheduled.astype(np.int64), 0).sum()) + 17
+    for g in b.groups:                                       # K/V rows: exactly T
+        g.k = np.resize(g.k, (T,) + g.k.shape[1:])
+        g.v = np.resize(g.v, (T,) + g.v.shape[1:])
+    say(f"[case] wide step errors n={n} T={T} groups={len(b.groups)}")
+    step = DeviceStep(b.sched_rows, b.num_scheduled, b.completed, b.token_ids,
+                      [GroupSpec(g.block_table, g.block_size, g.num_blocks, g.k, g.v)
+                       for g in b.groups],
+                      cache_fill=SENTINEL16, ibt_fill=oracle.IBT_UNWRITTEN, num_tokens=T)
+    step.run_fused()
+    torch.cuda.synchronize()
+    prep = oracle.prepare_batch(b.sched_rows, b.num_scheduled, b.completed, b.token_ids, T=T)
+    want = prep["status"]
+    for key in ("index_mapping", "query_start_loc", "seq_lens", "positions", "input_ids"):
+        assert_equal(key, step.host(key), prep[key])
+    for gi, g in enumerate(b.groups):
+        sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                         prep["seq_lens"], prep["positions"], g.block_table,
+                                         g.block_size, g.num_blocks)
+        kc = np.full((g.num_slots, g.num_heads, g.head_dim), 0xFFFF, np.uint16)
+        vc = kc.copy()
+        rc, sst = oracle.scatter_kv(g.k, g.v, kc, vc, sm["slot_mapping"])
+        want |= sm["status"] | sst
+        assert_equal(f"g{gi} slots", step.host("slot_mapping", gi), sm["slot_mapping"])
+        assert_equal(f"g{gi} pages", step.host("input_block_tables", gi),
+                     sm["input_block_tables"])
+        assert_equal(f"g{gi} k_cache", step.host("k_cache", gi).view(np.uint16), kc)
+        assert_equal(f"g{gi} v_cache", step.host("v_cache", gi).view(np.uint16), vc)
+    assert step.status_bits() == want, (step.status_bits(), want)
+    assert (want & 0x3F) == 0x3F            # every data error above was hit
+
+
+@pytest.mark.parametrize("W", [1, 37, 300])
+def test_wide_step_window(W):
+    """pkv_step past 512 requests with two sliding-window groups: blocks behind
+    every window freed first (the -1 holes), then the step's pages and slots
+    against the oracle's."""
+    from test_gpu_alloc import check_free
+    from paged_kv_input_amd.step import DeviceStep, GroupSpec
+    from gpu_util import SENTINEL16
+    import torch
+
+    b = _random_wide(7900 + W, 700, 701)
+    while len(b.groups) < 2:
+        b = _random_wide(b.seed + 1000, 700, 701)
+    b.groups = b.groups[:2]
+    tables, specs = [], []
+    for gi, g in enumerate(b.groups):
+        bt = check_free(b.sched_rows, b.completed, g.block_table, g.block_size, W, f"g{gi}")
+        tables.append(bt)
+        specs.append(GroupSpec(bt, g.block_size, g.num_blocks, g.k, g.v, sliding_window=W))
+    say(f"[case] wide step window W={W} n={b.n} T={b.T}")
+    step = DeviceStep(b.sched_rows, b.num_scheduled, b.completed, b.token_ids, specs,
+                      cache_fill=SENTINEL16, ibt_fill=oracle.IBT_UNWRITTEN)
+    step.run_fused()
+    torch.cuda.synchronize()
+    prep = oracle.prepare_batch(b.sched_rows, b.num_scheduled, b.completed, b.token_ids)
+    status = prep["status"]
+    for gi, (g, bt) in enumerate(zip(b.groups, tables)):
+        sm = oracle.compute_slot_mapping(prep["index_mapping"], prep["query_start_loc"],
+                                         prep["seq_lens"], prep["positions"], bt, g.block_size,
+                                         g.num_blocks, sliding_window=W)
+        status |= sm["status"]
+        assert_equal(f"g{gi} slots", step.host("slot_mapping", gi), sm["slot_mapping"])
+        assert_equal(f"g{gi} pages", step.host("input_block_tables", gi),
+                     sm["input_block_tables"])
+    assert step.status_bits() == status == 0
