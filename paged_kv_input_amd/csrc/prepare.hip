@@ -20,6 +20,14 @@
 // kernel's time is about three memory round trips (schedule, completed
 // counts, token table) plus the launch; no grid-wide barrier, second launch
 // or device-side counter is needed.
+//
+// With KV-cache groups attached (pkv_step past its one-launch limits) the same
+// pass also writes every group's slots, through the coordinate-conversion
+// chain of the article's "Multi-Layer Coordinate Conversion Pipeline" and
+// "Address Calculation Example", and each workgroup copies its requests'
+// visible pages ("Complete Input Preparation for the Attention Module"), where
+// a sliding-window group may hold -1 holes before the window (the blocks
+// freed by "allocate_slots()" of the caffein.top scheduler page).
 #include "internal.h"
 #include "launchers.h"
 
