@@ -12,8 +12,10 @@ caches), so consecutive steps never find each other's data in L2 or the
 256 MB Infinity Cache (a cycle touches over 1 GB).  W untimed warm-up steps,
 then exactly K timed steps back to back, bracketed by torch.cuda.synchronize()
 on both sides and by HIP events on the launch stream; ms_per_step is the
-event interval / K.  The step runs through pkv_step (one launch) and, timed
-the same way, through the three separate calls.  Secondary figures: the
+event interval / K.  The step runs through pkv_step (one launch up to 512
+requests and four groups; past that, the batch with every group's slots and
+pages in one launch, then the scatters) and, timed the same way, through the
+three separate calls; value is the faster.  Secondary figures: the
 per-call split of the three calls, the host wall time of one step with the
 schedule uploaded from pinned host memory, a single-step cold measurement (a
 1 GiB rewrite before each step, events around it; median, p10, p90), ceilings to
@@ -696,14 +698,23 @@ def main():
 
     ab = algorithmic_bytes(batch)
     cb = call_bytes(batch)
-    # pkv_step is one launch only within the fused kernel's batch and group
-    # limits; past them it runs the three calls itself.
+    # pkv_step is one launch (k_step) within the fused kernel's batch and group
+    # limits; past them it runs k_prepare with the groups' slots and pages,
+    # then the scatters (more than four groups: the three calls).
     one_launch = batch.n <= api.STEP_MAX_BATCH and 1 <= ng <= api.STEP_MAX_GROUPS
-    use_fused = one_launch and fused_ms <= calls_ms
+    use_fused = fused_ms <= calls_ms
     ms = fused_ms if use_fused else calls_ms
+    if use_fused and one_launch:
+        path = "pkv_step (one launch)"
+    elif use_fused and ng <= api.STEP_MAX_GROUPS:
+        path = "pkv_step (batch with slots and pages, then the scatters)"
+    elif use_fused:
+        path = "pkv_step (the separate kernels)"
+    else:
+        path = "three calls"
     context = context_figures(ab["total"], args.steps, args.warmup, stream)
     context["step_vs_copy"] = context["d2d_copy_same_bytes"]["ms"] / ms
-    if use_fused:
+    if use_fused and one_launch:
         kernel, launch_ms, kbytes, prof_key = "pkv_step (k_step)", fused_ms, ab["total"], "step"
     else:
         kernel = "scatter_kv (k_scatter)"
@@ -734,7 +745,7 @@ def main():
             "kv_groups": ng, "layers": 1, "rotating_batches": ROTATE,
         },
         "step": {
-            "path": "pkv_step (one launch)" if use_fused else "three calls",
+            "path": path,
             "algorithmic_bytes": ab["total"],
             "hbm_gbs": ab["total"] / (ms * 1e-3) / 1e9,
             "frac_of_peak": ab["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
