@@ -77,3 +77,19 @@ def test_more_than_one_gpu_is_refused(gpus):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_wide_decode_bytes_closed_form():
+    """4096 decodes among 8192 rows, contexts U{128..2048}, block size 16:
+    one touched block per request, ceil(seq_len / 16) visible pages each."""
+    import numpy as np
+
+    b = workloads.make("decode_4096x1")
+    assert (b.n, b.T, b.completed.shape[0]) == (4096, 4096, 8192)
+    ab = bench.algorithmic_bytes(b)
+    seq = b.completed[b.sched_rows].astype(np.int64) + 1
+    assert seq.min() >= 129 and seq.max() <= 2049
+    assert ab["block_table"] == 4 * 4096
+    assert ab["pages"] == 8 * int(((seq + 15) // 16).sum())
+    assert ab["kv"] == 4 * 4096 * 2048
+    assert ab["requests"] == 24 * 4096 + 4
