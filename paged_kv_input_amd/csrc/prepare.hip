@@ -16,7 +16,9 @@
 // 512 requests 11.0 -> 6.0 us, a 16-request prefill 7.1 -> 5.3-6.3 us).  Each
 // workgroup stages every key in LDS, ranks its own 1 .. 16 requests (fewer
 // when their tokens are many), writes their per-request outputs and then
-// their flat tokens, which need no search beyond its own requests.  The
+// their flat tokens, which need no search beyond its own requests; when even
+// one request has many tokens, several workgroups (the grid's second
+// dimension) rank the same requests and split their tokens.  The
 // kernel's time is about three memory round trips (schedule, completed
 // counts, token table) plus the launch; no grid-wide barrier, second launch
 // or device-side counter is needed.
@@ -81,8 +83,9 @@ constexpr int kPagePer = 4;                                 // visible pages per
 
 // A batch of 0 <= n <= PKV_MAX_BATCH requests (n = 0: one workgroup, for
 // query_start_loc[0] and the tokens); workgroup w serves the kKeys
-// requests kKeys*w .. kKeys*w + kKeys - 1 in schedule order, with 16 / kKeys
-// wavefronts each.  A request's batch row b is the number of keys that sort
+// requests kKeys*w .. kKeys*w + kKeys - 1 in schedule order (w = blockIdx.x),
+// with 16 / kKeys wavefronts each, and slice blockIdx.y of gridDim.y of their
+// token and page lists.  A request's batch row b is the number of keys that sort
 // before its own and its first flat token the sum of their counts; the
 // workgroup then writes its requests' per-request outputs and flat tokens
 // (every token below T that belongs to one of them), and its share of the
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
         if (i < n) {
             int32_t c = counts[u];
             if (c < 0) {
-                if (blockIdx.x == 0)
+                if (blockIdx.x == 0 && blockIdx.y == 0)
                     flags |= PKV_ST_BAD_COUNT;
                 c = 0;
             }
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
         const int32_t q_end = end > INT32_MAX ? INT32_MAX : (int32_t)end;
         const int32_t q_start = start > INT32_MAX ? INT32_MAX : (int32_t)start;
         const int32_t sl = row_ok ? (int32_t)(uint32_t)(uint64_t)((int64_t)done + c) : -1;
-        if (have) {
+        if (have && blockIdx.y == 0) {                  // one split writes them
             index_mapping[b] = row;
             query_start_loc[b + 1] = q_end;
             seq_lens[b] = sl;
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
         s_done[q] = done;
         s_first[q + 1] = own;
     }
-    if (blockIdx.x == 0 && tid == 0) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
         query_start_loc[0] = 0;
         if (total != (int64_t)T)
             flags |= PKV_ST_TOKEN_SUM;
@@ -248,10 +251,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
     // The workgroup's token lists, concatenated, kPrepTok tokens per thread
     // and round: resolve each token's request, then issue all token-table
     // loads of the round together.
+    // This split's slice [f_lo, f_hi) of the concatenated lists.
     const int64_t F = s_first[kKeys];
+    const int64_t per = gridDim.y == 1 ? F : (F + gridDim.y - 1) / gridDim.y;   // uniform
+    const int64_t f_lo = (int64_t)blockIdx.y * per;
+    const int64_t f_hi = f_lo + per < F ? f_lo + per : F;
     const bool want_ids = input_ids != nullptr;
     const bool have_ids = want_ids && R > 0 && L > 0;
-    for (int64_t f0 = 0; f0 < F; f0 += (int64_t)kPrepTok * kPrepThreads) {
+    for (int64_t f0 = f_lo; f0 < f_hi; f0 += (int64_t)kPrepTok * kPrepThreads) {
         int64_t t_of[kPrepTok];
         int32_t pos_out[kPrepTok];
         int64_t src[kPrepTok];
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
             pos_out[u] = -1;
             src[u] = -1;
             w_of[u] = 0;
-            if (f >= F)
+            if (f >= f_hi)
                 continue;
             int w = 0;                                      // last list starting at or before f
 #pragma unroll
@@ -385,7 +392,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
             }
             __syncthreads();
             const int64_t P = s_pfirst[kKeys];
-            for (int64_t f0 = 0; f0 < P; f0 += (int64_t)kPagePer * kPrepThreads) {
+            const int64_t pper = gridDim.y == 1 ? P : (P + gridDim.y - 1) / gridDim.y;
+            const int64_t p_lo = (int64_t)blockIdx.y * pper;
+            const int64_t p_hi = p_lo + pper < P ? p_lo + pper : P;
+            for (int64_t f0 = p_lo; f0 < p_hi; f0 += (int64_t)kPagePer * kPrepThreads) {
                 int64_t psrc[kPagePer];
                 int64_t pdst[kPagePer];
                 bool maybe_hole[kPagePer];
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
                     psrc[u] = -1;
                     pdst[u] = -1;
                     maybe_hole[u] = false;
-                    if (f >= P)
+                    if (f >= p_hi)
                         continue;
                     int w = 0;
 #pragma unroll
@@ -426,8 +436,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_prepare(
     }
 
     // Tokens past the counts' sum belong to no request (TOKEN_SUM).
-    for (int64_t t = total + (int64_t)blockIdx.x * kPrepThreads + tid; t < T;
-         t += (int64_t)gridDim.x * kPrepThreads) {
+    const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    for (int64_t t = total + wg * kPrepThreads + tid; t < T;
+         t += (int64_t)gridDim.x * gridDim.y * kPrepThreads) {
         positions[t] = -1;
         if (want_ids)
             input_ids[t] = -1;
@@ -450,6 +461,21 @@ __host__ inline int prep_keys(int32_t n, int32_t T)
     while (k < 16 && (k * 2 <= by_tokens || k < by_grid))
         k *= 2;
     return k;
+}
+
+// Splits of each workgroup's token and page lists (the grid's second
+// dimension): about 8192 tokens per workgroup on average, so that a few long
+// requests still spread over the chip; every split ranks its requests again
+// (cheap: splits > 1 only when n is small next to T).
+__host__ inline int prep_splits(int32_t n, int32_t T, int keys)
+{
+    const int64_t per_wg = n > 0 ? (int64_t)T * keys / n : (int64_t)T;
+    int64_t s = (per_wg + 8191) / 8192;
+    if (s < 1)
+        s = 1;
+    if (s > 1024)
+        s = 1024;
+    return (int)s;
 }
 
 }  // namespace
@@ -477,7 +503,7 @@ hipError_t launch_prepare(int32_t n, int32_t T, const int32_t* sched_rows,
     }
     const int keys = prep_keys(n, T);
     const int64_t blocks = n > 0 ? ((int64_t)n + keys - 1) / keys : 1;
-    const dim3 grid((unsigned)blocks), block(kPrepThreads);
+    const dim3 grid((unsigned)blocks, (unsigned)prep_splits(n, T, keys)), block(kPrepThreads);
 #define PKV_PREP_LAUNCH(K, S)                                                                     \
     k_prepare<K, S><<<grid, block, 0, stream>>>(n, T, sched_rows, num_scheduled, completed, R,   \
                                                 token_ids, token_stride, L, index_mapping,        \

@@ -168,12 +168,15 @@ def test_wide_whole_step(n):
 
 
 @pytest.mark.parametrize("n,mean,delta", [(16, 2048, 0), (16, 2048, -1000), (20, 750, 0),
-                                          (40, 300, 7), (100, 200, 0), (300, 40, -5)])
+                                          (40, 300, 7), (100, 200, 0), (300, 40, -5),
+                                          (16, 12000, 5), (4, 20000, 0), (2, 60000, -7)])
 def test_requests_per_workgroup(n, mean, delta):
     """Batches whose tokens per request select 1, 2, 4, 8 and 16 requests per
     workgroup (about 2048 tokens per workgroup: means of 2048, 750, 300, 200
-    and 40 tokens), with the host's token count equal to, above and below the
-    counts' sum (the cut falling inside a request)."""
+    and 40 tokens), and requests so long that several workgroups split one
+    request's tokens (means of 12000 to 60000), with the host's token count
+    equal to, above and below the counts' sum (the cut falling inside a
+    request)."""
     rng = np.random.default_rng(7600 + n + delta)
     R, L = 2 * n, 4 * mean + 64
     rows = rng.choice(R, n, replace=False).astype(np.int32)
@@ -320,3 +323,27 @@ def test_wide_step_window(W):
         assert_equal(f"g{gi} pages", step.host("input_block_tables", gi),
                      sm["input_block_tables"])
     assert step.status_bits() == status == 0
+
+
+def test_wide_step_long_requests():
+    """pkv_step past 512 requests with about 3000 tokens per request (1.8 M
+    tokens): two workgroups split each group of requests' tokens and pages."""
+    rng = np.random.default_rng(7950)
+    n, L, bs = 600, 4100, 64
+    R = 2 * n
+    rows = rng.choice(R, n, replace=False).astype(np.int32)
+    counts = rng.integers(2500, 3501, n).astype(np.int32)
+    completed = np.zeros(R, np.int32)
+    completed[rows] = rng.integers(0, 500, n)
+    MB = L // bs + 1
+    need = int(sum(max(0, -(-(int(completed[r]) + int(c)) // bs) - int(completed[r]) // bs)
+                   for r, c in zip(rows, counts)))
+    NB = need + 9
+    bt = workloads._block_table(rng, R, MB, NB, bs, rows, counts, completed)
+    T = int(counts.sum())
+    k = rng.integers(0, 65535, (T, 1, 8), dtype=np.uint16)
+    v = rng.integers(0, 65535, (T, 1, 8), dtype=np.uint16)
+    b = workloads.Batch("wide_long", 7950, rows, counts, completed,
+                        rng.integers(0, 1 << 20, (R, L), dtype=np.int32),
+                        [workloads.KVGroup(bs, NB, MB, bt, 1, 8, "fp16", k, v)])
+    run_and_compare(b, mode="fused")
