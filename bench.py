@@ -23,7 +23,7 @@ read the step against (a same-byte device copy, the dispatch floor), and the
 calls around the path: the state updates, the paged K/V read, the
 prefix-cache calls and the sliding-window and lookahead variants.
 
-Prints one JSON line (N = 1 only: this build runs on one GPU).
+Prints one JSON line (N = 1 only: the benchmark runs on one GPU).
 """
 from __future__ import annotations
 
@@ -562,7 +562,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} "
               f"(WORLD_SIZE {world}) is not supported", file=sys.stderr, flush=True)
         sys.exit(2)
 
