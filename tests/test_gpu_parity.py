@@ -357,3 +357,40 @@ def test_scatter_skips_negative_and_flags_out_of_range_slots():
     assert rc == 0 and ost == oracle.ST_SLOT_OOR == int(st.item())
     assert_equal("k_cache", kc.cpu().numpy(), ko)
     assert_equal("v_cache", vc.cpu().numpy(), vo)
+
+
+@pytest.mark.parametrize("name", ["seeded_16req", "mixed_8192", "two_groups_512req"])
+def test_later_layers_reuse_slot_mapping(name):
+    """One model step over four layers: pkv_step writes layer 0 and produces
+    each group's slot_mapping; layers 1-3 scatter their own K/V with
+    pkv_scatter_kv into their own caches through those slots.  Every layer's
+    rows at the oracle's slots hold that layer's payload, and no other row of
+    its caches was written (the payload never holds the 0xFFFF sentinel)."""
+    import torch
+    from paged_kv_input_amd import api
+
+    b = workloads.make(name, reduced=True) if name != "seeded_16req" else workloads.make(name)
+    step, prep, groups_o = run_and_compare(b, full_cache=False, mode="fused")
+    rng = np.random.default_rng(4040)
+    for layer in range(1, 4):
+        for gi, (g, go) in enumerate(zip(b.groups, groups_o)):
+            say(f"[case] {b.name} layer {layer} group {gi}")
+            k = rng.integers(0, 65535, (b.T, g.num_heads, g.head_dim), dtype=np.uint16)
+            v = rng.integers(0, 65535, (b.T, g.num_heads, g.head_dim), dtype=np.uint16)
+            shape = (g.num_slots, g.num_heads, g.head_dim)
+            kc = torch.full(shape, SENTINEL16, dtype=torch.int16, device="cuda")
+            vc = torch.full(shape, SENTINEL16, dtype=torch.int16, device="cuda")
+            st = torch.zeros(1, dtype=torch.int32, device="cuda")
+            api.scatter_kv(torch.from_numpy(k.view(np.int16)).cuda(),
+                           torch.from_numpy(v.view(np.int16)).cuda(), kc, vc,
+                           step.groups[gi]["slot_mapping"], status=st)
+            torch.cuda.synchronize()
+            assert int(st.item()) == 0
+            slots = np.asarray(go["slot_mapping"])
+            tok = np.flatnonzero(slots >= 0)
+            idx = torch.from_numpy(slots[tok].astype(np.int64)).cuda()
+            for key, cache, pay in (("k", kc, k), ("v", vc, v)):
+                got = cache.index_select(0, idx).cpu().numpy().view(np.uint16)
+                assert_equal(f"layer {layer} g{gi} {key} rows", got, pay[tok])
+                written = int((cache != SENTINEL16).flatten(1).any(dim=1).sum().item())
+                assert written == tok.size, (key, written, tok.size)
