@@ -130,46 +130,43 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v)
 
 // Elements of the register bitonic sort: kPer per lane (element s of lane l in
 // wavefront w has sort index w * 64 * kPer + s * 64 + l), each a 64-bit key
-// and, when kIdx, the key's original index.
-template <int kPer, bool kIdx>
+// and the key's original index.
+template <int kPer>
 struct SortRegs {
     uint64_t key[kPer];
-    int32_t idx[kIdx ? kPer : 1];
+    int32_t idx[kPer];
 };
 
 // Compare-exchange of element s with the partner's (okey, oidx): the lower
 // position of an ascending pair keeps the smaller key, and so on.  Strict
 // comparisons on both sides, so equal keys never move and the indices stay a
 // permutation.
-template <int kPer, bool kIdx>
-__device__ __forceinline__ void keep(SortRegs<kPer, kIdx>& r, int s, uint64_t okey, int32_t oidx,
+template <int kPer>
+__device__ __forceinline__ void keep(SortRegs<kPer>& r, int s, uint64_t okey, int32_t oidx,
                                      bool lower, bool ascending)
 {
     const bool take = lower == ascending ? okey < r.key[s] : r.key[s] < okey;
     r.key[s] = take ? okey : r.key[s];
-    if constexpr (kIdx)
-        r.idx[s] = take ? oidx : r.idx[s];
+    r.idx[s] = take ? oidx : r.idx[s];
 }
 
-template <int J, int kPer, bool kIdx>
-__device__ __forceinline__ void lane_pass(SortRegs<kPer, kIdx>& r, int base, int k)
+template <int J, int kPer>
+__device__ __forceinline__ void lane_pass(SortRegs<kPer>& r, int base, int k)
 {
     const int lane = (int)(threadIdx.x & (kWave - 1));
 #pragma unroll
     for (int s = 0; s < kPer; ++s) {
         const uint32_t lo = lane_xor<J>((uint32_t)r.key[s]);
         const uint32_t hi = lane_xor<J>((uint32_t)(r.key[s] >> 32));
-        int32_t oidx = 0;
-        if constexpr (kIdx)
-            oidx = (int32_t)lane_xor<J>((uint32_t)r.idx[s]);
+        const int32_t oidx = (int32_t)lane_xor<J>((uint32_t)r.idx[s]);
         const int i = base + s * kWave + lane;
         keep(r, s, ((uint64_t)hi << 32) | lo, oidx, (lane & J) == 0, (i & k) == 0);
     }
 }
 
 // Compare-exchange of slots s and s ^ D of each lane (elements 64 * D apart).
-template <int D, int kPer, bool kIdx>
-__device__ __forceinline__ void slot_pass(SortRegs<kPer, kIdx>& r, int base, int k)
+template <int D, int kPer>
+__device__ __forceinline__ void slot_pass(SortRegs<kPer>& r, int base, int k)
 {
     const int lane = (int)(threadIdx.x & (kWave - 1));
 #pragma unroll
@@ -182,28 +179,25 @@ __device__ __forceinline__ void slot_pass(SortRegs<kPer, kIdx>& r, int base, int
             const uint64_t tk = r.key[s];
             r.key[s] = swap ? r.key[o] : r.key[s];
             r.key[o] = swap ? tk : r.key[o];
-            if constexpr (kIdx) {
-                const int32_t ti = r.idx[s];
-                r.idx[s] = swap ? r.idx[o] : r.idx[s];
-                r.idx[o] = swap ? ti : r.idx[o];
-            }
+            const int32_t ti = r.idx[s];
+            r.idx[s] = swap ? r.idx[o] : r.idx[s];
+            r.idx[o] = swap ? ti : r.idx[o];
         }
     }
 }
 
-// Ascending bitonic sort of key[0 .. n) (with idx[0 .. n), the keys' original
-// indices, when kIdx) by every wavefront of a kThreads-thread workgroup; call
+// Ascending bitonic sort of key[0 .. n) with idx[0 .. n), the keys' original
+// indices, by every wavefront of a kThreads-thread workgroup; call
 // from every thread with the same n <= kPad.  The network spans kPad (a power
 // of two, at most kThreads * kPer) positions, padded with ~0 keys, and is
 // unrolled whole.  The elements stay in registers: pairs closer than 64 are
 // exchanged between lanes, pairs 64 .. 64 * (kPer - 1) apart are swapped
 // inside a lane, and only pairs in different wavefronts go through LDS.
-// Wavefronts holding only padding skip the work but keep the barriers.  With
-// a second buffer (kTwo: xkey, xidx) an LDS exchange costs one barrier,
-// alternating between the buffers; without one, two.  LDS traffic only, so
-// the wavefronts' outstanding loads stay in flight.  key / idx hold the result
-// on return, after a barrier.
-template <int kThreads, int kPer, int kPad, bool kIdx, bool kTwo>
+// Wavefronts holding only padding skip the work but keep the barriers.  The
+// LDS exchanges alternate between two buffers (key / idx and xkey / xidx), so
+// each costs one barrier.  LDS traffic only, so the wavefronts' outstanding
+// loads stay in flight.  key / idx hold the result on return, after a barrier.
+template <int kThreads, int kPer, int kPad>
 __device__ __forceinline__ void bitonic_regs(uint64_t* key, int16_t* idx, uint64_t* xkey,
                                              int16_t* xidx, int32_t n)
 {
@@ -213,14 +207,13 @@ __device__ __forceinline__ void bitonic_regs(uint64_t* key, int16_t* idx, uint64
     const int lane = (int)(threadIdx.x & (kWave - 1));
     const int base = (int)(threadIdx.x / kWave) * kSpan;
     const bool active = base < kPad;                      // uniform per wavefront
-    SortRegs<kPer, kIdx> r;
+    SortRegs<kPer> r;
     __syncthreads();                                      // the keys are in LDS
 #pragma unroll
     for (int s = 0; s < kPer; ++s) {
         const int i = base + s * kWave + lane;
         r.key[s] = i < n ? key[i] : ~0ull;                // padding sorts last
-        if constexpr (kIdx)
-            r.idx[s] = i < n ? idx[i] : i;
+        r.idx[s] = i < n ? idx[i] : i;
     }
     int pass = 0;                                         // LDS exchanges so far
 #pragma unroll
@@ -229,18 +222,15 @@ __device__ __forceinline__ void bitonic_regs(uint64_t* key, int16_t* idx, uint64
         for (int j = k >> 1; j >= kWave; j >>= 1) {
             if (j >= kSpan) {
                 // partner in another wavefront
-                const bool second = kTwo && (pass & 1) == 0;
+                const bool second = (pass & 1) == 0;
                 uint64_t* bk = second ? xkey : key;
                 int16_t* bi = second ? xidx : idx;
-                if (!kTwo)
-                    __syncthreads();                      // the buffer's last reads are done
                 if (active) {
 #pragma unroll
                     for (int s = 0; s < kPer; ++s) {
                         const int i = base + s * kWave + lane;
                         bk[i] = r.key[s];
-                        if constexpr (kIdx)
-                            bi[i] = (int16_t)r.idx[s];
+                        bi[i] = (int16_t)r.idx[s];
                     }
                 }
                 __syncthreads();
@@ -248,9 +238,7 @@ __device__ __forceinline__ void bitonic_regs(uint64_t* key, int16_t* idx, uint64
 #pragma unroll
                     for (int s = 0; s < kPer; ++s) {
                         const int i = base + s * kWave + lane;
-                        int32_t oidx = 0;
-                        if constexpr (kIdx)
-                            oidx = bi[i ^ j];
+                        const int32_t oidx = bi[i ^ j];
                         keep(r, s, bk[i ^ j], oidx, (i & j) == 0, (i & k) == 0);
                     }
                 }
@@ -275,7 +263,7 @@ __device__ __forceinline__ void bitonic_regs(uint64_t* key, int16_t* idx, uint64
     // key / idx were read by the initial loads or by an exchange: wait for every
     // wavefront before overwriting them, unless the last exchange used the
     // second buffer (every read of key / idx then came before its barrier).
-    if (!kTwo || (pass & 1) == 0)
+    if ((pass & 1) == 0)
         __syncthreads();
     if (active) {
 #pragma unroll
@@ -283,8 +271,7 @@ __device__ __forceinline__ void bitonic_regs(uint64_t* key, int16_t* idx, uint64
             const int i = base + s * kWave + lane;
             if (i < n) {
                 key[i] = r.key[s];
-                if constexpr (kIdx)
-                    idx[i] = (int16_t)r.idx[s];
+                idx[i] = (int16_t)r.idx[s];
             }
         }
     }
@@ -413,11 +400,11 @@ template <int kThreads, int kMaxN>
 __device__ __forceinline__ void block_sort(WaveBatchLds<kMaxN>& w, int32_t n)
 {
     if (n <= kThreads / 2)
-        bitonic_regs<kThreads, 1, kThreads / 2, true, true>(w.b.key, w.idx, w.xkey, w.xidx, n);
+        bitonic_regs<kThreads, 1, kThreads / 2>(w.b.key, w.idx, w.xkey, w.xidx, n);
     else if (n <= kThreads)
-        bitonic_regs<kThreads, 1, kThreads, true, true>(w.b.key, w.idx, w.xkey, w.xidx, n);
+        bitonic_regs<kThreads, 1, kThreads>(w.b.key, w.idx, w.xkey, w.xidx, n);
     else
-        bitonic_regs<kThreads, 2, 2 * kThreads, true, true>(w.b.key, w.idx, w.xkey, w.xidx, n);
+        bitonic_regs<kThreads, 2, 2 * kThreads>(w.b.key, w.idx, w.xkey, w.xidx, n);
 }
 
 // Stable rank of each lane's key among run[0 .. len) (an LDS array holding
