@@ -199,11 +199,13 @@ int pkv_scatter_kv(int32_t T, int64_t row_bytes,
  * K/V).  The outputs, status bits and return codes are exactly those of that
  * sequence of calls; later layers reuse each group's slot_mapping with
  * pkv_scatter_kv.  With n <= PKV_STEP_MAX_BATCH and 1 <= num_groups <=
- * PKV_STEP_MAX_GROUPS everything runs in a single kernel launch.  Larger
- * batches with at most PKV_STEP_MAX_GROUPS groups take two kinds of launch:
- * the batch with every group's slots and visible pages, then one scatter per
- * group; more groups enqueue the separate kernels of the sequence.  Either way
- * the results are the same.
+ * PKV_STEP_MAX_GROUPS everything runs in a single kernel launch, except for
+ * decode-like batches (n > PKV_STEP_RANKED_MIN_BATCH and T <= 2 n), where
+ * ordering the batch in every workgroup of that launch costs more than a
+ * second launch.  Those and larger batches with at most PKV_STEP_MAX_GROUPS
+ * groups take two kinds of launch: the batch with every group's slots and
+ * visible pages, then one scatter per group; more groups enqueue the separate
+ * kernels of the sequence.  Either way the results are the same.
  *
  * The schedule and per-request outputs are as for pkv_prepare_batch (R and the
  * token table are shared by all groups).  groups is a HOST array of num_groups
@@ -218,6 +220,7 @@ int pkv_scatter_kv(int32_t T, int64_t row_bytes,
  */
 #define PKV_STEP_MAX_BATCH 512
 #define PKV_STEP_MAX_GROUPS 4
+#define PKV_STEP_RANKED_MIN_BATCH 256
 
 typedef struct pkv_group {
     const int32_t* block_table;

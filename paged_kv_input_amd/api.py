@@ -35,6 +35,7 @@ _I64 = ctypes.c_int64
 
 STEP_MAX_BATCH = 512
 STEP_MAX_GROUPS = 4
+STEP_RANKED_MIN_BATCH = 256
 
 
 class Group(ctypes.Structure):

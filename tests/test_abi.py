@@ -59,6 +59,7 @@ def test_constants_match_binding(lib):
     assert api.MAX_BATCH == m["PKV_MAX_BATCH"]
     assert api.STEP_MAX_BATCH == m["PKV_STEP_MAX_BATCH"]
     assert api.STEP_MAX_GROUPS == m["PKV_STEP_MAX_GROUPS"]
+    assert api.STEP_RANKED_MIN_BATCH == m["PKV_STEP_RANKED_MIN_BATCH"]
     assert ctypes.sizeof(api.Group) == 104
     for name, bit in api.ST_BITS.items():
         assert m["PKV_ST_" + name] == bit

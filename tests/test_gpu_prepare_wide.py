@@ -347,3 +347,30 @@ def test_wide_step_long_requests():
                         rng.integers(0, 1 << 20, (R, L), dtype=np.int32),
                         [workloads.KVGroup(bs, NB, MB, bt, 1, 8, "fp16", k, v)])
     run_and_compare(b, mode="fused")
+
+
+@pytest.mark.parametrize("n,extra", [(257, 0), (384, 0), (512, 0), (384, 384), (300, 301)])
+def test_decode_like_batches(n, extra):
+    """Decode-like batches past 256 requests (T <= 2n: the batch ranked once,
+    then the scatter) and one just past that bound (T = 2n + 1: the single
+    launch); each against the oracle, caches included."""
+    rng = np.random.default_rng(8100 + n + extra)
+    R, L, bs = 3 * n, 512, 16
+    rows = rng.choice(R, n, replace=False).astype(np.int32)
+    counts = np.ones(n, np.int32)
+    counts[rng.choice(n, min(extra, n), replace=False)] += 1
+    counts[0] += max(0, extra - n)                           # T = n + extra
+    completed = np.zeros(R, np.int32)
+    completed[rows] = rng.integers(0, 400, n)
+    MB = L // bs
+    need = int(sum(max(0, -(-(int(completed[r]) + int(c)) // bs) - int(completed[r]) // bs)
+                   for r, c in zip(rows, counts)))
+    NB = need + 13
+    bt = workloads._block_table(rng, R, MB, NB, bs, rows, counts, completed)
+    T = int(counts.sum())
+    k = rng.integers(0, 65535, (T, 2, 64), dtype=np.uint16)
+    v = rng.integers(0, 65535, (T, 2, 64), dtype=np.uint16)
+    b = workloads.Batch(f"decode_like_{n}_{extra}", 8100 + n, rows, counts, completed,
+                        rng.integers(0, 1 << 20, (R, L), dtype=np.int32),
+                        [workloads.KVGroup(bs, NB, MB, bt, 2, 64, "fp16", k, v)])
+    run_and_compare(b, mode="fused")
