@@ -702,7 +702,7 @@ def main():
     # limits, decode-like batches past 256 requests excepted; otherwise it
     # runs k_prepare with the groups' slots and pages, then the scatters (more
     # than four groups: the three calls).
-    decode_like = batch.n > api.STEP_RANKED_MIN_BATCH and T <= 2 * batch.n
+    decode_like = batch.n > api.STEP_RANKED_MIN_BATCH and T <= 4 * batch.n
     one_launch = batch.n <= api.STEP_MAX_BATCH and 1 <= ng <= api.STEP_MAX_GROUPS and not decode_like
     use_fused = fused_ms <= calls_ms
     ms = fused_ms if use_fused else calls_ms

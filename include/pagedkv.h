@@ -200,7 +200,7 @@ int pkv_scatter_kv(int32_t T, int64_t row_bytes,
  * sequence of calls; later layers reuse each group's slot_mapping with
  * pkv_scatter_kv.  With n <= PKV_STEP_MAX_BATCH and 1 <= num_groups <=
  * PKV_STEP_MAX_GROUPS everything runs in a single kernel launch, except for
- * decode-like batches (n > PKV_STEP_RANKED_MIN_BATCH and T <= 2 n), where
+ * decode-like batches (n > PKV_STEP_RANKED_MIN_BATCH and T <= 4 n), where
  * ordering the batch in every workgroup of that launch costs more than a
  * second launch.  Those and larger batches with at most PKV_STEP_MAX_GROUPS
  * groups take two kinds of launch: the batch with every group's slots and

@@ -160,9 +160,9 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
     // decode-like batches past PKV_STEP_RANKED_MIN_BATCH requests: ordering
     // them in every tile workgroup costs more than ranking them once
     // (measured on MI355X: 384 and 512 decodes 13.2 -> 10.8 and 13.6 -> 11.1
-    // us; 256 decodes and every batch of 8192 tokens or more stay faster in
-    // one launch).
-    const bool decode_like = n > PKV_STEP_RANKED_MIN_BATCH && (int64_t)T <= 2 * (int64_t)n;
+    // us, with 4 tokens each 13.8 -> 11.9 and 14.2 -> 12.7 us; 256 decodes and
+    // every batch of 8192 tokens or more stay faster in one launch).
+    const bool decode_like = n > PKV_STEP_RANKED_MIN_BATCH && (int64_t)T <= 4 * (int64_t)n;
     const bool fused = n <= PKV_STEP_MAX_BATCH && num_groups >= 1 &&
                        num_groups <= PKV_STEP_MAX_GROUPS && !decode_like &&
                        pkv::step_grid_threads(n, T, num_groups, groups) < kMaxGridThreads;

@@ -349,17 +349,16 @@ def test_wide_step_long_requests():
     run_and_compare(b, mode="fused")
 
 
-@pytest.mark.parametrize("n,extra", [(257, 0), (384, 0), (512, 0), (384, 384), (300, 301)])
+@pytest.mark.parametrize("n,extra", [(257, 0), (384, 0), (512, 0), (384, 1152), (300, 901)])
 def test_decode_like_batches(n, extra):
-    """Decode-like batches past 256 requests (T <= 2n: the batch ranked once,
-    then the scatter) and one just past that bound (T = 2n + 1: the single
+    """Decode-like batches past 256 requests (T <= 4n: the batch ranked once,
+    then the scatter) and one just past that bound (T = 4n + 1: the single
     launch); each against the oracle, caches included."""
     rng = np.random.default_rng(8100 + n + extra)
     R, L, bs = 3 * n, 512, 16
     rows = rng.choice(R, n, replace=False).astype(np.int32)
-    counts = np.ones(n, np.int32)
-    counts[rng.choice(n, min(extra, n), replace=False)] += 1
-    counts[0] += max(0, extra - n)                           # T = n + extra
+    counts = np.full(n, 1 + extra // n, np.int32)
+    counts[rng.choice(n, extra % n, replace=False)] += 1     # T = n + extra
     completed = np.zeros(R, np.int32)
     completed[rows] = rng.integers(0, 400, n)
     MB = L // bs
