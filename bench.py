@@ -17,8 +17,9 @@ requests and four groups; past that, the batch with every group's slots and
 pages in one launch, then the scatters) and, timed the same way, through the
 three separate calls; value is the faster.  Secondary figures: the
 per-call split of the three calls, the host wall time of one step with the
-schedule uploaded from pinned host memory, a single-step cold measurement (a
-1 GiB rewrite before each step, events around it; median, p10, p90), ceilings to
+schedule uploaded from pinned host memory, flushed single steps (100 of them
+whatever K is: a 1 GiB rewrite before each step, events around it; median,
+p10, p90 and the fraction of peak at the median), ceilings to
 read the step against (a same-byte device copy, the dispatch floor), and the
 calls around the path: the state updates, the paged K/V read, the
 prefix-cache calls and the sliding-window and lookahead variants.
@@ -43,6 +44,7 @@ METRIC = "scheduled tokens/sec (prep+slot_mapping+KV scatter); HBM GB/s % of pea
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
 FLUSH_BYTES = 1 << 30
 ROTATE = 4
+COLD_REPS = 100                # flushed single-step reps, whatever --steps is
 
 
 def algorithmic_bytes(batch):
@@ -492,19 +494,45 @@ def prefix_calls(batch, step, steps, warmup, stream):
     return out
 
 
+def hip_enum_values(enum, header="/opt/rocm/include/hip/hip_runtime_api.h"):
+    """Values of a C enum of the installed HIP header: each enumerator is the
+    previous one plus one unless it is assigned a literal or an earlier name."""
+    with open(header) as f:
+        text = f.read()
+    m = re.search(r"typedef\s+enum\s+" + enum + r"\s*\{(.*?)\}", text, re.S)
+    if m is None:
+        raise ValueError(f"{enum} not found in {header}")
+    body = re.sub(r"//[^\n]*|/\*.*?\*/", "", m.group(1), flags=re.S)
+    if "#" in body:
+        raise ValueError(f"preprocessor lines inside {enum}")
+    vals, nxt = {}, 0
+    for item in body.split(","):
+        item = item.strip()
+        if not item:
+            continue
+        name, _, expr = (x.strip() for x in item.partition("="))
+        if expr:
+            nxt = vals[expr] if expr in vals else int(expr, 0)
+        vals[name] = nxt
+        nxt += 1
+    return vals
+
+
 def device_hbm_peak():
     """HBM peak from the device's own figures (HIP's device attributes, read
     through the HIP runtime): bus width x memory clock x transfers per clock.
     HBM3E pins run at four transfers per reported memory clock (8 Gb/s at
-    2 GHz), so on MI355X this gives 8192 bits x 2 GHz x 4 / 8 = 8.19 TB/s."""
+    2 GHz), so on MI355X this gives 8192 bits x 2 GHz x 4 / 8 = 8.19 TB/s.
+    The attribute numbers come from the installed hip_runtime_api.h."""
     import ctypes
 
     try:
         hip = ctypes.CDLL("libamdhip64.so")
-    except OSError:
+        attrs = hip_enum_values("hipDeviceAttribute_t")
+        bus_attr = attrs["hipDeviceAttributeMemoryBusWidth"]
+        clock_attr = attrs["hipDeviceAttributeMemoryClockRate"]
+    except (OSError, ValueError, KeyError):
         return None
-    # hipDeviceAttribute_t values of this ROCm's hip_runtime_api.h
-    bus_attr, clock_attr = 59, 60
     vals = []
     for attr in (bus_attr, clock_attr):
         v = ctypes.c_int(0)
@@ -675,11 +703,12 @@ def main():
         if i >= args.warmup:
             upload_wall.append((time.perf_counter() - w0) * 1e6)
 
-    # Single cold step: 1 GiB rewrite, then events around one fused step.
+    # Flushed single steps: a 1 GiB rewrite (L2 and the 256 MB Infinity Cache
+    # hold nothing of the step afterwards), then events around one fused step;
+    # COLD_REPS of them whatever --steps is, median and deciles reported.
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
-    cold = []
-    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-    for i in range(reps):
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(COLD_REPS)]
+    for i in range(COLD_REPS):
         flush.fill_(1)
         cev[i][0].record(stream)
         steps[i % ROTATE].run_fused(stream)
@@ -698,17 +727,16 @@ def main():
 
     ab = algorithmic_bytes(batch)
     cb = call_bytes(batch)
-    # pkv_step is one launch (k_step) within the fused kernel's batch and group
-    # limits, decode-like batches past 256 requests excepted; otherwise it
-    # runs k_prepare with the groups' slots and pages, then the scatters (more
-    # than four groups: the three calls).
-    decode_like = batch.n > api.STEP_RANKED_MIN_BATCH and T <= 4 * batch.n
-    one_launch = batch.n <= api.STEP_MAX_BATCH and 1 <= ng <= api.STEP_MAX_GROUPS and not decode_like
+    # The launch plan pkv_step takes for this batch, as the library decides it
+    # (pkv_step_path): one launch (k_step), or the batch with every group's
+    # slots and pages then the scatters, or the separate kernels.
+    plan = steps[0].fused_path()
+    one_launch = plan == api.STEP_ONE_LAUNCH
     use_fused = fused_ms <= calls_ms
     ms = fused_ms if use_fused else calls_ms
     if use_fused and one_launch:
         path = "pkv_step (one launch)"
-    elif use_fused and ng <= api.STEP_MAX_GROUPS:
+    elif use_fused and plan == api.STEP_BATCH_THEN_SCATTER:
         path = "pkv_step (batch with slots and pages, then the scatters)"
     elif use_fused:
         path = "pkv_step (the separate kernels)"
@@ -783,10 +811,13 @@ def main():
                     "synchronize; host clock, one step at a time from an idle GPU",
         },
         "cold_single_step": {
+            "reps": COLD_REPS,
             "ms_median": statistics.median(cold),
             "ms_p10": statistics.quantiles(cold, n=10)[0],
             "ms_p90": statistics.quantiles(cold, n=10)[-1],
-            "note": "1 GiB rewrite before each step; HIP events around the single launch",
+            "note": "1 GiB rewrite before each step (L2 and Infinity Cache flushed); HIP "
+                    "events around the one step, so each rep also carries the event and "
+                    "dispatch latency of a lone launch",
         },
         "roofline": {
             "kernel": kernel,
@@ -798,6 +829,20 @@ def main():
             "traffic": traffic_from_profile(prof_key, args.workload),
             "algorithmic_bytes_per_launch": kbytes,
             "launch_ms": launch_ms,
+            "flushed_step": {
+                "reps": COLD_REPS,
+                "ms_median": statistics.median(cold),
+                "ms_p10": statistics.quantiles(cold, n=10)[0],
+                "ms_p90": statistics.quantiles(cold, n=10)[-1],
+                "frac_median": ab["total"] / (statistics.median(cold) * 1e-3) / 1e9
+                / PEAK_HBM_GBS,
+                "frac_p10_time": ab["total"] / (statistics.quantiles(cold, n=10)[0] * 1e-3)
+                / 1e9 / PEAK_HBM_GBS,
+                "frac_p90_time": ab["total"] / (statistics.quantiles(cold, n=10)[-1] * 1e-3)
+                / 1e9 / PEAK_HBM_GBS,
+                "note": "the whole step's algorithmic bytes over single steps timed after a "
+                        "1 GiB cache flush, HIP events around each (median of the reps)",
+            },
         },
         "cpu_baseline": cpu,
     }

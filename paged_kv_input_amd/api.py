@@ -16,110 +16,20 @@ from typing import Optional
 
 import torch
 
+from . import _abi
+from ._abi import (EALIGN, EHIP, EINVAL, ENOMEM, ENOROWS, EUNSUPPORTED, MAX_BATCH, NO_BLOCK, OK,
+                   ST_BITS, STEP_BATCH_THEN_SCATTER, STEP_MAX_BATCH, STEP_MAX_GROUPS,
+                   STEP_ONE_LAUNCH, STEP_RANKED_MIN_BATCH, STEP_SEPARATE, Group, PagedKVError,
+                   load_library)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.environ.get("PAGEDKV_LIB", os.path.join(_HERE, "libpagedkv.so"))
-
-OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP, ENOROWS, ENOMEM = 0, -1, -2, -3, -4, -5, -6
-ST_BITS = {
-    "BAD_ROW": 0x01, "BAD_COUNT": 0x02, "TOKEN_SUM": 0x04, "POS_OOR": 0x08,
-    "LB_OOR": 0x10, "BLOCK_OOR": 0x20, "SLOT_OOR": 0x40, "BAD_RANGE": 0x80,
-    "TABLE_FULL": 0x100,
-}
-NO_BLOCK = 2**31 - 1        # prefix index: an entry without a block
-MAX_BATCH = 4096
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 
-
-STEP_MAX_BATCH = 512
-STEP_MAX_GROUPS = 4
-STEP_RANKED_MIN_BATCH = 256
-
-
-class Group(ctypes.Structure):
-    """pkv_group: one KV-cache group's inputs and outputs for pkv_step."""
-
-    _fields_ = [
-        ("block_table", _P), ("slot_mapping", _P), ("input_block_tables", _P),
-        ("k", _P), ("v", _P), ("k_cache", _P), ("v_cache", _P),
-        ("k_stride", _I64), ("v_stride", _I64), ("num_slots", _I64), ("row_bytes", _I64),
-        ("MB", _I32), ("block_size", _I32), ("num_blocks", _I32), ("sliding_window", _I32),
-    ]
-
-
-class PagedKVError(RuntimeError):
-    def __init__(self, fn: str, code: int):
-        super().__init__(f"{fn}: {error_string(code)} (code {code})")
-        self.code = code
-
-
-def load_library(path: str = library_path) -> ctypes.CDLL:
-    """Load libpagedkv and declare its signatures.  torch is imported first so
-    the library binds to the HIP runtime torch already loaded."""
-    if not os.path.exists(path):
-        raise ImportError(
-            f"libpagedkv not built at {path}: run `python __graft_entry__.py` or "
-            "`python paged_kv_input_amd/build.py` (no CPU fallback exists)")
-    lib = ctypes.CDLL(path)
-    lib.pkv_prepare_batch.restype = ctypes.c_int
-    lib.pkv_prepare_batch.argtypes = [_I32, _I32, _P, _P, _P, _I32, _P, _I64, _I32,
-                                      _P, _P, _P, _P, _P, _P, _P]
-    lib.pkv_compute_slot_mapping.restype = ctypes.c_int
-    lib.pkv_compute_slot_mapping.argtypes = [_I32, _I32, _P, _P, _P, _P, _P, _I32, _I32,
-                                             _I32, _I32, _I32, _P, _P, _P, _P]
-    lib.pkv_scatter_kv.restype = ctypes.c_int
-    lib.pkv_scatter_kv.argtypes = [_I32, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _P, _P]
-    lib.pkv_step.restype = ctypes.c_int
-    lib.pkv_step.argtypes = [_I32, _I32, _P, _P, _P, _I32, _P, _I64, _I32, _P, _P, _P, _P, _P,
-                             _I32, ctypes.POINTER(Group), _P, _P]
-    lib.pkv_gather_kv.restype = ctypes.c_int
-    lib.pkv_gather_kv.argtypes = [_I32, _P, _P, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _I64,
-                                  _P, _I64, _P, _I64, _P, _P, _P]
-    lib.pkv_window_free.restype = ctypes.c_int
-    lib.pkv_window_free.argtypes = [_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
-    lib.pkv_lookahead_slots.restype = ctypes.c_int
-    lib.pkv_lookahead_slots.argtypes = [_I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P,
-                                        _P]
-    lib.pkv_blocks_needed.restype = ctypes.c_int
-    lib.pkv_blocks_needed.argtypes = [_I32, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P]
-    lib.pkv_hash_blocks.restype = ctypes.c_int
-    lib.pkv_hash_blocks.argtypes = [_I32, _P, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P]
-    lib.pkv_prefix_clear.restype = ctypes.c_int
-    lib.pkv_prefix_clear.argtypes = [_P, _P, _I64, _P]
-    lib.pkv_prefix_lookup.restype = ctypes.c_int
-    lib.pkv_prefix_lookup.argtypes = [_I32, _P, _I32, _P, _I32, _P, _P, _I64, _P, _P, _P, _P]
-    lib.pkv_prefix_insert.restype = ctypes.c_int
-    lib.pkv_prefix_insert.argtypes = [_I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I64, _P,
-                                      _P]
-    lib.pkv_prefix_evict.restype = ctypes.c_int
-    lib.pkv_prefix_evict.argtypes = [_I32, _P, _P, _P, _P, _I64, _P]
-    lib.pkv_add_requests.restype = ctypes.c_int
-    lib.pkv_add_requests.argtypes = [_I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P,
-                                     _I64, _I32, _P, _I32, _P, _P, _P]
-    lib.pkv_append_blocks.restype = ctypes.c_int
-    lib.pkv_append_blocks.argtypes = [_I32, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _P]
-    lib.pkv_advance_state.restype = ctypes.c_int
-    lib.pkv_advance_state.argtypes = [_I32, _P, _P, _P, _I32, _P, _P, _I64, _I32, _P, _P]
-    lib.pkv_row_pool_create.restype = ctypes.c_int
-    lib.pkv_row_pool_create.argtypes = [_I32, ctypes.POINTER(_P)]
-    lib.pkv_row_pool_destroy.restype = None
-    lib.pkv_row_pool_destroy.argtypes = [_P]
-    lib.pkv_row_pool_acquire.restype = ctypes.c_int
-    lib.pkv_row_pool_acquire.argtypes = [_P, _I32, _P]
-    lib.pkv_row_pool_release.restype = ctypes.c_int
-    lib.pkv_row_pool_release.argtypes = [_P, _I32, _P]
-    lib.pkv_row_pool_num_free.restype = _I32
-    lib.pkv_row_pool_num_free.argtypes = [_P]
-    lib.pkv_error_string.restype = ctypes.c_char_p
-    lib.pkv_error_string.argtypes = [ctypes.c_int]
-    lib.pkv_abi_version.restype = ctypes.c_int
-    lib.pkv_abi_version.argtypes = []
-    return lib
-
-
-_lib = load_library()
+_lib = load_library(library_path)
 
 
 def abi_version() -> int:
@@ -127,7 +37,7 @@ def abi_version() -> int:
 
 
 def error_string(code: int) -> str:
-    return _lib.pkv_error_string(code).decode()
+    return _abi.error_string(_lib, code)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -176,7 +86,7 @@ def _prepared(name: str, fn, args: tuple, keep: tuple):
                              f"cuda:{on}")
         rc = fn(*args, s.cuda_stream)
         if rc != OK:
-            raise PagedKVError(name, rc)
+            raise PagedKVError(name, rc, _lib)
 
     launch.__name__ = f"prepared_{name}"
     return launch
@@ -388,7 +298,9 @@ def prepared_step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, complet
                   input_ids: Optional[torch.Tensor] = None,
                   status: Optional[torch.Tensor] = None):
     """Check and marshal the arguments of ``step`` once; return a function
-    ``launch(stream=None)`` that enqueues pkv_step with them.  For loops that
+    ``launch(stream=None)`` that enqueues pkv_step with them.  ``launch.path``
+    is the launch plan pkv_step takes for them (pkv_step_path: STEP_ONE_LAUNCH,
+    STEP_BATCH_THEN_SCATTER or STEP_SEPARATE).  For loops that
     repeat a step on the same buffers (new contents, same tensors), this keeps
     the host's per-step cost to one foreign call.  The tensors must stay alive
     and unmoved while the returned function is used."""
@@ -430,9 +342,15 @@ def prepared_step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, complet
     args = (n, T, _ptr(sched_rows), _ptr(num_scheduled), _ptr(completed), R, _ptr(token_ids),
             stride, L, _ptr(index_mapping), _ptr(query_start_loc), _ptr(seq_lens),
             _ptr(positions), _ptr(input_ids), len(groups), arr, _ptr(status))
-    return _prepared("step", _lib.pkv_step, args,
-                     (sched_rows, num_scheduled, completed, token_ids, index_mapping,
-                      query_start_loc, seq_lens, positions, input_ids, status, list(groups), arr))
+    launch = _prepared("step", _lib.pkv_step, args,
+                       (sched_rows, num_scheduled, completed, token_ids, index_mapping,
+                        query_start_loc, seq_lens, positions, input_ids, status, list(groups),
+                        arr))
+    # the launch plan the library takes for these arguments (pkv_step_path)
+    launch.path = _lib.pkv_step_path(n, T, len(groups), arr)
+    if launch.path < 0:
+        raise PagedKVError("step_path", launch.path, _lib)
+    return launch
 
 
 # -- persistent request state -------------------------------------------------
@@ -551,41 +469,13 @@ def prepared_advance_state(index_mapping: torch.Tensor, seq_lens: torch.Tensor,
                      (index_mapping, seq_lens, sampled, completed, token_ids, status))
 
 
-class RowPool:
+class RowPool(_abi.RowPool):
     """Host-side pool of request_state_index rows (pkv_row_pool_*): ``acquire(m)``
     hands out m free rows (the most recently released first), ``release(rows)``
     takes rows back.  Both raise PagedKVError and change nothing on failure."""
 
     def __init__(self, R: int):
-        h = _P()
-        rc = _lib.pkv_row_pool_create(int(R), ctypes.byref(h))
-        if rc != OK:
-            raise PagedKVError("row_pool_create", rc)
-        self._h = h
-        self.R = int(R)
-
-    def acquire(self, m: int):
-        out = (_I32 * max(int(m), 1))()
-        rc = _lib.pkv_row_pool_acquire(self._h, int(m), out)
-        if rc != OK:
-            raise PagedKVError("row_pool_acquire", rc)
-        return list(out[:int(m)])
-
-    def release(self, rows) -> None:
-        rows = [int(r) for r in rows]
-        arr = (_I32 * max(len(rows), 1))(*rows)
-        rc = _lib.pkv_row_pool_release(self._h, len(rows), arr)
-        if rc != OK:
-            raise PagedKVError("row_pool_release", rc)
-
-    @property
-    def num_free(self) -> int:
-        return int(_lib.pkv_row_pool_num_free(self._h))
-
-    def __del__(self):
-        h, self._h = getattr(self, "_h", None), None
-        if h is not None and _lib is not None:
-            _lib.pkv_row_pool_destroy(h)
+        super().__init__(R, _lib)
 
 
 # -- prefix-cache block hashes and the prefix index ---------------------------

@@ -10,9 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "prepare.hip", "slots.hip", "scatter.hip", "step.hip", "state.hip",
-           "rowpool.hip", "gather.hip", "prefix.hip",
-           "alloc.hip"]
+SOURCES = ["api.cpp", "prepare.hip", "slots.hip", "scatter.hip", "step.hip", "state.hip",
+           "rowpool.cpp", "gather.hip", "prefix.hip", "alloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 instructions are kept out of every kernel (-packed-fp32-ops).

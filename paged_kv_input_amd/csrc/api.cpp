@@ -1,8 +1,10 @@
-// api.hip -- the extern "C" entry points of libpagedkv: argument checks on the
+// api.cpp -- the extern "C" entry points of libpagedkv: argument checks on the
 // host, then stream-ordered launches.  The contract of each entry point
-// (layouts, outputs, error behaviour) is stated in include/pagedkv.h.
+// (layouts, outputs, error behaviour) is stated in include/pagedkv.h.  Host
+// code only: it reaches the GPU through the launchers of launchers.h alone.
 #include <stdint.h>
 
+#include "geometry.h"
 #include "launchers.h"
 
 namespace {
@@ -76,6 +78,31 @@ int check_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride,
     if ((int64_t)T * (row_bytes / 16) / 4 >= kMaxGridThreads)
         return PKV_EUNSUPPORTED;
     return PKV_OK;
+}
+
+// The launch plan of pkv_step (pkv_step_path's value): one launch whenever the
+// batch fits the in-LDS ordering of every workgroup, the group count fits the
+// kernel arguments, the grid fits one dimension and each group's tile rows can
+// be addressed by 32-bit chunk offsets -- except for decode-like batches past
+// PKV_STEP_RANKED_MIN_BATCH requests (T <= 4 n): ordering them in every tile
+// workgroup costs more than ranking them once (measured on MI355X: 384 and 512
+// decodes 13.2 -> 10.8 and 13.6 -> 11.1 us, with 4 tokens each 13.8 -> 11.9
+// and 14.2 -> 12.7 us; 256 decodes and every batch of 8192 tokens or more stay
+// faster in one launch).  Otherwise, up to PKV_STEP_MAX_GROUPS groups: the
+// batch with every group's slots and pages, then the scatters; more groups:
+// the separate kernels.
+int step_path(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups)
+{
+    const bool decode_like = n > PKV_STEP_RANKED_MIN_BATCH && (int64_t)T <= 4 * (int64_t)n;
+    bool fused = n <= PKV_STEP_MAX_BATCH && num_groups >= 1 &&
+                 num_groups <= PKV_STEP_MAX_GROUPS && !decode_like &&
+                 pkv::step_grid_blocks(n, T, num_groups, groups) * pkv::kStepThreads <
+                     kMaxGridThreads;
+    for (int i = 0; fused && i < num_groups; ++i)
+        fused = pkv::step_offsets_fit(groups[i]);
+    if (fused)
+        return PKV_STEP_ONE_LAUNCH;
+    return num_groups <= PKV_STEP_MAX_GROUPS ? PKV_STEP_BATCH_THEN_SCATTER : PKV_STEP_SEPARATE;
 }
 
 }  // namespace
@@ -155,25 +182,15 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
             return rc;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // One launch whenever the batch fits the in-LDS ordering of every
-    // workgroup and the group count fits the kernel arguments, except for
-    // decode-like batches past PKV_STEP_RANKED_MIN_BATCH requests: ordering
-    // them in every tile workgroup costs more than ranking them once
-    // (measured on MI355X: 384 and 512 decodes 13.2 -> 10.8 and 13.6 -> 11.1
-    // us, with 4 tokens each 13.8 -> 11.9 and 14.2 -> 12.7 us; 256 decodes and
-    // every batch of 8192 tokens or more stay faster in one launch).
-    const bool decode_like = n > PKV_STEP_RANKED_MIN_BATCH && (int64_t)T <= 4 * (int64_t)n;
-    const bool fused = n <= PKV_STEP_MAX_BATCH && num_groups >= 1 &&
-                       num_groups <= PKV_STEP_MAX_GROUPS && !decode_like &&
-                       pkv::step_grid_threads(n, T, num_groups, groups) < kMaxGridThreads;
-    if (fused)
+    const int path = step_path(n, T, num_groups, groups);
+    if (path == PKV_STEP_ONE_LAUNCH)
         return from_hip(pkv::launch_step(n, T, sched_rows, num_scheduled, completed, R, token_ids,
                                          token_stride, L, index_mapping, query_start_loc,
                                          seq_lens, positions, input_ids, num_groups, groups,
                                          status, s));
     // Past the one-launch limits: the batch and, for up to PKV_STEP_MAX_GROUPS
     // groups, their slots and pages in one launch; then one scatter per group.
-    const bool with_slots = num_groups <= PKV_STEP_MAX_GROUPS;
+    const bool with_slots = path == PKV_STEP_BATCH_THEN_SCATTER;
     hipError_t e = pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
                                        token_stride, L, index_mapping, query_start_loc, seq_lens,
                                        positions, input_ids, with_slots ? num_groups : 0,
@@ -190,6 +207,13 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
                                 g.v_cache, g.num_slots, g.slot_mapping, status, s);
     }
     return from_hip(e);
+}
+
+int pkv_step_path(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups)
+{
+    if (n < 0 || T < 0 || num_groups < 0 || (num_groups > 0 && groups == nullptr))
+        return PKV_EINVAL;
+    return step_path(n, T, num_groups, groups);
 }
 
 int pkv_gather_kv(int32_t n, const int32_t* seq_lens, const int32_t* query_start_loc,

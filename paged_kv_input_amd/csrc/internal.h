@@ -6,11 +6,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "geometry.h"
 #include "pagedkv.h"
 
 namespace pkv {
-
-constexpr int kWave = 64;
 
 // One DPP move of a 64-bit value (its two 32-bit halves from the same source
 // lane); lanes without a source, or in rows outside kRowMask, get 0.

@@ -1,8 +1,8 @@
 // launchers.h -- host-side launchers of libpagedkv's kernels, called by the C
-// entry points in api.hip.  Not part of the public ABI.
+// entry points in api.cpp.  Not part of the public ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 #include "pagedkv.h"
@@ -35,9 +35,6 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
                        int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
                        int32_t* positions, int32_t* input_ids, int32_t num_groups,
                        const pkv_group* groups, uint32_t* status, hipStream_t stream);
-
-// Work-items of the grid launch_step would launch.
-int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
 
 hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* query_start_loc,
                          int32_t sliding_window, const int32_t* input_block_tables, int32_t MB,

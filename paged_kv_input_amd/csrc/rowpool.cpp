@@ -1,4 +1,4 @@
-// rowpool.hip -- the pool of request_state_index rows (host code only).
+// rowpool.cpp -- the pool of request_state_index rows (host code only).
 //
 // A new request is handed a row of the persistent state and a completed one
 // gives it back to be handed out again, so rows are pooled rather than

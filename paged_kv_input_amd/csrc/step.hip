@@ -33,45 +33,11 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef PKV_STEP_COPY_WAVES
-#define PKV_STEP_COPY_WAVES 3
-#endif
-#ifndef PKV_STEP_UNROLL
-#define PKV_STEP_UNROLL 6
-#endif
-
-#ifndef PKV_STEP_TILE_WGS
-#define PKV_STEP_TILE_WGS 1536             // persistent tile workgroups per step, over all groups
-#endif
-
-constexpr int kCopyThreads = PKV_STEP_COPY_WAVES * kWave; // copy wavefronts
-constexpr int kStepThreads = kCopyThreads + kWave;        // plus one index wavefront
-constexpr int kStepUnroll = PKV_STEP_UNROLL;
-constexpr int kStepChunks = kCopyThreads * kStepUnroll;   // 16-byte chunks per round
-constexpr int kStepMaxTile = 256;                         // tokens per tile, at most
+// Launch geometry (geometry.h): kStepThreads threads per workgroup, kStepChunks
+// 16-byte chunks of K (and of V) per round, tiles of step_tile_tokens() rows.
+constexpr int kCopyThreads = kStepCopyThreads;
 constexpr int kTokensPerLane = kStepMaxTile / kWave;
-constexpr int kPageRows = kCopyThreads / kWave;           // batch rows per page workgroup
-// Persistent tile workgroups: 1536 per step, split evenly over the groups
-// (measured on MI355X: best for a 16-request prefill; for 512 requests in two
-// groups 768 per group beat 512 and 1024; fewer were slower for 72 requests).
-// Tokens per tile: as many whole rows as one round of the copy wavefronts
-// moves, rounded down to a power of two, so that tiles never straddle a block
-// of a power-of-two block size (each tile writes one contiguous run of slots;
-// measured on MI355X: 8 instead of 9 rows of 2 KiB, 52.9 vs 53.9 us at the
-// 32k-token prefill).
-__host__ inline int64_t tile_tokens_for(int64_t chunks_per_row)
-{
-    int64_t tile = 1;
-    while (tile * 2 * chunks_per_row <= kStepChunks)
-        tile *= 2;
-    return tile;
-}
-
-__host__ inline int64_t tile_workgroups(int32_t num_groups)
-{
-    const int64_t per = PKV_STEP_TILE_WGS / (num_groups > 0 ? num_groups : 1);
-    return per > 0 ? per : 1;
-}
+constexpr int kPageRows = kStepPageRows;
 
 struct StepGroup {
     const int32_t* block_table;
@@ -500,14 +466,12 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
         const int64_t cpr = in.row_bytes / 16;
         g.chunks_per_row = (int32_t)cpr;
         g.row_shift = (cpr & (cpr - 1)) == 0 ? __builtin_ctzll((unsigned long long)cpr) : -1;
-        int64_t tile = tile_tokens_for(cpr);
-        if (tile > kStepMaxTile)
-            tile = kStepMaxTile;
+        const int64_t tile = step_tile_tokens(cpr);
         g.tile_tokens = (int32_t)tile;
         g.rounds = (int32_t)((tile * cpr + kStepChunks - 1) / kStepChunks);
         g.first_block = (int32_t)blocks;
         g.tiles = (int32_t)(((int64_t)T + tile - 1) / tile);
-        const int64_t wgs = tile_workgroups(num_groups);
+        const int64_t wgs = step_tile_workgroups(num_groups);
         g.tile_blocks = (int32_t)(g.tiles < wgs ? g.tiles : wgs);
         g.page_blocks = in.input_block_tables != nullptr ? (n + kPageRows - 1) / kPageRows : 0;
         blocks += (int64_t)g.tile_blocks + g.page_blocks;
@@ -528,22 +492,6 @@ hipError_t launch_step(int32_t n, int32_t T, const int32_t* sched_rows,
     else
         k_step<false, true><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
-}
-
-int64_t step_grid_threads(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups)
-{
-    int64_t blocks = 0;
-    for (int i = 0; i < num_groups; ++i) {
-        const int64_t cpr = groups[i].row_bytes / 16;
-        int64_t tile = tile_tokens_for(cpr);
-        if (tile > kStepMaxTile)
-            tile = kStepMaxTile;
-        const int64_t tiles = ((int64_t)T + tile - 1) / tile;
-        blocks += tiles < tile_workgroups(num_groups) ? tiles : tile_workgroups(num_groups);
-        if (groups[i].input_block_tables != nullptr)
-            blocks += (n + kPageRows - 1) / kPageRows;
-    }
-    return (blocks > 0 ? blocks : 1) * kStepThreads;
 }
 
 }  // namespace pkv

@@ -134,9 +134,7 @@ class DeviceStep:
         for gi in range(len(self.groups)):
             self.scatter(gi, stream)
 
-    def run_fused(self, stream=None):
-        """The same step through the single pkv_step entry point (arguments
-        checked and marshalled on the first call, then reused)."""
+    def _prepared_fused(self):
         if self._fused is None:
             self._fused = api.prepared_step(
                 self.sched_rows, self.num_scheduled, self.completed, self.token_ids, self.T,
@@ -148,7 +146,17 @@ class DeviceStep:
                 index_mapping=self.index_mapping, query_start_loc=self.query_start_loc,
                 seq_lens=self.seq_lens, positions=self.positions, input_ids=self.input_ids,
                 status=self.status)
-        self._fused(stream)
+        return self._fused
+
+    def run_fused(self, stream=None):
+        """The same step through the single pkv_step entry point (arguments
+        checked and marshalled on the first call, then reused)."""
+        self._prepared_fused()(stream)
+
+    def fused_path(self) -> int:
+        """The launch plan pkv_step takes for this step (pkv_step_path:
+        api.STEP_ONE_LAUNCH, STEP_BATCH_THEN_SCATTER or STEP_SEPARATE)."""
+        return self._prepared_fused().path
 
     def status_bits(self) -> int:
         return int(self.status.item()) & 0xFFFFFFFF

@@ -1,6 +1,8 @@
 """The C-ABI library on the CPU host: it loads, exports every entry point the
-public header declares, and rejects bad arguments on the host before any HIP
-call (no GPU is touched by these tests)."""
+public header declares with the signature the boundary documents, and rejects
+bad arguments on the host before any HIP call (no GPU is touched by these
+tests).  The argument-check tests take the library as a parameter, so that a
+host-only sanitized build runs them too (tests/test_host_sanitized.py)."""
 import ctypes
 import os
 import re
@@ -31,6 +33,21 @@ def lib():
     return api._lib
 
 
+def test_signatures_match_the_documented_boundary(tmp_path):
+    """Every declaration in the header has the signature listed in
+    tests/abi_signatures.cpp (static_asserts; g++ -fsyntax-only), which
+    includes the departures from the first interface plan: the scatter's row
+    bytes and strides, pkv_error_string, void* streams, the slot mapping's
+    sliding window, and pkv_step_path."""
+    src = os.path.join(ROOT, "tests", "abi_signatures.cpp")
+    r = subprocess.run(["g++", "-std=c++17", "-fsyntax-only", f"-I{os.path.join(ROOT, 'include')}",
+                        src], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    text = open(src).read()
+    checked = set(re.findall(r"PKV_SIG\((pkv_\w+),", text))
+    assert checked == set(declared_functions())
+
+
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == sorted(["pkv_abi_version", "pkv_add_requests", "pkv_advance_state",
@@ -40,7 +57,7 @@ def test_exports_every_declared_symbol(lib):
                      "pkv_lookahead_slots", "pkv_prefix_insert", "pkv_prefix_lookup",
                      "pkv_prepare_batch", "pkv_row_pool_acquire", "pkv_row_pool_create",
                      "pkv_row_pool_destroy", "pkv_row_pool_num_free", "pkv_row_pool_release",
-                     "pkv_scatter_kv", "pkv_step", "pkv_window_free"])
+                     "pkv_scatter_kv", "pkv_step", "pkv_step_path", "pkv_window_free"])
     for name in names:
         assert hasattr(lib, name), name
     so = os.path.join(ROOT, "paged_kv_input_amd", "libpagedkv.so")
@@ -51,7 +68,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_constants_match_binding(lib):
-    from paged_kv_input_amd import api
+    from paged_kv_input_amd import _abi as api
     import oracle
 
     m = declared_macros()
@@ -67,8 +84,10 @@ def test_constants_match_binding(lib):
     for code in ("OK", "EINVAL", "EALIGN", "EUNSUPPORTED", "EHIP", "ENOROWS", "ENOMEM"):
         assert m["PKV_" + code] == getattr(api, code)
     assert m["PKV_ENOROWS"] == oracle.ENOROWS
+    assert (m["PKV_STEP_ONE_LAUNCH"], m["PKV_STEP_BATCH_THEN_SCATTER"], m["PKV_STEP_SEPARATE"]) \
+        == (api.STEP_ONE_LAUNCH, api.STEP_BATCH_THEN_SCATTER, api.STEP_SEPARATE)
     for code in (0, -1, -2, -3, -4, -5, -6, 99):
-        assert api.error_string(code)
+        assert api.error_string(lib, code)
 
 
 def test_host_argument_errors(lib):
@@ -104,7 +123,7 @@ def test_host_argument_errors(lib):
 
 
 def test_step_host_argument_errors(lib):
-    from paged_kv_input_amd import api
+    from paged_kv_input_amd import _abi as api
 
     P = ctypes.c_void_p
     fake = 0x1000
@@ -249,6 +268,17 @@ def test_state_host_argument_errors(lib):
     assert adv(*with_(ok, a1=N)) == -1
     assert adv(*with_(ok, a6=N)) == -1                  # sampled without a token table
     assert adv(*with_(ok, a0=0, a1=N, a2=N)) == 0
+
+
+def test_step_path_argument_errors(lib):
+    from paged_kv_input_amd import _abi as api
+
+    g = (api.Group * 1)(api.Group(row_bytes=2048, k_stride=2048, v_stride=2048))
+    assert lib.pkv_step_path(-1, 0, 1, g) == -1
+    assert lib.pkv_step_path(1, -1, 1, g) == -1
+    assert lib.pkv_step_path(1, 1, -1, g) == -1
+    assert lib.pkv_step_path(1, 1, 1, None) == -1
+    assert lib.pkv_step_path(0, 0, 0, None) == api.STEP_BATCH_THEN_SCATTER
 
 
 def test_binding_rejects_cpu_tensors():

@@ -372,4 +372,10 @@ def test_decode_like_batches(n, extra):
     b = workloads.Batch(f"decode_like_{n}_{extra}", 8100 + n, rows, counts, completed,
                         rng.integers(0, 1 << 20, (R, L), dtype=np.int32),
                         [workloads.KVGroup(bs, NB, MB, bt, 2, 64, "fp16", k, v)])
-    run_and_compare(b, mode="fused")
+    step, _, _ = run_and_compare(b, mode="fused")
+    from paged_kv_input_amd import api
+
+    # which plan ran (the same rule pkv_step routes by; pinned on the CPU in
+    # test_step_plan.py)
+    assert step.fused_path() == (api.STEP_BATCH_THEN_SCATTER if T <= 4 * n
+                                 else api.STEP_ONE_LAUNCH)

@@ -1,24 +1,27 @@
 """The library's host-side row pool against the oracle's (no GPU: the pool is
 host code).  Same random acquire/release sequences, same rows handed out,
-same return codes, same free count after every call."""
+same return codes, same free count after every call.  The tests take the
+library as a parameter, so that a host-only sanitized build runs them too
+(tests/test_host_sanitized.py)."""
 import numpy as np
 import pytest
 
 import oracle
+from paged_kv_input_amd import _abi as api
 
 
 @pytest.fixture(scope="module")
-def api():
-    from paged_kv_input_amd import api
+def lib():
+    from paged_kv_input_amd.api import _lib
 
-    return api
+    return _lib
 
 
 @pytest.mark.parametrize("seed", range(30))
-def test_pool_matches_oracle(api, seed):
+def test_pool_matches_oracle(lib, seed):
     rng = np.random.default_rng(3100 + seed)
     R = int(rng.integers(0, 70))
-    mine, ref = api.RowPool(R), oracle.RowPool(R)
+    mine, ref = api.RowPool(R, lib), oracle.RowPool(R)
     out = []
     for _ in range(60):
         if rng.random() < 0.5:
@@ -46,10 +49,9 @@ def test_pool_matches_oracle(api, seed):
         assert mine.num_free == ref.free == R - len(out)
 
 
-def test_pool_host_argument_errors(api):
+def test_pool_host_argument_errors(lib):
     import ctypes
 
-    lib = api._lib
     h = ctypes.c_void_p()
     assert lib.pkv_row_pool_create(-1, ctypes.byref(h)) == api.EINVAL
     assert lib.pkv_row_pool_create(4, None) == api.EINVAL
@@ -65,10 +67,10 @@ def test_pool_host_argument_errors(api):
     lib.pkv_row_pool_destroy(None)
 
 
-def test_pool_epoch_reuse(api):
+def test_pool_epoch_reuse(lib):
     """Many releases in a row: the duplicate check's per-call marks never
     mistake an old call's row for a duplicate."""
-    pool = api.RowPool(3)
+    pool = api.RowPool(3, lib)
     for _ in range(2000):
         rows = pool.acquire(3)
         pool.release(rows[::-1])
