@@ -119,8 +119,9 @@ def source_digest(paths):
 
 def kernel_sources(kernel):
     csrc = os.path.join(ROOT, "paged_kv_input_amd", "csrc")
-    files = {"step": ["step.hip", "internal.h"], "scatter_kv": ["scatter.hip", "internal.h"],
-             "gather_kv": ["gather.hip", "internal.h"]}
+    files = {"step": ["step.hip", "internal.h", "geometry.h"],
+             "scatter_kv": ["scatter.hip", "internal.h", "geometry.h"],
+             "gather_kv": ["gather.hip", "internal.h", "geometry.h"]}
     return [os.path.join(csrc, f) for f in files[kernel]]
 
 
@@ -586,6 +587,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch a plain 256 MiB device copy (for counter calibration)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time pkv_step alone (warm-up, then K steps back to back) and print a "
+                         "short line; for profiler runs, not a benchmark result")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -647,6 +651,10 @@ def main():
         return e0.elapsed_time(e1) / args.steps, wall * 1e3 / args.steps
 
     fused_ms, fused_wall = back_to_back(lambda s: s.run_fused(stream))
+    if args.step_only:
+        print(json.dumps({"workload": batch.name, "step_only": True, "steps": args.steps,
+                          "ms_per_step": fused_ms, "plan": steps[0].fused_path()}), flush=True)
+        return
     calls_ms, calls_wall = back_to_back(lambda s: s.run(stream))
 
     # The same steps captured once per batch in HIP graphs and replayed back to
