@@ -12,8 +12,10 @@ caches), so consecutive steps never find each other's data in L2 or the
 256 MB Infinity Cache (a cycle touches over 1 GB).  W untimed warm-up steps,
 then exactly K timed steps back to back, bracketed by torch.cuda.synchronize()
 on both sides and by HIP events on the launch stream; ms_per_step is the
-event interval / K.  The step runs through pkv_step (one launch up to 512
-requests and four groups; past that, the batch with every group's slots and
+event interval / K.  The step runs through pkv_step (one launch whenever
+the groups fit: each workgroup ranking its own requests for batches of short
+requests, else each workgroup ordering the batch and writing a tile of flat
+tokens; past 512 longer requests, the batch with every group's slots and
 pages in one launch, then the scatters) and, timed the same way, through the
 three separate calls; value is the faster.  Secondary figures: the
 per-call split of the three calls, the host wall time of one step with the
@@ -120,6 +122,7 @@ def source_digest(paths):
 def kernel_sources(kernel):
     csrc = os.path.join(ROOT, "paged_kv_input_amd", "csrc")
     files = {"step": ["step.hip", "internal.h", "geometry.h"],
+             "ranked_step": ["prepare.hip", "internal.h", "geometry.h"],
              "scatter_kv": ["scatter.hip", "internal.h", "geometry.h"],
              "gather_kv": ["gather.hip", "internal.h", "geometry.h"]}
     return [os.path.join(csrc, f) for f in files[kernel]]
@@ -739,10 +742,12 @@ def main():
     # (pkv_step_path): one launch (k_step), or the batch with every group's
     # slots and pages then the scatters, or the separate kernels.
     plan = steps[0].fused_path()
-    one_launch = plan == api.STEP_ONE_LAUNCH
+    one_launch = plan in (api.STEP_ONE_LAUNCH, api.STEP_RANKED_ONE_LAUNCH)
     use_fused = fused_ms <= calls_ms
     ms = fused_ms if use_fused else calls_ms
-    if use_fused and one_launch:
+    if use_fused and plan == api.STEP_RANKED_ONE_LAUNCH:
+        path = "pkv_step (one launch, each workgroup ranking its own requests)"
+    elif use_fused and one_launch:
         path = "pkv_step (one launch)"
     elif use_fused and plan == api.STEP_BATCH_THEN_SCATTER:
         path = "pkv_step (batch with slots and pages, then the scatters)"
@@ -752,7 +757,10 @@ def main():
         path = "three calls"
     context = context_figures(ab["total"], args.steps, args.warmup, stream)
     context["step_vs_copy"] = context["d2d_copy_same_bytes"]["ms"] / ms
-    if use_fused and one_launch:
+    if use_fused and plan == api.STEP_RANKED_ONE_LAUNCH:
+        kernel, launch_ms, kbytes, prof_key = ("pkv_step (k_prepare with the K/V write)", fused_ms,
+                                               ab["total"], "ranked_step")
+    elif use_fused and one_launch:
         kernel, launch_ms, kbytes, prof_key = "pkv_step (k_step)", fused_ms, ab["total"], "step"
     else:
         kernel = "scatter_kv (k_scatter)"

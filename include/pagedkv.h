@@ -199,15 +199,17 @@ int pkv_scatter_kv(int32_t T, int64_t row_bytes,
  * K/V).  The outputs, status bits and return codes are exactly those of that
  * sequence of calls; later layers reuse each group's slot_mapping with
  * pkv_scatter_kv.  How many launches it enqueues (pkv_step_path below) depends
- * on the sizes only; the results never do.  With n <= PKV_STEP_MAX_BATCH and
- * 1 <= num_groups <= PKV_STEP_MAX_GROUPS everything runs in a single kernel
- * launch, except for decode-like batches (n > PKV_STEP_RANKED_MIN_BATCH and T
- * <= 4 n), where ordering the batch in every workgroup of that launch costs
- * more than a second launch, and for K/V strides so large that one tile's rows
- * span more than 2^32 16-byte chunks.  Those and larger batches with at most
- * PKV_STEP_MAX_GROUPS groups take two kinds of launch: the batch with every
- * group's slots and visible pages, then one scatter per group; more groups
- * enqueue the separate kernels of the sequence.
+ * on the sizes only; the results never do.  With 1 <= num_groups <=
+ * PKV_STEP_MAX_GROUPS everything runs in a single kernel launch: for batches
+ * of at least PKV_STEP_RANKED_MIN_BATCH requests with few tokens each (T <= 8
+ * n, or T <= 16 n past PKV_STEP_MAX_BATCH / 2 requests) one in which each
+ * workgroup ranks its own requests and writes everything of theirs; else, for
+ * n <= PKV_STEP_MAX_BATCH, one in which each workgroup orders the whole batch
+ * and writes a tile of flat tokens -- unless the K/V strides are so large
+ * that one tile's rows span more than 2^32 16-byte chunks.  Larger batches
+ * with at most PKV_STEP_MAX_GROUPS groups take two kinds of launch: the batch
+ * with every group's slots and visible pages, then one scatter per group;
+ * more groups enqueue the separate kernels of the sequence.
  *
  * The schedule and per-request outputs are as for pkv_prepare_batch (R and the
  * token table are shared by all groups).  groups is a HOST array of num_groups
@@ -222,7 +224,7 @@ int pkv_scatter_kv(int32_t T, int64_t row_bytes,
  */
 #define PKV_STEP_MAX_BATCH 512
 #define PKV_STEP_MAX_GROUPS 4
-#define PKV_STEP_RANKED_MIN_BATCH 256
+#define PKV_STEP_RANKED_MIN_BATCH 32
 
 typedef struct pkv_group {
     const int32_t* block_table;
@@ -256,12 +258,16 @@ int pkv_step(int32_t n, int32_t T,
  * enqueueing anything (host code only; it reads n, T, num_groups and, from
  * each descriptor, row_bytes, k_stride, v_stride and whether
  * input_block_tables is NULL, never the memory behind the pointers):
- *   PKV_STEP_ONE_LAUNCH          the whole step in one kernel launch;
+ *   PKV_STEP_ONE_LAUNCH          one launch; each workgroup orders the whole
+ *                                batch and writes a tile of flat tokens;
  *   PKV_STEP_BATCH_THEN_SCATTER  the batch with every group's slots and pages
  *                                in one launch, then one scatter per group;
  *   PKV_STEP_SEPARATE            the kernels of pkv_prepare_batch, then of
  *                                pkv_compute_slot_mapping and pkv_scatter_kv
- *                                per group.
+ *                                per group;
+ *   PKV_STEP_RANKED_ONE_LAUNCH   one launch; each workgroup ranks its own
+ *                                requests and writes their outputs, tokens,
+ *                                slots, pages and K/V rows.
  * The plan changes only how the work is launched ("Contiguous Token Sequence
  * Processing" of the kongchang.com article: the batch is flattened so that a
  * step runs as few launches as possible); the results are the same.  EINVAL
@@ -270,6 +276,7 @@ int pkv_step(int32_t n, int32_t T,
 #define PKV_STEP_ONE_LAUNCH 0
 #define PKV_STEP_BATCH_THEN_SCATTER 1
 #define PKV_STEP_SEPARATE 2
+#define PKV_STEP_RANKED_ONE_LAUNCH 3
 int pkv_step_path(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups);
 
 /*

@@ -21,9 +21,9 @@ MAX_BATCH = 4096
 
 STEP_MAX_BATCH = 512
 STEP_MAX_GROUPS = 4
-STEP_RANKED_MIN_BATCH = 256
+STEP_RANKED_MIN_BATCH = 32
 # pkv_step_path's values: the launch plan of pkv_step
-STEP_ONE_LAUNCH, STEP_BATCH_THEN_SCATTER, STEP_SEPARATE = 0, 1, 2
+STEP_ONE_LAUNCH, STEP_BATCH_THEN_SCATTER, STEP_SEPARATE, STEP_RANKED_ONE_LAUNCH = 0, 1, 2, 3
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32

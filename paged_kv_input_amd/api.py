@@ -19,8 +19,8 @@ import torch
 from . import _abi
 from ._abi import (EALIGN, EHIP, EINVAL, ENOMEM, ENOROWS, EUNSUPPORTED, MAX_BATCH, NO_BLOCK, OK,
                    ST_BITS, STEP_BATCH_THEN_SCATTER, STEP_MAX_BATCH, STEP_MAX_GROUPS,
-                   STEP_ONE_LAUNCH, STEP_RANKED_MIN_BATCH, STEP_SEPARATE, Group, PagedKVError,
-                   load_library)
+                   STEP_ONE_LAUNCH, STEP_RANKED_MIN_BATCH, STEP_RANKED_ONE_LAUNCH, STEP_SEPARATE,
+                   Group, PagedKVError, load_library)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.environ.get("PAGEDKV_LIB", os.path.join(_HERE, "libpagedkv.so"))
@@ -300,7 +300,7 @@ def prepared_step(sched_rows: torch.Tensor, num_scheduled: torch.Tensor, complet
     """Check and marshal the arguments of ``step`` once; return a function
     ``launch(stream=None)`` that enqueues pkv_step with them.  ``launch.path``
     is the launch plan pkv_step takes for them (pkv_step_path: STEP_ONE_LAUNCH,
-    STEP_BATCH_THEN_SCATTER or STEP_SEPARATE).  For loops that
+    STEP_RANKED_ONE_LAUNCH, STEP_BATCH_THEN_SCATTER or STEP_SEPARATE).  For loops that
     repeat a step on the same buffers (new contents, same tensors), this keeps
     the host's per-step cost to one foreign call.  The tensors must stay alive
     and unmoved while the returned function is used."""

@@ -80,22 +80,32 @@ int check_scatter(int32_t T, int64_t row_bytes, const void* k, int64_t k_stride,
     return PKV_OK;
 }
 
-// The launch plan of pkv_step (pkv_step_path's value): one launch whenever the
-// batch fits the in-LDS ordering of every workgroup, the group count fits the
-// kernel arguments, the grid fits one dimension and each group's tile rows can
-// be addressed by 32-bit chunk offsets -- except for decode-like batches past
-// PKV_STEP_RANKED_MIN_BATCH requests (T <= 4 n): ordering them in every tile
-// workgroup costs more than ranking them once (measured on MI355X: 384 and 512
-// decodes 13.2 -> 10.8 and 13.6 -> 11.1 us, with 4 tokens each 13.8 -> 11.9
-// and 14.2 -> 12.7 us; 256 decodes and every batch of 8192 tokens or more stay
-// faster in one launch).  Otherwise, up to PKV_STEP_MAX_GROUPS groups: the
-// batch with every group's slots and pages, then the scatters; more groups:
-// the separate kernels.
+// The launch plan of pkv_step (pkv_step_path's value), measured on MI355X
+// (back-to-back steps, 8 x 128 bf16 rows, block size 16):
+//   - Batches of at least PKV_STEP_RANKED_MIN_BATCH requests with few tokens
+//     each (T <= 8 n, or T <= 16 n past 256 requests), 1-4 groups: one launch
+//     in which each workgroup ranks its own requests and writes their
+//     outputs, tokens, slots, pages and K/V rows -- no workgroup orders the
+//     whole batch.  256 decodes 10.1 -> 7.8 us, 64 decodes 9.9 -> 7.4, 32
+//     requests x 8 tokens 8.5 -> 7.9, 512 x 8 17.1 -> 11.7, 512 x 16 22.0 ->
+//     17.2, 4096 decodes 19.7 -> 18.1; smaller batches stay faster in the
+//     tile launch (2 requests x 4 tokens 6.2 against 7.2, 16 x 16 7.9 against
+//     8.3), and so do longer requests (128 x 16 10.1 against 10.6, 256 x 32
+//     16.5 against 17.0).
+//   - Otherwise one launch of the tile kernel (k_step) whenever the batch fits
+//     the in-LDS ordering of every workgroup, the group count fits the kernel
+//     arguments, the grid fits one dimension and each group's tile rows can
+//     be addressed by 32-bit chunk offsets.
+//   - Otherwise, up to PKV_STEP_MAX_GROUPS groups: the batch with every
+//     group's slots and pages, then the scatters; more groups: the separate
+//     kernels.
 int step_path(int32_t n, int32_t T, int32_t num_groups, const pkv_group* groups)
 {
-    const bool decode_like = n > PKV_STEP_RANKED_MIN_BATCH && (int64_t)T <= 4 * (int64_t)n;
-    bool fused = n <= PKV_STEP_MAX_BATCH && num_groups >= 1 &&
-                 num_groups <= PKV_STEP_MAX_GROUPS && !decode_like &&
+    const bool groups_fit = num_groups >= 1 && num_groups <= PKV_STEP_MAX_GROUPS;
+    const int64_t per = n > PKV_STEP_MAX_BATCH / 2 ? 16 : 8;   // tokens per request, on average
+    if (groups_fit && n >= PKV_STEP_RANKED_MIN_BATCH && (int64_t)T <= per * (int64_t)n)
+        return PKV_STEP_RANKED_ONE_LAUNCH;
+    bool fused = n <= PKV_STEP_MAX_BATCH && groups_fit &&
                  pkv::step_grid_blocks(n, T, num_groups, groups) * pkv::kStepThreads <
                      kMaxGridThreads;
     for (int i = 0; fused && i < num_groups; ++i)
@@ -122,7 +132,7 @@ int pkv_prepare_batch(int32_t n, int32_t T, const int32_t* sched_rows,
         return rc;
     return from_hip(pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
                                         token_stride, L, index_mapping, query_start_loc, seq_lens,
-                                        positions, input_ids, 0, nullptr, status,
+                                        positions, input_ids, 0, nullptr, false, status,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -188,13 +198,18 @@ int pkv_step(int32_t n, int32_t T, const int32_t* sched_rows, const int32_t* num
                                          token_stride, L, index_mapping, query_start_loc,
                                          seq_lens, positions, input_ids, num_groups, groups,
                                          status, s));
+    if (path == PKV_STEP_RANKED_ONE_LAUNCH)
+        return from_hip(pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R,
+                                            token_ids, token_stride, L, index_mapping,
+                                            query_start_loc, seq_lens, positions, input_ids,
+                                            num_groups, groups, true, status, s));
     // Past the one-launch limits: the batch and, for up to PKV_STEP_MAX_GROUPS
     // groups, their slots and pages in one launch; then one scatter per group.
     const bool with_slots = path == PKV_STEP_BATCH_THEN_SCATTER;
     hipError_t e = pkv::launch_prepare(n, T, sched_rows, num_scheduled, completed, R, token_ids,
                                        token_stride, L, index_mapping, query_start_loc, seq_lens,
                                        positions, input_ids, with_slots ? num_groups : 0,
-                                       groups, status, s);
+                                       groups, false, status, s);
     for (int i = 0; !with_slots && e == hipSuccess && i < num_groups; ++i) {
         const pkv_group& g = groups[i];
         e = pkv::launch_slots(n, T, index_mapping, query_start_loc, seq_lens, positions,

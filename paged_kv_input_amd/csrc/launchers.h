@@ -13,14 +13,16 @@ namespace pkv {
 // hipError_t from the launch.
 
 // Batch assembly and flattening; with 1 <= num_groups <= PKV_STEP_MAX_GROUPS
-// also every group's slots and visible pages (those of launch_slots), in the
-// same launch.  num_groups = 0: the batch alone.
+// also every group's slots and visible pages (those of launch_slots), and
+// with with_scatter also every group's K/V write (that of launch_scatter), in
+// the same launch.  num_groups = 0: the batch alone.
 hipError_t launch_prepare(int32_t n, int32_t T, const int32_t* sched_rows,
                           const int32_t* num_scheduled, const int32_t* completed, int32_t R,
                           const int32_t* token_ids, int64_t token_stride, int32_t L,
                           int32_t* index_mapping, int32_t* query_start_loc, int32_t* seq_lens,
                           int32_t* positions, int32_t* input_ids, int32_t num_groups,
-                          const pkv_group* groups, uint32_t* status, hipStream_t stream);
+                          const pkv_group* groups, bool with_scatter, uint32_t* status,
+                          hipStream_t stream);
 
 hipError_t launch_slots(int32_t n, int32_t T, const int32_t* index_mapping,
                         const int32_t* query_start_loc, const int32_t* seq_lens,

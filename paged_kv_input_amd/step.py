@@ -155,7 +155,8 @@ class DeviceStep:
 
     def fused_path(self) -> int:
         """The launch plan pkv_step takes for this step (pkv_step_path:
-        api.STEP_ONE_LAUNCH, STEP_BATCH_THEN_SCATTER or STEP_SEPARATE)."""
+        api.STEP_ONE_LAUNCH, STEP_RANKED_ONE_LAUNCH, STEP_BATCH_THEN_SCATTER or
+        STEP_SEPARATE)."""
         return self._prepared_fused().path
 
     def status_bits(self) -> int:

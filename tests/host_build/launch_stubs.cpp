@@ -28,10 +28,10 @@ namespace pkv {
 
 hipError_t launch_prepare(int32_t, int32_t, const int32_t*, const int32_t*, const int32_t*,
                           int32_t, const int32_t*, int64_t, int32_t, int32_t*, int32_t*, int32_t*,
-                          int32_t*, int32_t*, int32_t num_groups, const pkv_group*, uint32_t*,
-                          hipStream_t)
+                          int32_t*, int32_t*, int32_t num_groups, const pkv_group*,
+                          bool with_scatter, uint32_t*, hipStream_t)
 {
-    return logged(("prepare+" + std::to_string(num_groups)).c_str());
+    return logged(("prepare+" + std::to_string(num_groups) + (with_scatter ? "+kv" : "")).c_str());
 }
 
 hipError_t launch_slots(int32_t, int32_t, const int32_t*, const int32_t*, const int32_t*,

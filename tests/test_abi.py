@@ -84,8 +84,10 @@ def test_constants_match_binding(lib):
     for code in ("OK", "EINVAL", "EALIGN", "EUNSUPPORTED", "EHIP", "ENOROWS", "ENOMEM"):
         assert m["PKV_" + code] == getattr(api, code)
     assert m["PKV_ENOROWS"] == oracle.ENOROWS
-    assert (m["PKV_STEP_ONE_LAUNCH"], m["PKV_STEP_BATCH_THEN_SCATTER"], m["PKV_STEP_SEPARATE"]) \
-        == (api.STEP_ONE_LAUNCH, api.STEP_BATCH_THEN_SCATTER, api.STEP_SEPARATE)
+    assert (m["PKV_STEP_ONE_LAUNCH"], m["PKV_STEP_BATCH_THEN_SCATTER"], m["PKV_STEP_SEPARATE"],
+            m["PKV_STEP_RANKED_ONE_LAUNCH"]) \
+        == (api.STEP_ONE_LAUNCH, api.STEP_BATCH_THEN_SCATTER, api.STEP_SEPARATE,
+            api.STEP_RANKED_ONE_LAUNCH)
     for code in (0, -1, -2, -3, -4, -5, -6, 99):
         assert api.error_string(lib, code)
 

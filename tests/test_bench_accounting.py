@@ -59,6 +59,7 @@ def test_traffic_guard(tmp_path, monkeypatch):
     csrc.mkdir(parents=True)
     (csrc / "step.hip").write_text("kernel A\n")
     (csrc / "internal.h").write_text("helpers\n")
+    (csrc / "geometry.h").write_text("launch geometry\n")
     (tmp_path / "profiles").mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     digest = bench.source_digest(bench.kernel_sources("step"))

@@ -351,9 +351,8 @@ def test_wide_step_long_requests():
 
 @pytest.mark.parametrize("n,extra", [(257, 0), (384, 0), (512, 0), (384, 1152), (300, 901)])
 def test_decode_like_batches(n, extra):
-    """Decode-like batches past 256 requests (T <= 4n: the batch ranked once,
-    then the scatter) and one just past that bound (T = 4n + 1: the single
-    launch); each against the oracle, caches included."""
+    """Decode-like batches past 256 requests, with 1-4 tokens per request (the
+    request-ranked single launch); each against the oracle, caches included."""
     rng = np.random.default_rng(8100 + n + extra)
     R, L, bs = 3 * n, 512, 16
     rows = rng.choice(R, n, replace=False).astype(np.int32)
@@ -376,6 +375,7 @@ def test_decode_like_batches(n, extra):
     from paged_kv_input_amd import api
 
     # which plan ran (the same rule pkv_step routes by; pinned on the CPU in
-    # test_step_plan.py)
-    assert step.fused_path() == (api.STEP_BATCH_THEN_SCATTER if T <= 4 * n
+    # test_step_plan.py): past 256 requests with up to 16 tokens each, the
+    # request-ranked single launch
+    assert step.fused_path() == (api.STEP_RANKED_ONE_LAUNCH if T <= 16 * n
                                  else api.STEP_ONE_LAUNCH)

@@ -1,5 +1,5 @@
 """pkv_step's launch plan on the CPU: pkv_step_path's value at the edges of
-each rule (batch size, decode-like batches, group count, 32-bit tile
+each rule (batch size, tokens per request, group count, 32-bit tile
 offsets), and -- through a host-only build whose launchers only log (see
 host_lib.py) -- the launches pkv_step really enqueues for the same arguments.
 Both paths give the same results (the GPU tests compare them); these tests pin
@@ -26,28 +26,41 @@ def groups(num, row_bytes=2048, k_stride=None, v_stride=None, pages=True):
 
 
 # (n, T, num_groups, group kwargs, expected plan).  The rules, restated:
-# one launch for 1..4 groups and n <= 512, unless n > 256 and T <= 4 n
-# (decode-like), or a tile's rows span more than 2^32 16-byte chunks of K or
-# V; otherwise the batch with slots and pages then the scatters for <= 4
-# groups, else the separate kernels.
-ONE, BATCH, SEP = _abi.STEP_ONE_LAUNCH, _abi.STEP_BATCH_THEN_SCATTER, _abi.STEP_SEPARATE
+# with 1..4 groups, n >= 32 and T <= 8 n (T <= 16 n past 256 requests): the
+# request-ranked single launch; otherwise the tile launch for n <= 512, unless
+# a tile's rows span more than 2^32 16-byte chunks of K or V; otherwise the
+# batch with slots and pages then the scatters for <= 4 groups, else the
+# separate kernels.
+ONE, BATCH, SEP, RANKED = (_abi.STEP_ONE_LAUNCH, _abi.STEP_BATCH_THEN_SCATTER,
+                           _abi.STEP_SEPARATE, _abi.STEP_RANKED_ONE_LAUNCH)
 # 2 KiB rows: 8-token tiles, 7 rows past the first; 16 B rows: 256-token tiles
 S2K = (2**32 - 128) // 7            # largest 16-byte stride that fits with 2 KiB rows
 S16 = (2**32 - 1) // 255            # and with 16-byte rows
 CASES = [
-    (256, 256, 1, {}, ONE),                      # 256 decodes: one launch
-    (257, 257, 1, {}, BATCH),                    # 257 decodes: ranked two-launch plan
-    (300, 1200, 1, {}, BATCH),                   # T = 4 n: still decode-like
-    (300, 1201, 1, {}, ONE),                     # T = 4 n + 1: one launch
-    (512, 8192, 1, {}, ONE),
-    (513, 8192, 1, {}, BATCH),                   # past PKV_STEP_MAX_BATCH
-    (4096, 4096, 2, {}, BATCH),
+    (31, 31, 1, {}, ONE),                        # 31 decodes: the tile launch
+    (32, 32, 1, {}, RANKED),                     # 32 decodes: ranked
+    (32, 256, 1, {}, RANKED),                    # T = 8 n
+    (32, 257, 1, {}, ONE),                       # T = 8 n + 1
+    (256, 2048, 1, {}, RANKED),
+    (256, 2049, 1, {}, ONE),                     # 8 n + 1 at 256 requests
+    (257, 4112, 1, {}, RANKED),                  # T = 16 n past 256 requests
+    (257, 4113, 1, {}, ONE),
+    (512, 8192, 1, {}, RANKED),
+    (512, 8193, 1, {}, ONE),
+    (513, 16 * 513, 1, {}, RANKED),
+    (513, 16 * 513 + 1, 1, {}, BATCH),           # past PKV_STEP_MAX_BATCH, longer requests
+    (4096, 4096, 2, {}, RANKED),
+    (4096, 65536, 4, {}, RANKED),                # 16 tokens each, four groups
+    (4096, 65537, 4, {}, BATCH),
+    (4096, 4096, 5, {}, SEP),                    # past PKV_STEP_MAX_GROUPS
+    (256, 256, 0, {}, BATCH),                    # no group: the batch alone
     (16, 32768, 4, {}, ONE),
-    (16, 32768, 5, {}, SEP),                     # past PKV_STEP_MAX_GROUPS
-    (16, 32768, 0, {}, BATCH),                   # no group: the batch alone
+    (16, 32768, 5, {}, SEP),
+    (16, 32768, 0, {}, BATCH),
     (16, 32768, 1, dict(k_stride=16 * S2K), ONE),
     (16, 32768, 1, dict(k_stride=16 * (S2K + 1)), BATCH),
     (16, 32768, 1, dict(v_stride=16 * (S2K + 1)), BATCH),
+    (64, 64, 1, dict(k_stride=16 * (S2K + 1)), RANKED),  # 64-bit offsets in the ranked launch
     (16, 32768, 1, dict(row_bytes=16, k_stride=16 * S16, v_stride=16 * S16), ONE),
     (16, 32768, 1, dict(row_bytes=16, v_stride=16 * (S16 + 1)), BATCH),
     (2, 9, 1, dict(pages=False), ONE),
@@ -72,6 +85,8 @@ def check_routing(lib):
         assert rc == 0, (n, T, ng, kw, rc)
         if want == ONE:
             expect = ["step"]
+        elif want == RANKED:
+            expect = [f"prepare+{ng}+kv"]
         elif want == BATCH:
             expect = [f"prepare+{ng}"] + ["scatter"] * ng
         else:
