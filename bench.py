@@ -22,7 +22,7 @@ per-call split of the three calls, the host wall time of one step with the
 schedule uploaded from pinned host memory, flushed single steps (100 of them
 whatever K is: a 1 GiB rewrite before each step, events around it; median,
 p10, p90 and the fraction of peak at the median), ceilings to
-read the step against (a same-byte device copy, the dispatch floor), and the
+read the step against (a same-byte device copy, the rate at which the host issues one-lane launches), and the
 calls around the path: the state updates, the paged K/V read, the
 prefix-cache calls and the sliding-window and lookahead variants.
 
@@ -551,11 +551,11 @@ def device_hbm_peak():
 def context_figures(step_bytes, steps, warmup, stream):
     """Ceilings to read the step against (not targets): a device-to-device copy
     moving the same bytes (half read, half written; torch's copy kernel, four
-    rotating buffer pairs, back to back) and the dispatch floor of a one-lane
-    kernel launched back to back."""
+    rotating buffer pairs, back to back) and the rate at which the host issues
+    a one-lane kernel launched back to back."""
     import torch
 
-    half = step_bytes // 2
+    half = int(round(step_bytes)) // 2
     src = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(ROTATE)]
     dst = [torch.empty_like(x) for x in src]
 
@@ -635,7 +635,11 @@ def main():
         torch.cuda.synchronize()
 
     ng = len(batch.groups)
-    T = batch.T
+    # Every timed loop cycles through the ROTATE batches evenly, so the tokens
+    # and bytes of a step are their means over the rotation (the batches'
+    # token counts differ where the workload draws them).
+    T = statistics.fmean(b.T for b in batches)
+    T = int(T) if T == int(T) else T
 
     def back_to_back(run):
         for i in range(args.warmup):
@@ -678,7 +682,7 @@ def main():
     # Per-call split of the three calls (events between the calls add their own
     # overhead; for attribution only).
     split = {"prepare_batch": [], "compute_slot_mapping": [], "scatter_kv": []}
-    reps = min(args.steps, 60)
+    reps = max(ROTATE, min(args.steps, 60) // ROTATE * ROTATE)   # whole rotations
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
     for i in range(reps):
         s, e = steps[i % ROTATE], marks[i]
@@ -736,8 +740,9 @@ def main():
     gather = gather_calls(batch, steps, args.steps, args.warmup, stream, args.workload)
     prefix = prefix_calls(batch, steps[0], args.steps, args.warmup, stream)
 
-    ab = algorithmic_bytes(batch)
-    cb = call_bytes(batch)
+    ab = {"total": statistics.fmean(algorithmic_bytes(b)["total"] for b in batches)}
+    cbs = [call_bytes(b) for b in batches]
+    cb = {k: statistics.fmean(c[k] for c in cbs) for k in cbs[0]}
     # The launch plan pkv_step takes for this batch, as the library decides it
     # (pkv_step_path): one launch (k_step), or the batch with every group's
     # slots and pages then the scatters, or the separate kernels.
@@ -765,7 +770,8 @@ def main():
     else:
         kernel = "scatter_kv (k_scatter)"
         launch_ms = statistics.fmean(split["scatter_kv"]) / ng
-        kbytes = statistics.fmean(scatter_bytes_per_launch(batch, gi) for gi in range(ng))
+        kbytes = statistics.fmean(scatter_bytes_per_launch(b, gi) for b in batches
+                                  for gi in range(ng))
         prof_key = "scatter_kv"
     achieved = kbytes / (launch_ms * 1e-3) / 1e9
 
