@@ -405,8 +405,10 @@ hipError_t launch_gather(int32_t n, const int32_t* seq_lens, const int32_t* quer
     // Tiles as long as kTile rows, shortened (by halves) while the output has
     // fewer than PKV_GATHER_TARGET_TILES of them, so a short read still spreads
     // over the whole chip; but never below PKV_GATHER_MIN_TILE rows nor below
-    // the rows one round of the copy wavefronts moves (64 rows of 256 bytes:
-    // measured on MI355X, 11.5 instead of 13.5-15 us for a 32k-row read).
+    // the largest power of two of rows that one round of the copy wavefronts
+    // moves (128 rows of 256 bytes: a 32k-row read of such rows is one tile per
+    // workgroup, 9.4 us on MI355X; with tiles of 16 rows such reads took
+    // 13.5-15 us).
     int min_tile = PKV_GATHER_MIN_TILE;
     while (min_tile < kTile && (int64_t)min_tile * 2 * a.chunks_per_row <= kChunks)
         min_tile <<= 1;

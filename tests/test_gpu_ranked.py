@@ -207,3 +207,32 @@ def test_ranked_strided_kv_and_short_cache():
     assert_equal("k_cache", kc.cpu().numpy(), ko)
     assert_equal("v_cache", vc.cpu().numpy(), vo)
     assert int(st.item()) == prep["status"] | want["status"] | sst
+
+
+@pytest.mark.parametrize("extra_groups", [0, 3])
+def test_ranked_maximum_batch(extra_groups):
+    """The plan's largest case: 4096 requests of 16 tokens each (T = 16 n,
+    65536 tokens, the ranked rule's edge) in 1 or 4 groups with block sizes 16,
+    1, 64 and 3 and rows of 256, 16, 48 and 256 bytes; histories up to 4000
+    tokens, so block-table rows of up to 4016 entries at block size 1."""
+    rng = np.random.default_rng(4242 + extra_groups)
+    n, R = 4096, 6000
+    rows = rng.choice(R, n, replace=False).astype(np.int32)
+    counts = np.full(n, 16, np.int32)
+    completed = np.zeros(R, np.int32)
+    completed[rows] = rng.integers(0, 4000, n)
+    T = int(counts.sum())
+    L = 4016
+    groups = []
+    for bs, (H, D) in [(16, (1, 128)), (1, (1, 8)), (64, (3, 8)), (3, (2, 64))][:1 + extra_groups]:
+        MB = -(-L // bs)
+        need = int(sum(-(-(int(completed[r]) + 16) // bs) - int(completed[r]) // bs for r in rows))
+        NB = need + 17
+        bt = workloads._block_table(rng, R, MB, NB, bs, rows, counts, completed)
+        k = rng.integers(0, 65535, (T, H, D), dtype=np.uint16)
+        v = rng.integers(0, 65535, (T, H, D), dtype=np.uint16)
+        groups.append(workloads.KVGroup(bs, NB, MB, bt, H, D, "bf16", k, v))
+    tok = rng.integers(0, 1 << 20, (R, L), dtype=np.int32)
+    b = workloads.Batch(f"ranked_max_{1 + extra_groups}g", 4242, rows, counts, completed, tok,
+                        groups)
+    run_ranked(b, [0] * len(groups))
