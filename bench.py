@@ -730,7 +730,18 @@ def main():
         cev[i][1].record(stream)
     torch.cuda.synchronize()
     cold = [e[0].elapsed_time(e[1]) for e in cev]
-    del flush
+    # The same protocol around a one-element torch kernel: the event and
+    # dispatch latency that every flushed rep above also carries.
+    one = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(COLD_REPS)]
+    for i in range(COLD_REPS):
+        flush.fill_(1)
+        lev[i][0].record(stream)
+        one.add_(1)
+        lev[i][1].record(stream)
+    torch.cuda.synchronize()
+    lone = [e[0].elapsed_time(e[1]) for e in lev]
+    del flush, one
 
     for s in steps:
         if s.status_bits() != 0:
@@ -837,9 +848,11 @@ def main():
             "ms_median": statistics.median(cold),
             "ms_p10": statistics.quantiles(cold, n=10)[0],
             "ms_p90": statistics.quantiles(cold, n=10)[-1],
+            "lone_tiny_kernel_ms_median": statistics.median(lone),
             "note": "1 GiB rewrite before each step (L2 and Infinity Cache flushed); HIP "
                     "events around the one step, so each rep also carries the event and "
-                    "dispatch latency of a lone launch",
+                    "dispatch latency of a lone launch (lone_tiny_kernel: the same protocol "
+                    "around a one-element kernel)",
         },
         "roofline": {
             "kernel": kernel,
@@ -862,8 +875,11 @@ def main():
                 / 1e9 / PEAK_HBM_GBS,
                 "frac_p90_time": ab["total"] / (statistics.quantiles(cold, n=10)[-1] * 1e-3)
                 / 1e9 / PEAK_HBM_GBS,
+                "lone_tiny_kernel_ms_median": statistics.median(lone),
                 "note": "the whole step's algorithmic bytes over single steps timed after a "
-                        "1 GiB cache flush, HIP events around each (median of the reps)",
+                        "1 GiB cache flush, HIP events around each (median of the reps); "
+                        "lone_tiny_kernel: the same protocol around a one-element kernel, "
+                        "the event and dispatch latency each rep carries",
             },
         },
         "cpu_baseline": cpu,
