@@ -31,14 +31,16 @@ namespace {
 constexpr uint64_t kFnvBasis = 14695981039346656037ull;
 constexpr uint64_t kFnvPrime = 1099511628211ull;
 constexpr int32_t kNoBlock = INT32_MAX;
-// One workgroup per request.  Hashing is bound by the byte-serial FNV
-// multiplies, so 256 threads; the index probes are bound by memory latency, so
-// 1024 threads take the longest request's blocks in fewer rounds (measured on
-// MI355X, 512 requests of up to 1056 blocks: lookup 16 -> 12 us, insert
-// 19.6 -> 16.6 us; 1024-thread hashing was slower).
-constexpr int kHashThreads = 256;
-constexpr int kLookupThreads = 1024;
-constexpr int kInsertThreads = 1024;
+// One workgroup per request, of as many threads as the block-table width
+// (MB, the most blocks a request can have) needs, at least one wavefront and
+// at most: 256 for hashing, which is bound by the byte-serial FNV multiplies;
+// 1024 for the index probes, which are bound by memory latency, so that a long
+// request's blocks take fewer rounds (measured on MI355X, 512 requests of up
+// to 1056 blocks: lookup 16 -> 12 us, insert 19.6 -> 16.6 us; 1024-thread
+// hashing was slower).  Narrow tables get narrow workgroups, so that more
+// requests are resident at once.
+constexpr int kHashMaxThreads = 256;
+constexpr int kIndexMaxThreads = 1024;
 constexpr int kFlatThreads = 256;         // flat grids: eviction, clearing
 
 __device__ inline uint64_t fnv_byte(uint64_t h, uint32_t byte)
@@ -77,6 +79,7 @@ __device__ inline void wave_affine_scan(uint64_t& a, uint64_t& b)
     }
 }
 
+template <int kHashThreads>
 __global__ __launch_bounds__(kHashThreads) void k_hash_blocks(
     const int32_t* __restrict__ tokens, int64_t total, const int64_t* __restrict__ starts,
     const int32_t* __restrict__ lengths, int32_t block_size, int32_t MB,
@@ -171,6 +174,7 @@ __device__ inline int64_t probe(const uint64_t* keys, int64_t capacity, uint64_t
     return -1;
 }
 
+template <int kLookupThreads>
 __global__ __launch_bounds__(kLookupThreads) void k_prefix_lookup(
     const uint64_t* __restrict__ hashes, int32_t MB, const int32_t* __restrict__ lengths,
     int32_t block_size, const uint64_t* __restrict__ keys, const int32_t* __restrict__ vals,
@@ -218,6 +222,7 @@ __global__ __launch_bounds__(kLookupThreads) void k_prefix_lookup(
     report_status(status, flags);
 }
 
+template <int kInsertThreads>
 __global__ __launch_bounds__(kInsertThreads) void k_prefix_insert(
     const uint64_t* __restrict__ hashes, int32_t MB, const int32_t* __restrict__ lo,
     const int32_t* __restrict__ hi, const int32_t* __restrict__ rows,
@@ -292,6 +297,16 @@ __global__ __launch_bounds__(kFlatThreads) void k_prefix_clear(uint64_t* __restr
     }
 }
 
+// Threads of a request's workgroup: the smallest power of two from one
+// wavefront up to `most` that covers MB blocks.
+__host__ inline int request_threads(int32_t MB, int most)
+{
+    int t = kWave;
+    while (t < most && t < MB)
+        t *= 2;
+    return t;
+}
+
 }  // namespace
 
 hipError_t launch_hash_blocks(int32_t m, const int32_t* tokens, int64_t total,
@@ -301,8 +316,16 @@ hipError_t launch_hash_blocks(int32_t m, const int32_t* tokens, int64_t total,
 {
     if (m == 0)
         return hipSuccess;
-    k_hash_blocks<<<dim3((unsigned)m), dim3(kHashThreads), 0, stream>>>(
-        tokens, total, starts, lengths, block_size, MB, hashes, num_full, status);
+#define PKV_HASH_LAUNCH(W)                                                                         \
+    k_hash_blocks<W><<<dim3((unsigned)m), dim3(W), 0, stream>>>(tokens, total, starts, lengths,    \
+                                                                block_size, MB, hashes, num_full, \
+                                                                status)
+    switch (request_threads(MB, kHashMaxThreads)) {
+    case 64: PKV_HASH_LAUNCH(64); break;
+    case 128: PKV_HASH_LAUNCH(128); break;
+    default: PKV_HASH_LAUNCH(256); break;
+    }
+#undef PKV_HASH_LAUNCH
     return hipGetLastError();
 }
 
@@ -313,8 +336,17 @@ hipError_t launch_prefix_lookup(int32_t m, const uint64_t* hashes, int32_t MB,
 {
     if (m == 0)
         return hipSuccess;
-    k_prefix_lookup<<<dim3((unsigned)m), dim3(kLookupThreads), 0, stream>>>(
-        hashes, MB, lengths, block_size, keys, vals, capacity, hit_blocks, num_computed, status);
+#define PKV_LOOKUP_LAUNCH(W)                                                                       \
+    k_prefix_lookup<W><<<dim3((unsigned)m), dim3(W), 0, stream>>>(                                \
+        hashes, MB, lengths, block_size, keys, vals, capacity, hit_blocks, num_computed, status)
+    switch (request_threads(MB, kIndexMaxThreads)) {
+    case 64: PKV_LOOKUP_LAUNCH(64); break;
+    case 128: PKV_LOOKUP_LAUNCH(128); break;
+    case 256: PKV_LOOKUP_LAUNCH(256); break;
+    case 512: PKV_LOOKUP_LAUNCH(512); break;
+    default: PKV_LOOKUP_LAUNCH(1024); break;
+    }
+#undef PKV_LOOKUP_LAUNCH
     return hipGetLastError();
 }
 
@@ -326,8 +358,17 @@ hipError_t launch_prefix_insert(int32_t m, const uint64_t* hashes, int32_t MB, c
 {
     if (m == 0)
         return hipSuccess;
-    k_prefix_insert<<<dim3((unsigned)m), dim3(kInsertThreads), 0, stream>>>(
-        hashes, MB, lo, hi, rows, block_table, R, keys, vals, capacity, status);
+#define PKV_INSERT_LAUNCH(W)                                                                       \
+    k_prefix_insert<W><<<dim3((unsigned)m), dim3(W), 0, stream>>>(                                \
+        hashes, MB, lo, hi, rows, block_table, R, keys, vals, capacity, status)
+    switch (request_threads(MB, kIndexMaxThreads)) {
+    case 64: PKV_INSERT_LAUNCH(64); break;
+    case 128: PKV_INSERT_LAUNCH(128); break;
+    case 256: PKV_INSERT_LAUNCH(256); break;
+    case 512: PKV_INSERT_LAUNCH(512); break;
+    default: PKV_INSERT_LAUNCH(1024); break;
+    }
+#undef PKV_INSERT_LAUNCH
     return hipGetLastError();
 }
 
