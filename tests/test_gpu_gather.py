@@ -222,3 +222,44 @@ def test_full_size_prefill():
     """The 32k-token prefill at full size, every row compared (no history:
     every row read is one the step wrote)."""
     step_then_gather(workloads.make("prefill_16x2048"), patterned=False)
+
+
+@pytest.mark.parametrize("chunks,window", [(128, 0), (130, 0), (128, 2000), (130, 2000), (24, 0)])
+def test_long_reads(chunks, window):
+    """Reads long enough for tiles of several copy rounds, which move all of K,
+    then all of V (about 130k rows of 2 KiB, or 2080 B, plus a read of 384-byte
+    rows whose tiles stay one round): every row against the oracle, with and
+    without a sliding window (query counts of 1-40 tokens, holes before the
+    window's pages)."""
+    import torch
+
+    rng = np.random.default_rng(7300 + chunks + window)
+    n, bs = 64, 16
+    sl = rng.integers(1000, 3100, n).astype(np.int32)
+    MB = int(sl.max()) // bs + 1
+    NB = n * MB + 5
+    ibt = rng.permutation(NB)[: n * MB].reshape(n, MB).astype(np.int32)
+    counts = rng.integers(1, 41, n).astype(np.int32)
+    qsl = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    if window:
+        first = np.maximum(0, sl.astype(np.int64) - counts - window + 1) // bs
+        for b in range(n):
+            ibt[b, : first[b]] = -1                   # blocks freed behind the window
+    row = (chunks * 8,)
+    (kd, kc), (vd, vc) = pattern(NB * bs, row, 21 + chunks), pattern(NB * bs, row, 121 + chunks)
+    want = oracle.gather_kv(sl, ibt, bs, NB, kc, vc, query_start_loc=qsl, sliding_window=window)
+    rows = int(want["kv_start"][-1])
+    say(f"[case] gather long chunks={chunks} window={window} rows={rows}")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()   # noqa: E731
+    k_out = torch.full((rows, *row), SENTINEL16, dtype=torch.int16, device="cuda")
+    v_out = torch.full_like(k_out, SENTINEL16)
+    kv_start = torch.full((n + 1,), -7, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    from paged_kv_input_amd import api
+    api.gather_kv(up(sl), up(ibt), bs, NB, kd, vd, k_out=k_out, v_out=v_out, kv_start=kv_start,
+                  status=status, query_start_loc=up(qsl), sliding_window=window)
+    torch.cuda.synchronize()
+    assert_equal("kv_start", kv_start.cpu().numpy(), want["kv_start"])
+    assert int(status.item()) == want["status"] == 0
+    assert_equal("k_out", k_out.cpu().numpy().view(np.uint16), want["k"])
+    assert_equal("v_out", v_out.cpu().numpy().view(np.uint16), want["v"])
