@@ -522,28 +522,4 @@ __device__ inline void wave_finish(WaveBatchLds<kMaxN>& w, const WaveGather<kMax
     }
 }
 
-#ifndef PKV_XCD_REMAP
-#define PKV_XCD_REMAP 0
-#endif
-constexpr int kXcds = 8;   // MI355X: 8 accelerator dies, workgroups dealt round-robin
-
-// Tile of workgroup `blk` among `tiles` tiles so that each XCD (which receives
-// workgroups blk = x, x + 8, x + 16, ...) walks one contiguous range of tiles:
-// neighbouring tiles share cache lines, block-table words and destination
-// pages, and now share them inside one XCD's L2 and translation caches.  A
-// bijection on [0, tiles) for any tile count.
-__device__ inline int64_t xcd_tile(int64_t blk, int64_t tiles)
-{
-#if PKV_XCD_REMAP
-    const int64_t x = blk % kXcds;
-    const int64_t k = blk / kXcds;
-    const int64_t q = tiles / kXcds;
-    const int64_t r = tiles % kXcds;
-    return x * q + (x < r ? x : r) + k;
-#else
-    (void)tiles;
-    return blk;
-#endif
-}
-
 }  // namespace pkv
