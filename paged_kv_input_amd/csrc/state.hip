@@ -23,8 +23,13 @@
 namespace pkv {
 namespace {
 
-constexpr int kAddThreads = 256;
-constexpr int kAddUnroll = 16;         // 16 KiB of prompt per round trip
+// Registering a request: one workgroup per request.  Long prompts take 256
+// threads moving 16 KiB per round trip; prompts of at most 2048 tokens on
+// average take 128 threads moving 4 KiB, so that more requests are resident
+// at once (measured on MI355X, 4096 prompts of 128-2048 tokens: 12.2 -> 9.5
+// us; 512 prompts of up to 16.9k tokens stay at 256 threads: 10.3 us against
+// 14.7 us with 128).
+constexpr int kAddShortTokens = 2048;
 constexpr int kAppendThreads = 256;
 constexpr int kAppendRows = kAppendThreads / kWave;
 constexpr int kAdvanceThreads = 256;
@@ -37,6 +42,7 @@ __device__ inline bool bad_range(const int32_t* start, int i, int32_t total, int
     return lo < 0 || hi < lo || hi > total;
 }
 
+template <int kAddThreads, int kAddUnroll>
 __global__ __launch_bounds__(kAddThreads) void k_add_requests(
     const int32_t* __restrict__ rows, const int32_t* __restrict__ num_computed,
     const int32_t* __restrict__ prompt_start, const int32_t* __restrict__ prompt_tokens,
@@ -180,10 +186,17 @@ hipError_t launch_add_requests(int32_t m, const int32_t* rows, const int32_t* nu
 {
     if (m == 0)
         return hipSuccess;
-    k_add_requests<<<dim3((unsigned)m), dim3(kAddThreads), 0, stream>>>(
-        rows, num_computed, prompt_start, prompt_tokens, num_prompt_tokens, block_start, blocks,
-        num_blocks_given, R, completed, token_ids, token_stride, L, block_table, MB, row_blocks,
-        status);
+    const bool short_prompts = (int64_t)num_prompt_tokens <= (int64_t)kAddShortTokens * m;
+#define PKV_ADD_LAUNCH(W, U)                                                                       \
+    k_add_requests<W, U><<<dim3((unsigned)m), dim3(W), 0, stream>>>(                              \
+        rows, num_computed, prompt_start, prompt_tokens, num_prompt_tokens, block_start, blocks,   \
+        num_blocks_given, R, completed, token_ids, token_stride, L, block_table, MB, row_blocks,   \
+        status)
+    if (short_prompts)
+        PKV_ADD_LAUNCH(128, 8);
+    else
+        PKV_ADD_LAUNCH(256, 16);
+#undef PKV_ADD_LAUNCH
     return hipGetLastError();
 }
 

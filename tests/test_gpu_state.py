@@ -91,9 +91,12 @@ def _maybe_corrupt(rng, lists, p=0.15):
 
 SHAPES = {
     # R, L, MB, longest prompt, most blocks: small, then large enough that the
-    # copies span several 1024-element rounds with a ragged tail
+    # copies span several 1024-element rounds with a ragged tail, then prompts
+    # of 4500 tokens on average (the registration's wider workgroups, several
+    # 4096-token rounds)
     "small": (6, 12, 4, 14, 6),
     "large": (300, 3000, 300, 3300, 320),
+    "long": (64, 9000, 600, 9000, 620),
 }
 
 
