@@ -38,7 +38,8 @@ constexpr int32_t kNoBlock = INT32_MAX;
 // request's blocks take fewer rounds (measured on MI355X, 512 requests of up
 // to 1056 blocks: lookup 16 -> 12 us, insert 19.6 -> 16.6 us; 1024-thread
 // hashing was slower).  Narrow tables get narrow workgroups, so that more
-// requests are resident at once.
+// requests are resident at once (4096 requests with tables of 128 blocks:
+// lookup 28.9 -> 11.2 us, hashing 19.3 -> 12.3 us).
 constexpr int kHashMaxThreads = 256;
 constexpr int kIndexMaxThreads = 1024;
 constexpr int kFlatThreads = 256;         // flat grids: eviction, clearing
